@@ -1,0 +1,15 @@
+"""FP64 CPU oracle of the Flint sink-aware attention forward.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and
+the benchmark's CPU-baseline leg, never by the product path.
+"""
+
+from .flint_oracle import (  # noqa: F401
+    allowed_keys,
+    flint_attention,
+    kv_head_of,
+    rms_norm,
+    rope_frequencies,
+    rope_neox,
+    sink_softmax,
+)

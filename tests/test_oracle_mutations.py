@@ -1,0 +1,124 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check a pin catches each.
+
+Every mutation swaps one oracle function for a wrong variant, then runs the
+pins; the test passes when at least one pin fails. This shows that the pins
+pin the oracle down: a dropped term, a wrong sign, index or operand anywhere in
+it is seen.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.flint_oracle as fo
+
+from . import oracle_pins
+
+_rms = fo.rms_norm
+_rope = fo.rope_neox
+_freq = fo.rope_frequencies
+_allowed = fo.allowed_keys
+_softmax = fo.sink_softmax
+_kv = fo.kv_head_of
+
+
+def _rms_one_plus_w(x, w, eps):
+    return _rms(x, 1.0 + np.asarray(w, np.float64), eps)
+
+
+def _rms_eps_outside(x, w, eps):
+    x = np.asarray(x, np.float64)
+    return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * w
+
+
+def _rms_no_weight(x, w, eps):
+    return _rms(x, np.ones_like(np.asarray(w, np.float64)), eps)
+
+
+def _rope_interleaved(x, pos, theta):
+    x = np.asarray(x, np.float64)
+    perm = np.concatenate([np.arange(0, x.shape[-1], 2), np.arange(1, x.shape[-1], 2)])
+    inv = np.argsort(perm)
+    return _rope(x[..., perm], pos, theta)[..., inv]
+
+
+def _freq_half_rate(head_dim, theta):
+    c = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(np.float64(theta), -c / head_dim)
+
+
+def _rope_reversed(x, pos, theta):
+    return _rope(x, -np.asarray(pos, np.float64), theta)
+
+
+def _rope_position_plus_one(x, pos, theta):
+    return _rope(x, np.asarray(pos, np.float64) + 1, theta)
+
+
+def _window_off_by_one(lq, lk, valid_len, window):
+    return _allowed(lq, lk, valid_len, window + 1 if window > 0 else 0)
+
+
+def _non_causal_by_one(lq, lk, valid_len, window):
+    return _allowed(np.asarray(lq) + 1, lk, valid_len, window)
+
+
+def _sink_scaled(z, sink):
+    return _softmax(z, np.asarray(sink, np.float64) / math.sqrt(128))
+
+
+def _sink_dropped(z, sink):
+    w, _, m, e = _softmax(z, np.full_like(np.asarray(sink, np.float64), -np.inf))
+    return w, np.zeros_like(np.asarray(m)), m, e
+
+
+def _sink_as_zero_logit_token(z, sink):
+    return _softmax(z, np.zeros_like(np.asarray(sink, np.float64)))
+
+
+def _logits_unscaled(z, sink):
+    return _softmax(z * math.sqrt(128), sink)
+
+
+def _gqa_modulo(h, num_q_heads, num_kv_heads):
+    return h % num_kv_heads
+
+
+MUTATIONS = {
+    "rmsnorm 1+w": ("rms_norm", _rms_one_plus_w),
+    "rmsnorm eps outside sqrt": ("rms_norm", _rms_eps_outside),
+    "rmsnorm weight dropped": ("rms_norm", _rms_no_weight),
+    "rope interleaved pairs": ("rope_neox", _rope_interleaved),
+    "rope frequencies half rate": ("rope_frequencies", _freq_half_rate),
+    "rope rotation sign": ("rope_neox", _rope_reversed),
+    "rope position off by one": ("rope_neox", _rope_position_plus_one),
+    "window 514": ("allowed_keys", _window_off_by_one),
+    "causal off by one": ("allowed_keys", _non_causal_by_one),
+    "sink scaled by 1/sqrt(d)": ("sink_softmax", _sink_scaled),
+    "sink dropped": ("sink_softmax", _sink_dropped),
+    "sink as zero-logit token": ("sink_softmax", _sink_as_zero_logit_token),
+    "logits unscaled": ("sink_softmax", _logits_unscaled),
+    "gqa h % 4": ("kv_head_of", _gqa_modulo),
+}
+
+# Keeping padded keys is not a mutation here: padding is trailing, so every
+# padded key lies after every valid query and causality already drops it.
+
+# cheap pins first: the first failure ends the run for that mutation
+_ORDER = sorted(oracle_pins.ALL_PINS, key=lambda f: (f.__name__ in (
+    "pin_window_count", "pin_rope_frequencies_library", "pin_library_layer"), f.__name__))
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, bad = MUTATIONS[name]
+    monkeypatch.setattr(fo, attr, bad)
+    caught = []
+    for pin in _ORDER:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin caught the planted mistake '{name}'"
