@@ -1,0 +1,231 @@
+"""ctypes binding of libflint_attn.so.
+
+The functions named like the C entry points (``flint_attn_fwd`` and friends)
+take the same arguments as the C ABI: device pointers as ints, sizes and a
+stream handle. ``flint_attn`` is a convenience layer over them for torch
+tensors: it checks dtypes and layouts, allocates the output and the workspace
+with torch, and passes torch's current stream. Every step of the computation
+runs in the library's HIP kernels; nothing here computes any part of the layer.
+There is no fallback: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libflint_attn.so")
+
+NUM_Q_HEADS = 32
+NUM_KV_HEADS = 4
+HEAD_DIM = 128
+
+FLINT_OK = 0
+FLINT_ERR_NULL = -1
+FLINT_ERR_SHAPE = -2
+FLINT_ERR_UNSUPPORTED = -3
+FLINT_ERR_VALUE = -4
+FLINT_ERR_WORKSPACE = -5
+FLINT_ERR_ALIGN = -6
+FLINT_ERR_HIP = -7
+FLINT_ERR_DEVICE_DATA = -8
+
+EXPORTED = (
+    "flint_attn_workspace_bytes",
+    "flint_attn_fwd",
+    "flint_attn_seqused_from_mask",
+    "flint_attn_device_status",
+    "flint_attn_strerror",
+)
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class FlintError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = flint_attn_strerror(status)
+        super().__init__(f"{what}: {msg} (status {status})" if what else f"{msg} (status {status})")
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Loads the in-tree HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m attention_head_rmsnorm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.flint_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.flint_attn_workspace_bytes.restype = sz
+    lib.flint_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                   i32, i32, f32, f32, vp, sz, vp, vp]
+    lib.flint_attn_fwd.restype = ctypes.c_int
+    lib.flint_attn_seqused_from_mask.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.flint_attn_seqused_from_mask.restype = ctypes.c_int
+    lib.flint_attn_device_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
+    lib.flint_attn_device_status.restype = ctypes.c_int
+    lib.flint_attn_strerror.argtypes = [ctypes.c_int]
+    lib.flint_attn_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------- raw C ABI
+
+
+def flint_attn_workspace_bytes(total_tokens: int, n_seqs: int, max_seqlen: int,
+                               num_kv_heads: int = NUM_KV_HEADS, head_dim: int = HEAD_DIM) -> int:
+    return int(load_library().flint_attn_workspace_bytes(total_tokens, n_seqs, max_seqlen,
+                                                         num_kv_heads, head_dim))
+
+
+def flint_attn_fwd(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused, n_seqs,
+                   max_seqlen, total_tokens, num_q_heads, num_kv_heads, head_dim, window, use_rope,
+                   rope_theta, eps, workspace, workspace_bytes, out, stream) -> int:
+    """The C entry point with pointer arguments as ints (0 = NULL); returns the status."""
+    return int(load_library().flint_attn_fwd(q, k, v, q_norm_w, k_norm_w, sink, positions,
+                                             cu_seqlens, seqused, n_seqs, max_seqlen,
+                                             total_tokens, num_q_heads, num_kv_heads, head_dim,
+                                             window, use_rope, rope_theta, eps, workspace,
+                                             workspace_bytes, out, stream))
+
+
+def flint_attn_seqused_from_mask(mask, batch, seqlen, seqused, n_bad, stream) -> int:
+    return int(load_library().flint_attn_seqused_from_mask(mask, batch, seqlen, seqused, n_bad,
+                                                           stream))
+
+
+def flint_attn_device_status(workspace, stream):
+    """Returns (status, flags) after synchronizing the stream."""
+    flags = ctypes.c_int32(0)
+    st = int(load_library().flint_attn_device_status(workspace, stream, ctypes.byref(flags)))
+    return st, int(flags.value)
+
+
+def flint_attn_strerror(status: int) -> str:
+    return load_library().flint_attn_strerror(int(status)).decode()
+
+
+# ----------------------------------------------------------------- torch layer
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream_handle(device) -> int:
+    import torch
+
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def seqused_from_mask(attention_mask):
+    """[B, S] binary mask (1 = valid, trailing padding only) -> int32 [B] on the device."""
+    import torch
+
+    if attention_mask.dim() != 2:
+        raise ValueError("attention_mask must be [batch, seqlen]")
+    m = attention_mask
+    if m.dtype != torch.uint8:
+        m = (m != 0).to(torch.uint8)
+    m = m.contiguous()
+    B, S = m.shape
+    seqused = torch.empty(B, dtype=torch.int32, device=m.device)
+    n_bad = torch.empty(1, dtype=torch.int32, device=m.device)
+    st = flint_attn_seqused_from_mask(_ptr(m), B, S, _ptr(seqused), _ptr(n_bad),
+                                      _stream_handle(m.device))
+    if st != FLINT_OK:
+        raise FlintError(st, "flint_attn_seqused_from_mask")
+    if int(n_bad.item()) != 0:
+        raise ValueError("attention_mask has non-trailing padding; arbitrary padding uses THD "
+                         "packing (pass cu_seqlens)")
+    return seqused
+
+
+def flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens=None,
+               attention_mask=None, seqused=None, max_seqlen: Optional[int] = None,
+               window: int = 513, use_rope: bool = True, rope_theta: float = 1.0e6,
+               eps: float = 1.0e-6, out=None, workspace=None):
+    """Sink-aware GQA attention forward on torch tensors.
+
+    q: bf16 [B, S, 32, 128] (BSHD) or [T, 32, 128] (THD); k, v: bf16 with 4
+    heads in the same layout. q_norm_w, k_norm_w: fp32 [128]; sinks: fp32 [32].
+    THD takes ``cu_seqlens`` (int32 [n+1], device) and, optionally,
+    ``max_seqlen``; BSHD takes ``attention_mask`` [B, S] (trailing padding) or
+    ``seqused`` [B]. ``positions`` is int32 [B, S] or [T] (default: index in
+    the sequence). Returns the output in q's layout.
+    """
+    import torch
+
+    if not q.is_cuda:
+        raise ValueError("flint_attn runs on a HIP device; q is on the CPU")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
+    for name, t in (("q_norm_w", q_norm_w), ("k_norm_w", k_norm_w), ("sinks", sinks)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev:
+            raise TypeError(f"{name} must be a contiguous float32 tensor on {dev}")
+    if q.dim() == 4:
+        B, S = q.shape[0], q.shape[1]
+        T = B * S
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens is for THD input; BSHD takes attention_mask or seqused")
+        cu = torch.arange(0, T + 1, max(S, 1), dtype=torch.int32, device=dev)[:B + 1]
+        n = B
+        mx = S
+        if attention_mask is not None:
+            if seqused is not None:
+                raise ValueError("pass attention_mask or seqused, not both")
+            if tuple(attention_mask.shape) != (B, S):
+                raise ValueError("attention_mask must be [batch, seqlen]")
+            seqused = seqused_from_mask(attention_mask)
+    elif q.dim() == 3:
+        T = q.shape[0]
+        if attention_mask is not None:
+            raise ValueError("THD input takes cu_seqlens, not attention_mask")
+        if cu_seqlens is None:
+            cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+            mx = T
+        else:
+            cu = cu_seqlens
+            if cu.dtype != torch.int32 or not cu.is_contiguous() or cu.device != dev:
+                raise TypeError("cu_seqlens must be a contiguous int32 tensor on the device")
+            mx = max_seqlen
+            if mx is None:
+                mx = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+        n = cu.numel() - 1
+    else:
+        raise ValueError("q must be [B, S, H, D] or [T, H, D]")
+    if seqused is not None and (seqused.dtype != torch.int32 or seqused.device != dev
+                                or seqused.numel() != n):
+        raise TypeError("seqused must be int32 [n_seqs] on the device")
+    if positions is not None:
+        if positions.dtype != torch.int32 or positions.device != dev or positions.numel() != T:
+            raise TypeError("positions must be int32 with one entry per token, on the device")
+        positions = positions.contiguous()
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = flint_attn_workspace_bytes(T, n, mx, k.shape[-2], k.shape[-1])
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = flint_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(sinks),
+                        _ptr(positions), _ptr(cu), _ptr(seqused), n, mx, T, q.shape[-2],
+                        k.shape[-2], q.shape[-1], int(window), int(bool(use_rope)),
+                        float(rope_theta), float(eps), _ptr(workspace), workspace.numel(),
+                        _ptr(out), _stream_handle(dev))
+    if st != FLINT_OK:
+        raise FlintError(st, "flint_attn_fwd")
+    return out

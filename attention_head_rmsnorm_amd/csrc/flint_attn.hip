@@ -1,0 +1,737 @@
+// Flint sink-aware attention forward (prefill) for AMD Instinct MI355X (gfx950).
+//
+// The layer (NeMo AutoModel "flint" page, section "Model Architecture";
+// flint.layers API page, FlintAttention; Hugging Face discussion #26 on
+// RecursiveSI/flint, "What was unusually easy" and "Configuration oddities"):
+// per-head weight-form RMSNorm of q and k, NeoX RoPE (channel c with c+64) on
+// sliding layers only, grouped-query attention of 32 query heads over 4
+// key/value heads with head dimension 128, a causal window of 513 keys that
+// counts the current token (or full causal attention), and one FP32 sink
+// logit per query head that joins the softmax max and denominator with zero
+// value and no 1/sqrt(d) scaling.
+//
+// Three kernels run in order on the caller's stream:
+//   schedule_kernel   one workgroup; checks cu_seqlens/seqused, lays out the
+//                     64-token key tiles of every sequence and the 32-token
+//                     query blocks, and orders the blocks by decreasing work.
+//   kv_prologue_kernel  per (key tile, kv head): RMSNorm + RoPE of K in FP32,
+//                     one bf16 rounding, stored as an MFMA-ready swizzled tile;
+//                     V transposed and key-permuted into the PV operand order;
+//                     zeros for padded keys; zero rows of `out` for padded
+//                     queries.
+//   attn_kernel       per (query block, kv head): 8 waves, one per query head
+//                     of the group, share each K/V tile staged in LDS. The
+//                     query prologue (RMSNorm, RoPE, softmax scale in log2
+//                     units, bf16) is fused in. S^T = K Q^T and O^T += V^T P^T
+//                     run on v_mfma_f32_32x32x16_bf16 with FP32 accumulation;
+//                     the streaming softmax starts from the sink (m = sink,
+//                     l = 1) and only visits tiles inside the causal window.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "flint_attn.h"
+
+namespace flint {
+
+constexpr int kH = 32;        // query heads
+constexpr int kG = 4;         // key/value heads
+constexpr int kD = 128;       // head dimension
+constexpr int kHpg = kH / kG; // query heads per key/value head
+constexpr int kBM = 32;       // query tokens per work item
+constexpr int kBN = 64;       // keys per tile
+constexpr int kHalfTile = kBN * kD * 2;     // bytes of one K' tile or one V^T tile
+constexpr int kTileBytes = 2 * kHalfTile;   // K' tile followed by V^T tile
+constexpr int kTileVec = kTileBytes / 16;   // 16-byte vectors per tile
+constexpr int kBuckets = 4096;              // cost buckets of the schedule sort
+constexpr int kAttnThreads = 64 * kHpg;     // one wave per query head of a group
+constexpr float kLog2e = 1.4426950408889634f;
+// Keep a stale running max until a tile's max exceeds it by this much (log2
+// units): exp2 values then stay below 2^8, and the final O / l is unchanged.
+constexpr float kRescaleSlack = 8.0f;
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+struct Ws {
+  int* hdr;       // [0] device-data error bits, [1] key tiles, [2] query blocks
+  double* omega;  // [64] RoPE frequencies theta^(-c/64)
+  int4* seq;      // [n] {start, length, valid length, first tile}
+  int* tbase;     // [n+1] first key tile of each sequence
+  int* qbase;     // [n+1] first query block of each sequence
+  int2* tiles;    // [ntmax] {sequence, tile in sequence}
+  int2* items;    // [nqmax] {sequence, query block}, most work first
+  char* kv;       // [kG][ntmax][kTileBytes]
+  int ntmax;
+};
+
+struct Layout {
+  size_t hdr, omega, seq, tbase, qbase, tiles, items, kv, total;
+  int64_t ntmax, nqmax;
+};
+
+static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static Layout make_layout(int64_t T, int64_t n) {
+  Layout L;
+  L.ntmax = (T + kBN - 1) / kBN + n;
+  L.nqmax = (T + kBM - 1) / kBM + n;
+  size_t o = 0;
+  L.hdr = o;   o = align_up(o + 64 * sizeof(int), 256);
+  L.omega = o; o = align_up(o + 64 * sizeof(double), 256);
+  L.seq = o;   o = align_up(o + (size_t)n * sizeof(int4), 256);
+  L.tbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
+  L.qbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
+  L.tiles = o; o = align_up(o + (size_t)L.ntmax * sizeof(int2), 256);
+  L.items = o; o = align_up(o + (size_t)L.nqmax * sizeof(int2), 256);
+  L.kv = o;    o = align_up(o + (size_t)kG * (size_t)L.ntmax * kTileBytes, 256);
+  L.total = o;
+  return L;
+}
+
+// ----------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ void unpack8(const uint4& c, float* x) {
+  x[0] = bf16_lo(c.x); x[1] = bf16_hi(c.x);
+  x[2] = bf16_lo(c.y); x[3] = bf16_hi(c.y);
+  x[4] = bf16_lo(c.z); x[5] = bf16_hi(c.z);
+  x[6] = bf16_lo(c.w); x[7] = bf16_hi(c.w);
+}
+
+// Round to bf16 (nearest even) and pack two values into one word.
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+  bf16x2 p = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* x) {
+  return make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+}
+
+// cos and sin of pos * omega, with the angle reduced to [-pi, pi] in FP64 so
+// that positions up to 2^18 keep full FP32 accuracy.
+__device__ __forceinline__ void rope_cos_sin(int pos, double omega, float* c, float* s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double rev = (double)pos * omega * (1.0 / two_pi);
+  rev -= rint(rev);
+  sincosf((float)(rev * two_pi), s, c);
+}
+
+// Exclusive scan over the 1024 threads of a block; *total gets the sum.
+__device__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int tid = threadIdx.x;
+  tmp[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int x = tid >= off ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += x;
+    __syncthreads();
+  }
+  const int incl = tmp[tid];
+  *total = tmp[1023];
+  __syncthreads();
+  return incl - v;
+}
+
+// Largest s in [0, n) with base[s] <= e (base non-decreasing, base[0] = 0).
+__device__ __forceinline__ int find_seq(const int* base, int n, int e) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (base[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Key range of query block qb: [lo, hi) in sequence positions.
+__device__ __forceinline__ void block_keys(int u, int qb, int window, int* lo, int* hi) {
+  const int t0 = qb * kBM;
+  *hi = min(t0 + kBM, u);
+  *lo = window > 0 ? max(0, t0 - (window - 1)) : 0;
+}
+
+__device__ __forceinline__ int block_cost(int u, int qb, int window) {
+  int lo, hi;
+  block_keys(u, qb, window, &lo, &hi);
+  return ((hi + kBN - 1) / kBN) - lo / kBN;
+}
+
+// ----------------------------------------------------------------- schedule
+
+__global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ cu,
+                                                        const int* __restrict__ seqused, int n,
+                                                        int T, int max_seqlen, int window,
+                                                        double theta, Ws ws) {
+  __shared__ int tmp[1024];
+  __shared__ int hist[kBuckets];
+  __shared__ int sflags;
+  const int tid = threadIdx.x;
+  if (tid == 0) sflags = 0;
+  if (tid < 64) ws.omega[tid] = pow(theta, -(double)tid / 64.0);
+  __syncthreads();
+
+  int flags = 0;
+  int carry_t = 0, carry_q = 0;
+  for (int base = 0; base < n; base += 1024) {
+    const int s = base + tid;
+    int nt = 0, nq = 0, a = 0, len = 0, u = 0;
+    if (s < n) {
+      a = cu[s];
+      const int b = cu[s + 1];
+      if (s == 0 && a != 0) flags |= FLINT_DEV_CU_START;
+      if (b < a) flags |= FLINT_DEV_CU_ORDER;
+      if (s == n - 1 && b != T) flags |= FLINT_DEV_CU_END;
+      len = b >= a ? b - a : 0;
+      if (len > max_seqlen) flags |= FLINT_DEV_MAX_SEQLEN;
+      u = seqused ? seqused[s] : len;
+      if (u < 0 || u > len) {
+        flags |= FLINT_DEV_SEQUSED;
+        u = max(0, min(u, len));
+      }
+      nt = (len + kBN - 1) / kBN;
+      nq = (u + kBM - 1) / kBM;
+    }
+    int tot_t, tot_q;
+    const int ex_t = block_excl_scan(nt, tmp, &tot_t);
+    const int ex_q = block_excl_scan(nq, tmp, &tot_q);
+    if (s < n) {
+      ws.seq[s] = make_int4(a, len, u, carry_t + ex_t);
+      ws.tbase[s] = carry_t + ex_t;
+      ws.qbase[s] = carry_q + ex_q;
+    }
+    carry_t += tot_t;
+    carry_q += tot_q;
+  }
+  if (flags) atomicOr(&sflags, flags);
+  __syncthreads();
+  const int f = sflags;
+  if (f) {  // invalid device data: schedule nothing
+    if (tid == 0) {
+      ws.hdr[0] = f;
+      ws.hdr[1] = 0;
+      ws.hdr[2] = 0;
+    }
+    return;
+  }
+  if (tid == 0) {
+    ws.tbase[n] = carry_t;
+    ws.qbase[n] = carry_q;
+  }
+  const int NT = carry_t, NQ = carry_q;
+  for (int i = tid; i < kBuckets; i += 1024) hist[i] = 0;
+  __syncthreads();
+
+  for (int e = tid; e < NT; e += 1024) {
+    const int s = find_seq(ws.tbase, n, e);
+    ws.tiles[e] = make_int2(s, e - ws.tbase[s]);
+  }
+  for (int e = tid; e < NQ; e += 1024) {
+    const int s = find_seq(ws.qbase, n, e);
+    const int c = min(block_cost(ws.seq[s].z, e - ws.qbase[s], window), kBuckets - 1);
+    atomicAdd(&hist[c], 1);
+  }
+  __syncthreads();
+  // bucket starts in order of decreasing cost; thread tid owns 4 buckets
+  int local[4], sum = 0;
+  for (int j = 0; j < 4; ++j) {
+    local[j] = hist[kBuckets - 1 - (4 * tid + j)];
+    sum += local[j];
+  }
+  int tot;
+  int run = block_excl_scan(sum, tmp, &tot);
+  for (int j = 0; j < 4; ++j) {
+    hist[kBuckets - 1 - (4 * tid + j)] = run;
+    run += local[j];
+  }
+  __syncthreads();
+  for (int e = tid; e < NQ; e += 1024) {
+    const int s = find_seq(ws.qbase, n, e);
+    const int qb = e - ws.qbase[s];
+    const int c = min(block_cost(ws.seq[s].z, qb, window), kBuckets - 1);
+    const int pos = atomicAdd(&hist[c], 1);
+    ws.items[pos] = make_int2(s, qb);
+  }
+  if (tid == 0) {
+    ws.hdr[0] = 0;
+    ws.hdr[1] = NT;
+    ws.hdr[2] = NQ;
+  }
+}
+
+// ----------------------------------------------------------------- K/V prologue
+
+// Slot of key r (0..63) inside a V^T row: bits 2 and 3 swapped, which is the
+// order in which the softmax output P^T sits in the MFMA B operand.
+__device__ __forceinline__ int vt_slot(int r) { return r ^ ((((r >> 2) ^ (r >> 3)) & 1) * 12); }
+
+__global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          const float* __restrict__ k_norm_w,
+                                                          const int* __restrict__ positions,
+                                                          float eps, int use_rope, Ws ws,
+                                                          uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kD * kBN];
+  const int e = blockIdx.x, g = blockIdx.y;
+  if (e >= ws.hdr[1]) return;
+  const int2 te = ws.tiles[e];
+  const int4 meta = ws.seq[te.x];
+  const int start = meta.x, len = meta.y, u = meta.z;
+  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
+  const int ell = te.y * kBN + r;
+  const bool valid = ell < u;
+  const size_t t = (size_t)start + ell;
+  char* tile = ws.kv + ((size_t)g * ws.ntmax + meta.w + te.y) * kTileBytes;
+
+  // K: this thread owns channels [16p, 16p+16) and their RoPE partners +64.
+  float x[32];
+  if (valid) {
+    const uint4* src = reinterpret_cast<const uint4*>(k + (t * kG + g) * kD);
+    unpack8(src[2 * p], x);
+    unpack8(src[2 * p + 1], x + 8);
+    unpack8(src[8 + 2 * p], x + 16);
+    unpack8(src[9 + 2 * p], x + 24);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.f;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) ss += x[i] * x[i];
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[i] *= rstd * k_norm_w[16 * p + i];
+    x[16 + i] *= rstd * k_norm_w[64 + 16 * p + i];
+  }
+  if (use_rope && valid) {
+    const int pos = positions ? positions[t] : ell;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float c, s;
+      rope_cos_sin(pos, ws.omega[16 * p + i], &c, &s);
+      const float a = x[i], b = x[16 + i];
+      x[i] = a * c - b * s;
+      x[16 + i] = b * c + a * s;
+    }
+  }
+  {
+    uint4* krow = reinterpret_cast<uint4*>(tile + r * (kD * 2));
+    const int sw = r & 15;
+    krow[(2 * p) ^ sw] = pack8(x);
+    krow[(2 * p + 1) ^ sw] = pack8(x + 8);
+    krow[(8 + 2 * p) ^ sw] = pack8(x + 16);
+    krow[(9 + 2 * p) ^ sw] = pack8(x + 24);
+  }
+
+  // V: transpose through LDS; this thread owns channels [32p, 32p+32) of key r.
+  {
+    uint4 c4[4];
+    if (valid) {
+      const uint4* src = reinterpret_cast<const uint4*>(v + (t * kG + g) * kD);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c4[i] = src[4 * p + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c4[i] = make_uint4(0, 0, 0, 0);
+    }
+    const int slot = vt_slot(r);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w4[4] = {c4[i].x, c4[i].y, c4[i].z, c4[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * p + 8 * i + 2 * j;
+        vt[d * kBN + slot] = (uint16_t)(w4[j] & 0xffff);
+        vt[(d + 1) * kBN + slot] = (uint16_t)(w4[j] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  {
+    uint4* vtile = reinterpret_cast<uint4*>(tile + kHalfTile);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qv = tid + 256 * i;
+      const int d = qv >> 3, c = qv & 7;
+      vtile[d * 8 + (c ^ (d & 7))] = *reinterpret_cast<const uint4*>(&vt[d * kBN + c * 8]);
+    }
+  }
+
+  // Padded query rows of this kv head's 8 query heads are exact zeros.
+  if (ell >= u && ell < len) {
+    uint4* dst = reinterpret_cast<uint4*>(out + (t * kH + (size_t)g * kHpg) * kD);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) dst[p * 32 + i] = z;
+  }
+}
+
+// ----------------------------------------------------------------- attention
+
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __restrict__ q,
+                                                            const float* __restrict__ q_norm_w,
+                                                            const float* __restrict__ sink,
+                                                            const int* __restrict__ positions,
+                                                            int window, int use_rope, float eps,
+                                                            Ws ws, uint16_t* __restrict__ out) {
+  __shared__ uint4 smem[2][kTileVec];
+  const int g = blockIdx.x & (kG - 1);
+  const int e = blockIdx.x / kG;
+  if (e >= ws.hdr[2]) return;
+  const int2 item = ws.items[e];
+  const int4 meta = ws.seq[item.x];
+  const int start = meta.x, u = meta.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int h = g * kHpg + wave;
+  const int t0 = item.y * kBM;
+  int klo, khi;
+  block_keys(u, item.y, window, &klo, &khi);
+  const int tile_lo = klo / kBN;
+  const int ntiles = (khi + kBN - 1) / kBN - tile_lo;
+  const uint4* kvbase =
+      reinterpret_cast<const uint4*>(ws.kv + ((size_t)g * ws.ntmax + meta.w) * kTileBytes);
+
+  uint4 pre[kTileVec / kAttnThreads];
+  {
+    const uint4* src = kvbase + (size_t)tile_lo * kTileVec;
+#pragma unroll
+    for (int i = 0; i < kTileVec / kAttnThreads; ++i) pre[i] = src[tid + kAttnThreads * i];
+  }
+
+  // Query prologue: lane (col, half) holds channels 16kk + 8half + [0,8) of
+  // token t0 + col, which is the MFMA B-operand layout of Q^T.
+  const int qrow = t0 + col;
+  const bool qvalid = qrow < u;
+  const size_t tq = (size_t)start + qrow;
+  bf16x8 qf[8];
+  {
+    float x[64];
+    if (qvalid) {
+      const uint4* src = reinterpret_cast<const uint4*>(q + (tq * kH + h) * kD);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) unpack8(src[2 * kk + half], x + 8 * kk);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) x[i] = 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
+    ss += __shfl_xor(ss, 32);
+    const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[8 * kk + j] *= rstd * q_norm_w[16 * kk + 8 * half + j];
+    if (use_rope && qvalid) {
+      const int pos = positions ? positions[tq] : qrow;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float c, s;
+          rope_cos_sin(pos, ws.omega[16 * kk + 8 * half + j], &c, &s);
+          const float a = x[8 * kk + j], b = x[8 * (kk + 4) + j];
+          x[8 * kk + j] = a * c - b * s;
+          x[8 * (kk + 4) + j] = b * c + a * s;
+        }
+    }
+    // logits in log2 units: q . k / sqrt(128) * log2(e)
+    const float scale = kLog2e * 0.08838834764831845f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[8 * kk + j] *= scale;
+      qf[kk] = __builtin_bit_cast(bf16x8, pack8(x + 8 * kk));
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < kTileVec / kAttnThreads; ++i) smem[0][tid + kAttnThreads * i] = pre[i];
+  __syncthreads();
+
+  float m = sink[h] * kLog2e;                    // running max, seeded by the sink
+  float l = (half == 0 && m != -INFINITY) ? 1.f : 0.f;  // exp2(sink - m), counted once per query
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int j = tile_lo + it;
+    const bool more = it + 1 < ntiles;
+    if (more) {
+      const uint4* src = kvbase + (size_t)(j + 1) * kTileVec;
+#pragma unroll
+      for (int i = 0; i < kTileVec / kAttnThreads; ++i) pre[i] = src[tid + kAttnThreads * i];
+    }
+    const uint4* kt = smem[it & 1];
+    const uint4* vt = smem[it & 1] + kTileVec / 2;
+
+    // S^T[key, query] for keys [0,32) and [32,64) of the tile
+    f32x16 s0, s1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
+    const int ksw = col & 15;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int ch = (2 * kk + half) ^ ksw;
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, kt[col * 16 + ch]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, kt[(32 + col) * 16 + ch]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s1, 0, 0, 0);
+    }
+
+    const int k0 = j * kBN;
+    const bool need_mask =
+        (k0 + kBN - 1 > t0) || (k0 + kBN > u) || (window > 0 && t0 + kBM - 1 - k0 > window - 1);
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
+        const bool ok0 = key <= qrow && key < u && (window == 0 || qrow - key <= window - 1);
+        const bool ok1 =
+            key + 32 <= qrow && key + 32 < u && (window == 0 || qrow - key - 32 <= window - 1);
+        s0[i] = ok0 ? s0[i] : -INFINITY;
+        s1[i] = ok1 ? s1[i] : -INFINITY;
+      }
+    }
+
+    float mx = s0[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const bool resc = m_new > m + kRescaleSlack;
+    if (__any(resc)) {
+      const float alpha = resc ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+      m = resc ? m_new : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    }
+    const float msub = m == -INFINITY ? 0.f : m;
+
+    bf16x8 pk[4];
+    {
+      float p[16];
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(s0[i] - msub);
+        ls += p[i];
+      }
+      pk[0] = __builtin_bit_cast(bf16x8, pack8(p));
+      pk[1] = __builtin_bit_cast(bf16x8, pack8(p + 8));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(s1[i] - msub);
+        ls += p[i];
+      }
+      pk[2] = __builtin_bit_cast(bf16x8, pack8(p));
+      pk[3] = __builtin_bit_cast(bf16x8, pack8(p + 8));
+      l += ls;
+    }
+
+    // O^T[d, query] += V^T[d, keys] P^T[keys, query]
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int row = 32 * db + col;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, vt[row * 8 + ((2 * kk + half) ^ (row & 7))]);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], acc[db], 0, 0, 0);
+      }
+    }
+
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < kTileVec / kAttnThreads; ++i)
+        smem[(it + 1) & 1][tid + kAttnThreads * i] = pre[i];
+    }
+    __syncthreads();
+  }
+
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qvalid) {
+    uint16_t* dst = out + (tq * kH + h) * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = 32 * db + 8 * rg + 4 * half;
+        const uint2 w = make_uint2(pack2(acc[db][4 * rg] * inv, acc[db][4 * rg + 1] * inv),
+                                   pack2(acc[db][4 * rg + 2] * inv, acc[db][4 * rg + 3] * inv));
+        *reinterpret_cast<uint2*>(dst + d) = w;
+      }
+  }
+}
+
+// ----------------------------------------------------------------- mask helper
+
+__global__ __launch_bounds__(1024) void mask_kernel(const uint8_t* __restrict__ mask, int batch,
+                                                    int seqlen, int* __restrict__ seqused,
+                                                    int* __restrict__ n_bad) {
+  __shared__ int s_cnt, s_first, s_bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (tid == 0) {
+      s_cnt = 0;
+      s_first = seqlen;
+    }
+    __syncthreads();
+    int cnt = 0, first = seqlen;
+    const uint8_t* row = mask + (size_t)b * seqlen;
+    for (int i = tid; i < seqlen; i += 1024) {
+      if (row[i]) ++cnt;
+      else first = min(first, i);
+    }
+    atomicAdd(&s_cnt, cnt);
+    atomicMin(&s_first, first);
+    __syncthreads();
+    if (tid == 0) {
+      seqused[b] = s_cnt;
+      if (s_cnt != s_first) ++s_bad;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) *n_bad = s_bad;
+}
+
+}  // namespace flint
+
+// ===================================================================== C ABI
+
+using namespace flint;
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+extern "C" size_t flint_attn_workspace_bytes(int32_t total_tokens, int32_t n_seqs,
+                                             int32_t max_seqlen, int32_t num_kv_heads,
+                                             int32_t head_dim) {
+  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return 0;
+  if (num_kv_heads != kG || head_dim != kD) return 0;
+  return make_layout(total_tokens, n_seqs).total;
+}
+
+extern "C" const char* flint_attn_strerror(int status) {
+  switch (status) {
+    case FLINT_OK: return "ok";
+    case FLINT_ERR_NULL: return "a required pointer is NULL";
+    case FLINT_ERR_SHAPE: return "invalid sizes (negative or inconsistent)";
+    case FLINT_ERR_UNSUPPORTED: return "unsupported head layout (need 32 query heads, 4 kv heads, head_dim 128)";
+    case FLINT_ERR_VALUE: return "invalid value (window < 0, eps <= 0, rope_theta <= 0 with RoPE, or NaN)";
+    case FLINT_ERR_WORKSPACE: return "workspace missing or smaller than flint_attn_workspace_bytes()";
+    case FLINT_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, workspace 256, int32 arrays 4)";
+    case FLINT_ERR_HIP: return "HIP runtime error";
+    case FLINT_ERR_DEVICE_DATA: return "invalid device data (cu_seqlens, seqused or mask)";
+    default: return "unknown flint_attn status";
+  }
+}
+
+static bool debug_sync() {
+  const char* e = getenv("FLINT_ATTN_DEBUG");
+  return e && e[0] == '1';
+}
+
+extern "C" int flint_attn_device_status(const void* workspace, void* stream, int32_t* flags) {
+  if (!workspace || !flags) return FLINT_ERR_NULL;
+  if (!aligned(workspace, 256)) return FLINT_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int32_t host = 0;
+  if (hipMemcpyAsync(&host, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return FLINT_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return FLINT_ERR_HIP;
+  *flags = host;
+  return host ? FLINT_ERR_DEVICE_DATA : FLINT_OK;
+}
+
+extern "C" int flint_attn_fwd(const void* q, const void* k, const void* v, const float* q_norm_w,
+                              const float* k_norm_w, const float* sink, const int32_t* positions,
+                              const int32_t* cu_seqlens, const int32_t* seqused, int32_t n_seqs,
+                              int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                              int32_t use_rope, float rope_theta, float eps, void* workspace,
+                              size_t workspace_bytes, void* out, void* stream) {
+  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return FLINT_ERR_SHAPE;
+  if (num_q_heads != kH || num_kv_heads != kG || head_dim != kD) return FLINT_ERR_UNSUPPORTED;
+  if (window < 0 || !(eps > 0.f) || !isfinite(eps)) return FLINT_ERR_VALUE;
+  if (use_rope && (!(rope_theta > 0.f) || !isfinite(rope_theta))) return FLINT_ERR_VALUE;
+  if (total_tokens == 0) return FLINT_OK;
+  if (n_seqs < 1) return FLINT_ERR_SHAPE;
+  if (!q || !k || !v || !q_norm_w || !k_norm_w || !sink || !cu_seqlens || !out)
+    return FLINT_ERR_NULL;
+  if (!workspace) return FLINT_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 256) || !aligned(q_norm_w, 4) || !aligned(k_norm_w, 4) ||
+      !aligned(sink, 4) || !aligned(cu_seqlens, 4) || (positions && !aligned(positions, 4)) ||
+      (seqused && !aligned(seqused, 4)))
+    return FLINT_ERR_ALIGN;
+  const Layout L = make_layout(total_tokens, n_seqs);
+  if (workspace_bytes < L.total) return FLINT_ERR_WORKSPACE;
+
+  char* base = static_cast<char*>(workspace);
+  Ws ws;
+  ws.hdr = reinterpret_cast<int*>(base + L.hdr);
+  ws.omega = reinterpret_cast<double*>(base + L.omega);
+  ws.seq = reinterpret_cast<int4*>(base + L.seq);
+  ws.tbase = reinterpret_cast<int*>(base + L.tbase);
+  ws.qbase = reinterpret_cast<int*>(base + L.qbase);
+  ws.tiles = reinterpret_cast<int2*>(base + L.tiles);
+  ws.items = reinterpret_cast<int2*>(base + L.items);
+  ws.kv = base + L.kv;
+  ws.ntmax = (int)L.ntmax;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint16_t* qh = static_cast<const uint16_t*>(q);
+  const uint16_t* kh = static_cast<const uint16_t*>(k);
+  const uint16_t* vh = static_cast<const uint16_t*>(v);
+  uint16_t* oh = static_cast<uint16_t*>(out);
+  const int rope = use_rope ? 1 : 0;
+  const int* pos = rope ? positions : nullptr;
+
+  (void)hipGetLastError();
+  schedule_kernel<<<1, 1024, 0, st>>>(cu_seqlens, seqused, n_seqs, total_tokens, max_seqlen,
+                                      window, (double)rope_theta, ws);
+  kv_prologue_kernel<<<dim3((unsigned)L.ntmax, kG), 256, 0, st>>>(kh, vh, k_norm_w, pos, eps, rope,
+                                                                  ws, oh);
+  attn_kernel<<<(unsigned)(L.nqmax * kG), kAttnThreads, 0, st>>>(qh, q_norm_w, sink, pos, window,
+                                                                 rope, eps, ws, oh);
+  if (hipGetLastError() != hipSuccess) return FLINT_ERR_HIP;
+  if (debug_sync()) {
+    int32_t flags = 0;
+    return flint_attn_device_status(workspace, stream, &flags);
+  }
+  return FLINT_OK;
+}
+
+extern "C" int flint_attn_seqused_from_mask(const uint8_t* mask, int32_t batch, int32_t seqlen,
+                                            int32_t* seqused, int32_t* n_bad, void* stream) {
+  if (batch < 0 || seqlen < 0) return FLINT_ERR_SHAPE;
+  if (!seqused || !n_bad || (!mask && batch > 0 && seqlen > 0)) return FLINT_ERR_NULL;
+  if (!aligned(seqused, 4) || !aligned(n_bad, 4)) return FLINT_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  mask_kernel<<<1, 1024, 0, st>>>(mask, batch, seqlen, seqused, n_bad);
+  if (hipGetLastError() != hipSuccess) return FLINT_ERR_HIP;
+  return FLINT_OK;
+}

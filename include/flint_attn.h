@@ -1,0 +1,158 @@
+/*
+ * flint_attn.h - C ABI of the Flint sink-aware attention forward (prefill)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What one call computes, for every valid token t of sequence s, query head
+ * h (0..31) and its key/value head g = h / 8 (grouped-query attention,
+ * 32 query heads over 4 key/value heads, head dimension 128 - "flint" page of
+ * NeMo AutoModel, section "Model Architecture"):
+ *
+ *   qhat = RMSNorm(q[t,h,:]) * q_norm_w,  khat = RMSNorm(k[t',g,:]) * k_norm_w
+ *       weight-form RMSNorm, x / sqrt(mean(x^2) + eps) * w, over the 128
+ *       channels of one head (Hugging Face discussion #26 on RecursiveSI/flint,
+ *       "What was unusually easy": plain weight form, not 1+w);
+ *   if use_rope: NeoX rotation of channel c with channel c+64 by the angle
+ *       pos * theta^(-c/64), on all 128 channels, after the norm
+ *       ("Model Architecture": query/key normalization precedes RoPE;
+ *       flint.layers API page, FlintAttention._apply_rope);
+ *   z(t') = qhat . khat(t') / sqrt(128) over the allowed keys t' of the same
+ *       sequence: not padding, not after t, and when window > 0 at most
+ *       window-1 tokens before t (window 513 = the current token and the 512
+ *       before it, "Model Architecture"; window 0 = full causal attention,
+ *       flint.layers page, FlintAttention.forward);
+ *   out[t,h,:] = sum_t' exp(z(t') - m) v[t',g,:] / (exp(sink[h] - m) + sum_t' exp(z(t') - m)),
+ *       m = max(sink[h], max z): the sink is a per-query-head FP32 logit in
+ *       natural-log units, not scaled by 1/sqrt(128), that joins the max and
+ *       the denominator with zero value and is not a token (discussion #26,
+ *       "What was unusually easy" and "Configuration oddities" item 5;
+ *       flint.layers page, _FlintSinkParameters).
+ *
+ * Padded query rows (index in sequence >= seqused[s]) are written as exact
+ * zeros: padded queries and keys leave real attention and only the zero-value
+ * sink stays valid (flint.layers page, FlintAttention.forward, attention_mask).
+ * A row whose sink is -INF and whose key set is empty is also written as 0.
+ *
+ * Layout. BSHD [B, S, H, D] tensors are the THD [T, H, D] form with T = B*S
+ * and cu_seqlens = {0, S, 2S, ..., B*S}; THD packs documents back to back with
+ * document-local positions (flint.layers page, _apply_rope and forward:
+ * "[batch, sequence, heads, head_dim] or THD [tokens, heads, head_dim]").
+ *
+ * Ownership and threading. Every pointer is caller-owned. The library keeps no
+ * state and allocates nothing; it is reentrant. Two calls that share a
+ * workspace must not overlap on the device.
+ *
+ * Asynchrony. flint_attn_fwd validates its host arguments synchronously,
+ * enqueues three kernels on `stream` and returns. Argument errors return a
+ * negative status and launch nothing. Errors in device-resident data
+ * (cu_seqlens, seqused) are detected on the device: the call then writes
+ * nothing to `out` and records the error in the workspace, where
+ * flint_attn_device_status() reads it. With the environment variable
+ * FLINT_ATTN_DEBUG=1, flint_attn_fwd synchronizes and returns that status.
+ */
+#ifndef FLINT_ATTN_H
+#define FLINT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum flint_status {
+  FLINT_OK = 0,
+  FLINT_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  FLINT_ERR_SHAPE = -2,       /* negative or inconsistent sizes                  */
+  FLINT_ERR_UNSUPPORTED = -3, /* heads / head_dim other than 32 / 4 / 128         */
+  FLINT_ERR_VALUE = -4,       /* window < 0, eps <= 0, theta <= 0 with RoPE, NaN  */
+  FLINT_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required          */
+  FLINT_ERR_ALIGN = -6,       /* tensor pointers not 16-byte aligned, workspace
+                                 not 256-byte aligned, int32 arrays not 4-byte    */
+  FLINT_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed        */
+  FLINT_ERR_DEVICE_DATA = -8  /* cu_seqlens / seqused / mask content is invalid    */
+} flint_status;
+
+/* Device-data error bits reported by flint_attn_device_status(). */
+#define FLINT_DEV_CU_START 1     /* cu_seqlens[0] != 0                          */
+#define FLINT_DEV_CU_ORDER 2     /* cu_seqlens decreases somewhere              */
+#define FLINT_DEV_CU_END 4       /* cu_seqlens[n_seqs] != total_tokens          */
+#define FLINT_DEV_MAX_SEQLEN 8   /* a sequence is longer than max_seqlen        */
+#define FLINT_DEV_SEQUSED 16     /* seqused[s] < 0 or > the sequence length     */
+
+/*
+ * Bytes of device workspace flint_attn_fwd needs for these sizes; 0 when the
+ * sizes are invalid (negative, or heads / head_dim unsupported). The value
+ * only grows with each argument. It holds the work schedule and the
+ * normalized, rotated K and the V tiles of every sequence, laid out for the
+ * attention kernel (about 2 KiB per token and 256 KiB per sequence, rounded
+ * up to whole 64-token tiles).
+ */
+size_t flint_attn_workspace_bytes(int32_t total_tokens, int32_t n_seqs, int32_t max_seqlen,
+                                  int32_t num_kv_heads, int32_t head_dim);
+
+/*
+ * The attention forward. All tensor pointers are device pointers.
+ *
+ *   q          bf16 [T, num_q_heads, head_dim], contiguous, 16-byte aligned
+ *   k, v       bf16 [T, num_kv_heads, head_dim], contiguous, 16-byte aligned
+ *   q_norm_w   fp32 [head_dim] RMSNorm weight of the query heads (shared)
+ *   k_norm_w   fp32 [head_dim] RMSNorm weight of the key heads (shared)
+ *   sink       fp32 [num_q_heads] sink logits, natural-log units; -INF allowed
+ *   positions  int32 [T] RoPE positions (document-local for THD), or NULL for
+ *              the index inside the sequence; never read when use_rope == 0
+ *   cu_seqlens int32 [n_seqs + 1]: cu[0] = 0, non-decreasing, cu[n_seqs] = T
+ *   seqused    int32 [n_seqs] valid prefix length of each sequence (trailing
+ *              padding), or NULL when every token is valid
+ *   n_seqs, max_seqlen, total_tokens (T): sizes; max_seqlen bounds every
+ *              cu[s+1] - cu[s]
+ *   num_q_heads, num_kv_heads, head_dim: must be 32, 4, 128
+ *   window     keys per query including the current token (513 on Flint's
+ *              sliding layers), or 0 for full causal attention
+ *   use_rope   non-zero on sliding (RoPE) layers, 0 on full (NoPE) layers
+ *   rope_theta RoPE base (> 0 when use_rope)
+ *   eps        RMSNorm epsilon (> 0; Flint uses 1e-6)
+ *   workspace  device buffer of workspace_bytes >= flint_attn_workspace_bytes(),
+ *              256-byte aligned; its content on entry is ignored
+ *   out        bf16 [T, num_q_heads, head_dim], 16-byte aligned; every row is
+ *              written (padded rows as zeros)
+ *   stream     hipStream_t to enqueue on (NULL = the default stream)
+ *
+ * Returns FLINT_OK or a negative flint_status. T == 0 returns FLINT_OK
+ * without launching anything.
+ */
+int flint_attn_fwd(const void* q, const void* k, const void* v, const float* q_norm_w,
+                   const float* k_norm_w, const float* sink, const int32_t* positions,
+                   const int32_t* cu_seqlens, const int32_t* seqused, int32_t n_seqs,
+                   int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t window, int32_t use_rope,
+                   float rope_theta, float eps, void* workspace, size_t workspace_bytes, void* out,
+                   void* stream);
+
+/*
+ * Turns a binary BSHD attention mask into per-sequence valid lengths. The
+ * mask is uint8 [batch, seqlen] (device), non-zero = valid token. TE's BSHD
+ * form supports trailing padding only and arbitrary padding takes THD
+ * packing (flint.layers page, FlintAttention.forward, attention_mask), so
+ * each row must be ones followed by zeros. Writes seqused[b] (device int32
+ * [batch]) and *n_bad (device int32) = the number of rows that are not of that
+ * form (their seqused is the count of ones). Asynchronous on `stream`.
+ */
+int flint_attn_seqused_from_mask(const uint8_t* mask, int32_t batch, int32_t seqlen,
+                                 int32_t* seqused, int32_t* n_bad, void* stream);
+
+/*
+ * Synchronizes `stream` and reads the device-data error bits that the last
+ * flint_attn_fwd using this workspace recorded (FLINT_DEV_* bits, 0 if none)
+ * into *flags. Returns FLINT_OK if flags == 0, FLINT_ERR_DEVICE_DATA if not,
+ * or another negative status if the arguments or the HIP calls fail.
+ */
+int flint_attn_device_status(const void* workspace, void* stream, int32_t* flags);
+
+/* A static, human-readable name of a flint_status value. */
+const char* flint_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLINT_ATTN_H */

@@ -1,0 +1,90 @@
+"""Helpers for GPU parity tests: run the HIP path and grade it against the oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import attention_head_rmsnorm_amd as fa
+
+from .common import f64, i64, oracle_for, seq_index
+
+MAX_ERR_FRAC = 2e-2   # max |O_gpu - O_oracle| <= 2e-2 * max|V|
+MEAN_ERR_FRAC = 1e-3  # mean |O_gpu - O_oracle| <= 1e-3 * max|V|
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def run_gpu(wl, layer, *, sinks=None, positions="keep", bshd=None, workspace=None, out=None):
+    """Runs the HIP path on a workload; returns the device output (THD [T, 32, 128])."""
+    d = dev()
+    q, k, v = wl.q.to(d), wl.k.to(d), wl.v.to(d)
+    qw, kw = wl.q_norm_w.to(d), wl.k_norm_w.to(d)
+    sk = (wl.sinks if sinks is None else torch.as_tensor(sinks, dtype=torch.float32)).to(d)
+    pos = wl.positions if isinstance(positions, str) else positions
+    pos = None if pos is None else torch.as_tensor(pos).to(torch.int32).to(d)
+    use_bshd = (wl.layout == "bshd") if bshd is None else bshd
+    kw_args = dict(window=layer.window, use_rope=layer.use_rope, rope_theta=layer.theta,
+                   eps=layer.eps, workspace=workspace)
+    if use_bshd:
+        B, S = wl.batch, wl.seqlen
+        mask = wl.attention_mask()
+        o = fa.flint_attn(q.view(B, S, 32, 128), k.view(B, S, 4, 128), v.view(B, S, 4, 128), qw, kw,
+                          sk, positions=None if pos is None else pos.view(B, S),
+                          attention_mask=None if mask is None else mask.to(d),
+                          out=None if out is None else out.view(B, S, 32, 128), **kw_args)
+        return o.view(B * S, 32, 128)
+    cu = wl.cu_seqlens.to(d)
+    su = None if wl.seqused is None else wl.seqused.to(d)
+    return fa.flint_attn(q, k, v, qw, kw, sk, positions=pos, cu_seqlens=cu, seqused=su,
+                         max_seqlen=wl.max_seqlen, out=out, **kw_args)
+
+
+def valid_rows(wl):
+    T = wl.total_tokens
+    s, ell = seq_index(i64(wl.cu_seqlens), T)
+    if wl.seqused is None:
+        return np.ones(T, bool)
+    return ell < i64(wl.seqused)[s]
+
+
+def grade(got, ref, wl, rows=None, what=""):
+    """Asserts the tolerance on valid rows and exact zeros on padded rows.
+
+    got, ref: [len(rows), 32, 128] (rows=None: every token). Returns stats.
+    """
+    vmax = float(np.max(np.abs(f64(wl.v)))) if wl.v.numel() else 1.0
+    ok = valid_rows(wl)
+    if rows is not None:
+        ok = ok[np.asarray(rows)]
+    g = got.astype(np.float64)
+    err = np.abs(g[ok] - ref[ok])
+    max_err = float(err.max()) if err.size else 0.0
+    mean_err = float(err.mean()) if err.size else 0.0
+    stats = dict(max_err=max_err, mean_err=mean_err, vmax=vmax,
+                 max_frac=max_err / vmax, mean_frac=mean_err / vmax, rows=int(ok.sum()))
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    assert max_err <= MAX_ERR_FRAC * vmax, f"{what}: max err {max_err:.4g} > {MAX_ERR_FRAC}*{vmax:.4g}"
+    assert mean_err <= MEAN_ERR_FRAC * vmax, f"{what}: mean err {mean_err:.4g} > {MEAN_ERR_FRAC}*{vmax:.4g}"
+    if (~ok).any():
+        assert np.all(g[~ok] == 0.0), f"{what}: padded rows are not exact zeros"
+    return stats
+
+
+def to_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_against_oracle(wl, layer, rows=None, **gpu_kw):
+    out = run_gpu(wl, layer, **gpu_kw)
+    torch.cuda.synchronize()
+    got = to_np(out if rows is None else out[torch.as_tensor(rows, device=out.device)])
+    sinks = gpu_kw.get("sinks")
+    over = {} if sinks is None else {"sinks": np.asarray(sinks, np.float64)}
+    pos = gpu_kw.get("positions", "keep")
+    if not isinstance(pos, str):
+        over["positions"] = None if pos is None else i64(torch.as_tensor(pos))
+    ref = oracle_for(wl, layer, rows=rows, **over)
+    return grade(got, ref, wl, rows=rows, what=f"{wl.name}/{layer.name}"), out

@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path through the C ABI against the FP64 oracle.
+
+Tolerance: max |err| <= 2e-2 * max|V| and mean |err| <= 1e-3 * max|V| over
+valid rows (bf16 inputs and output, FP32 accumulation); padded rows must be
+exact zeros. Large workloads are compared on a seeded row sample, which is
+exact per row because each output row depends only on that row's query and
+its keys.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_head_rmsnorm_amd as fa
+from workload import Layer, make_custom, make_workload
+from workload.gen import FULL, SLIDING
+
+from .common import f64, i64, oracle_for, seq_index
+from .gpu_common import check_against_oracle, grade, run_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()
+    torch.cuda.init()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _rows_sample(wl, per_seq, seed, edges=()):
+    """Seeded row sample: first/last rows of each sequence, chosen edges, random rows."""
+    rng = np.random.default_rng(seed)
+    cu = i64(wl.cu_seqlens)
+    rows = []
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        L = b - a
+        u = L if wl.seqused is None else int(wl.seqused[s])
+        pick = set(range(min(L, 16)))
+        pick |= set(range(max(0, u - 16), u))
+        pick |= set(range(u, min(L, u + 8)))  # padded rows
+        pick |= {e for e in edges if e < L}
+        pick |= set(rng.integers(0, max(L, 1), size=per_seq).tolist()) if L else set()
+        rows += [a + x for x in pick if x < L]
+    return np.array(sorted(set(rows)), np.int64)
+
+
+# ----------------------------------------------------------------- small cases
+
+SMALL = [
+    ("one tile", make_custom(201, [40]), SLIDING),
+    ("several tiles sliding", make_custom(202, [700]), SLIDING),
+    ("several tiles full", make_custom(203, [333]), FULL),
+    ("ragged THD sliding", make_custom(204, [130, 1, 65, 300, 2], layout="thd"), SLIDING),
+    ("ragged THD full", make_custom(205, [130, 1, 65, 300, 2], layout="thd"), FULL),
+    ("BSHD trailing padding", make_custom(206, [256, 256, 256], layout="bshd", seqused=[256, 100, 0]),
+     SLIDING),
+    ("BSHD padding full", make_custom(207, [200, 200], layout="bshd", seqused=[1, 199]), FULL),
+    ("window 1", make_custom(208, [150]), Layer(window=1, use_rope=True)),
+    ("window 33", make_custom(209, [250], layout="thd"), Layer(window=33, use_rope=False)),
+    ("window 64", make_custom(210, [300]), Layer(window=64, use_rope=True)),
+    ("window 65 nope", make_custom(211, [300]), Layer(window=65, use_rope=False)),
+    ("random large positions", make_custom(212, [200], positions="random"), SLIDING),
+    ("no positions argument", make_custom(213, [90, 180], layout="thd", positions="none"), SLIDING),
+    ("strong sinks", make_custom(214, [260], sink_std=6.0), FULL),
+    ("theta 1e4", make_custom(215, [300]), Layer(window=513, use_rope=True, theta=1e4)),
+    ("tiny sequences", make_custom(216, [1, 2, 3, 31, 32, 33, 63, 64, 65], layout="thd"), SLIDING),
+]
+
+
+@pytest.mark.parametrize("name,wl,layer", SMALL, ids=[c[0] for c in SMALL])
+def test_small_parity(name, wl, layer):
+    _log(f"[gpu] small parity: {name} seed={wl.seed} T={wl.total_tokens}")
+    stats, _ = check_against_oracle(wl, layer)
+    _log(f"      {stats}")
+
+
+def test_sink_minus_inf():
+    wl = make_custom(220, [300, 45], layout="thd")
+    _log("[gpu] sink = -inf")
+    for layer in (SLIDING, FULL):
+        check_against_oracle(wl, layer, sinks=np.full(32, -np.inf, np.float32))
+
+
+def test_sink_large_gives_zero_output():
+    wl = make_custom(221, [200])
+    out = run_gpu(wl, SLIDING, sinks=np.full(32, 80.0, np.float32))
+    torch.cuda.synchronize()
+    assert float(out.float().abs().max()) < 1e-20
+
+
+def test_mixed_sinks_including_minus_inf():
+    wl = make_custom(222, [170, 3, 90], layout="thd")
+    s = np.random.default_rng(0).normal(0, 3, 32).astype(np.float32)
+    s[::5] = -np.inf
+    s[1] = 12.0
+    for layer in (SLIDING, FULL):
+        check_against_oracle(wl, layer, sinks=s)
+
+
+def test_zero_query_closed_form():
+    """q = 0 makes every allowed logit 0: O[t] = sum_A v / (e^sink + |A|)."""
+    wl = make_custom(223, [600], q_scale=0.0)
+    for layer in (SLIDING, FULL):
+        out = to_np(run_gpu(wl, layer))
+        v = f64(wl.v)
+        s = f64(wl.sinks)
+        cs = np.concatenate([np.zeros((1, 4, 128)), np.cumsum(v, 0)], 0)
+        ref = np.zeros_like(out)
+        for t in range(600):
+            lo = 0 if layer.window == 0 else max(0, t - layer.window + 1)
+            vs = cs[t + 1] - cs[lo]
+            n = t + 1 - lo
+            for h in range(32):
+                ref[t, h] = vs[h // 8] / (math.exp(s[h]) + n)
+        grade(out, ref, wl, what=f"q=0 {layer.name}")
+
+
+def test_nope_ignores_positions_bitwise():
+    wl = make_custom(224, [400, 100], layout="thd")
+    a = run_gpu(wl, FULL)
+    b = run_gpu(wl, FULL, positions=np.random.default_rng(3).integers(0, 262144, 500))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_thd_document_equals_alone_bitwise():
+    lengths = [300, 77, 513]
+    wl = make_custom(225, lengths, layout="thd")
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    for layer in (SLIDING, FULL):
+        packed = run_gpu(wl, layer)
+        for d, n in enumerate(lengths):
+            a, b = int(cu[d]), int(cu[d + 1])
+            one = make_custom(225, [n], layout="thd")
+            one.q, one.k, one.v = wl.q[a:b].clone(), wl.k[a:b].clone(), wl.v[a:b].clone()
+            one.positions = wl.positions[a:b].clone()
+            one.q_norm_w, one.k_norm_w, one.sinks = wl.q_norm_w, wl.k_norm_w, wl.sinks
+            alone = run_gpu(one, layer)
+            torch.cuda.synchronize()
+            assert torch.equal(packed[a:b], alone), f"document {d} {layer.name}"
+
+
+def test_deterministic_bitwise():
+    wl = make_custom(226, [900, 50], layout="thd")
+    for layer in (SLIDING, FULL):
+        a = run_gpu(wl, layer)
+        b = run_gpu(wl, layer)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_bshd_equals_thd():
+    wl = make_custom(227, [300, 300], layout="bshd", seqused=[300, 123])
+    for layer in (SLIDING, FULL):
+        a = run_gpu(wl, layer, bshd=True)
+        b = run_gpu(wl, layer, bshd=False)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_output_guard_bands_untouched():
+    """Writes stay inside out: a canary band around it survives."""
+    wl = make_custom(228, [257, 31], layout="thd")
+    T = wl.total_tokens
+    buf = torch.full(((T + 2) * 32 * 128,), 12345.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[32 * 128:(T + 1) * 32 * 128].view(T, 32, 128)
+    run_gpu(wl, SLIDING, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:32 * 128] == 12345.0) and torch.all(buf[(T + 1) * 32 * 128:] == 12345.0)
+
+
+def test_workspace_reuse_and_stale_content():
+    """A reused workspace holding another call's data gives the same result."""
+    wl1 = make_custom(229, [1000], layout="thd")
+    wl2 = make_custom(230, [64, 700], layout="thd")
+    nbytes = fa.flint_attn_workspace_bytes(1000, 2, 1000)
+    ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    r1 = run_gpu(wl2, SLIDING)
+    run_gpu(wl1, FULL, workspace=ws)
+    r2 = run_gpu(wl2, SLIDING, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(r1, r2)
+
+
+def test_invalid_cu_seqlens_reported_and_output_untouched():
+    wl = make_custom(231, [100, 100], layout="thd")
+    d = torch.device("cuda")
+    bad = torch.tensor([0, 120, 90], dtype=torch.int32, device=d)  # decreasing
+    out = torch.full((200, 32, 128), 7.0, dtype=torch.bfloat16, device=d)
+    nbytes = fa.flint_attn_workspace_bytes(200, 2, 200)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=d)
+    fa.flint_attn(wl.q.to(d), wl.k.to(d), wl.v.to(d), wl.q_norm_w.to(d), wl.k_norm_w.to(d),
+                  wl.sinks.to(d), cu_seqlens=bad, max_seqlen=200, out=out, workspace=ws)
+    st, flags = fa.flint_attn_device_status(ws.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FLINT_ERR_DEVICE_DATA and flags & 2 and flags & 4
+    assert torch.all(out == 7.0)
+    good = torch.tensor([0, 100, 200], dtype=torch.int32, device=d)
+    fa.flint_attn(wl.q.to(d), wl.k.to(d), wl.v.to(d), wl.q_norm_w.to(d), wl.k_norm_w.to(d),
+                  wl.sinks.to(d), cu_seqlens=good, max_seqlen=50, out=out, workspace=ws)
+    st, flags = fa.flint_attn_device_status(ws.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FLINT_ERR_DEVICE_DATA and flags == 8  # longer than max_seqlen
+    fa.flint_attn(wl.q.to(d), wl.k.to(d), wl.v.to(d), wl.q_norm_w.to(d), wl.k_norm_w.to(d),
+                  wl.sinks.to(d), cu_seqlens=good, max_seqlen=100, out=out, workspace=ws)
+    st, flags = fa.flint_attn_device_status(ws.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FLINT_OK and flags == 0
+
+
+def test_mask_helper():
+    d = torch.device("cuda")
+    m = torch.zeros(4, 50, dtype=torch.uint8, device=d)
+    m[0, :50] = 1
+    m[1, :7] = 1
+    m[3, :1] = 1
+    su = fa.seqused_from_mask(m)
+    assert su.tolist() == [50, 7, 0, 1]
+    m[2, 10] = 1  # a hole: not trailing padding
+    with pytest.raises(ValueError, match="THD"):
+        fa.seqused_from_mask(m)
+
+
+def test_empty_input():
+    d = torch.device("cuda")
+    q = torch.empty(0, 32, 128, dtype=torch.bfloat16, device=d)
+    k = torch.empty(0, 4, 128, dtype=torch.bfloat16, device=d)
+    w = torch.ones(128, device=d)
+    out = fa.flint_attn(q, k, k, w, w, torch.zeros(32, device=d),
+                        cu_seqlens=torch.zeros(1, dtype=torch.int32, device=d), max_seqlen=0)
+    assert out.shape == (0, 32, 128)
+
+
+# ----------------------------------------------------------------- named workloads
+
+
+def test_c1_full():
+    wl = make_workload("c1")
+    _log("[gpu] c1 full parity")
+    stats, _ = check_against_oracle(wl, wl.layers[0])
+    _log(f"      {stats}")
+
+
+def test_c2_full():
+    wl = make_workload("c2")
+    _log("[gpu] c2 full parity (massive v tokens, +8 sinks)")
+    stats, _ = check_against_oracle(wl, wl.layers[0])
+    _log(f"      {stats}")
+
+
+def test_c3_sampled():
+    wl = make_workload("c3")
+    rows = _rows_sample(wl, 96, 1004, edges=(31, 32, 511, 512, 513, 514, 543, 544, 1023, 1024))
+    _log(f"[gpu] c3 sampled parity rows={len(rows)}")
+    stats, _ = check_against_oracle(wl, wl.layers[0], rows=rows)
+    _log(f"      {stats}")
+
+
+@pytest.mark.parametrize("li", [0, 1], ids=["sliding", "full"])
+def test_c4_sampled(li):
+    wl = make_workload("c4")
+    rows = _rows_sample(wl, 24, 1005 + li, edges=(511, 512, 513))
+    _log(f"[gpu] c4 layer {li} sampled parity rows={len(rows)}")
+    stats, _ = check_against_oracle(wl, wl.layers[li], rows=rows)
+    _log(f"      {stats}")
+
+
+def test_tstar_sampled():
+    wl = make_workload("tstar")
+    rows = _rows_sample(wl, 96, 1007)
+    _log(f"[gpu] S=8192 full NoPE sampled parity rows={len(rows)}")
+    stats, _ = check_against_oracle(wl, wl.layers[0], rows=rows)
+    _log(f"      {stats}")
+
+
+def test_c5_sampled():
+    wl = make_workload("c5")
+    rows = _rows_sample(wl, 16, 1006)
+    _log(f"[gpu] c5 S=131072 sampled parity rows={len(rows)}")
+    stats, _ = check_against_oracle(wl, wl.layers[0], rows=rows)
+    _log(f"      {stats}")
