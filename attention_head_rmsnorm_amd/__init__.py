@@ -15,10 +15,15 @@ from .binding import (  # noqa: F401
     FLINT_ERR_VALUE,
     FLINT_ERR_WORKSPACE,
     FLINT_OK,
+    FLINT_PHASE_ALL,
+    FLINT_PHASE_ATTEND,
+    FLINT_PHASE_KV,
+    FLINT_PHASE_SCHEDULE,
     FlintError,
     flint_attn,
     flint_attn_device_status,
     flint_attn_fwd,
+    flint_attn_fwd_phases,
     flint_attn_seqused_from_mask,
     flint_attn_strerror,
     flint_attn_workspace_bytes,

@@ -32,9 +32,15 @@ FLINT_ERR_ALIGN = -6
 FLINT_ERR_HIP = -7
 FLINT_ERR_DEVICE_DATA = -8
 
+FLINT_PHASE_SCHEDULE = 1
+FLINT_PHASE_KV = 2
+FLINT_PHASE_ATTEND = 4
+FLINT_PHASE_ALL = 7
+
 EXPORTED = (
     "flint_attn_workspace_bytes",
     "flint_attn_fwd",
+    "flint_attn_fwd_phases",
     "flint_attn_seqused_from_mask",
     "flint_attn_device_status",
     "flint_attn_strerror",
@@ -68,6 +74,8 @@ def load_library() -> ctypes.CDLL:
     lib.flint_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                    i32, i32, f32, f32, vp, sz, vp, vp]
     lib.flint_attn_fwd.restype = ctypes.c_int
+    lib.flint_attn_fwd_phases.argtypes = lib.flint_attn_fwd.argtypes + [i32]
+    lib.flint_attn_fwd_phases.restype = ctypes.c_int
     lib.flint_attn_seqused_from_mask.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.flint_attn_seqused_from_mask.restype = ctypes.c_int
     lib.flint_attn_device_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
@@ -96,6 +104,19 @@ def flint_attn_fwd(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seq
                                              total_tokens, num_q_heads, num_kv_heads, head_dim,
                                              window, use_rope, rope_theta, eps, workspace,
                                              workspace_bytes, out, stream))
+
+
+def flint_attn_fwd_phases(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused,
+                          n_seqs, max_seqlen, total_tokens, num_q_heads, num_kv_heads, head_dim,
+                          window, use_rope, rope_theta, eps, workspace, workspace_bytes, out,
+                          stream, phases) -> int:
+    """flint_attn_fwd restricted to the FLINT_PHASE_* bits in ``phases``; returns the status."""
+    return int(load_library().flint_attn_fwd_phases(q, k, v, q_norm_w, k_norm_w, sink, positions,
+                                                    cu_seqlens, seqused, n_seqs, max_seqlen,
+                                                    total_tokens, num_q_heads, num_kv_heads,
+                                                    head_dim, window, use_rope, rope_theta, eps,
+                                                    workspace, workspace_bytes, out, stream,
+                                                    phases))
 
 
 def flint_attn_seqused_from_mask(mask, batch, seqlen, seqused, n_bad, stream) -> int:

@@ -20,12 +20,24 @@
 //                     zeros for padded keys; zero rows of `out` for padded
 //                     queries.
 //   attn_kernel       per (query block, kv head): 8 waves, one per query head
-//                     of the group, share each K/V tile staged in LDS. The
-//                     query prologue (RMSNorm, RoPE, softmax scale in log2
-//                     units, bf16) is fused in. S^T = K Q^T and O^T += V^T P^T
-//                     run on v_mfma_f32_32x32x16_bf16 with FP32 accumulation;
-//                     the streaming softmax starts from the sink (m = sink,
-//                     l = 1) and only visits tiles inside the causal window.
+//                     of the group, share each K/V tile, which arrives in a
+//                     3-stage LDS ring by direct global->LDS loads. The query
+//                     prologue (RMSNorm, RoPE, softmax scale in log2 units,
+//                     bf16) is fused in. S^T = K Q^T and O^T += V^T P^T run on
+//                     v_mfma_f32_32x32x16_bf16 with FP32 accumulation, over
+//                     the tiles inside the causal window only.
+//
+// Softmax shift. The QK RMSNorm bounds every logit: by Cauchy-Schwarz
+// s = q'.k' <= |q'| max|k'| = B for the rounded operands the MFMA multiplies.
+// A row whose bound B is small enough (B <= kStaticBound, log2 units) uses the
+// fixed shift M = max(sink, B): the MFMA accumulator starts at -M, so the
+// accumulator already holds s - M and P = exp2(acc) needs no running max, no
+// per-tile max reduction and no rescaling; every exp2 argument is <= 0 and
+// the largest key term stays above 2^-2B, far from underflow. Rows with a
+// larger bound take the streaming path, whose running max starts at the sink
+// (m = sink, l = 1) and rescales lazily. Both give softmax over
+// [sink, allowed logits] exactly up to rounding, since softmax is invariant to
+// the shift.
 
 #include <hip/hip_runtime.h>
 
@@ -53,14 +65,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Keep a stale running max until a tile's max exceeds it by this much (log2
 // units): exp2 values then stay below 2^8, and the final O / l is unchanged.
 constexpr float kRescaleSlack = 8.0f;
+// Largest logit bound (log2 units) that takes the fixed-shift path.
+constexpr float kStaticBound = 48.0f;
+constexpr int kStages = 3;  // LDS ring depth of the attention kernel
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 
 struct Ws {
   int* hdr;       // [0] device-data error bits, [1] key tiles, [2] query blocks
   double* omega;  // [64] RoPE frequencies theta^(-c/64)
   int4* seq;      // [n] {start, length, valid length, first tile}
+  unsigned* kmax; // [n] max |k'| over the sequence's keys (float bits)
   int* tbase;     // [n+1] first key tile of each sequence
   int* qbase;     // [n+1] first query block of each sequence
   int2* tiles;    // [ntmax] {sequence, tile in sequence}
@@ -70,7 +87,7 @@ struct Ws {
 };
 
 struct Layout {
-  size_t hdr, omega, seq, tbase, qbase, tiles, items, kv, total;
+  size_t hdr, omega, seq, kmax, tbase, qbase, tiles, items, kv, total;
   int64_t ntmax, nqmax;
 };
 
@@ -84,6 +101,7 @@ static Layout make_layout(int64_t T, int64_t n) {
   L.hdr = o;   o = align_up(o + 64 * sizeof(int), 256);
   L.omega = o; o = align_up(o + 64 * sizeof(double), 256);
   L.seq = o;   o = align_up(o + (size_t)n * sizeof(int4), 256);
+  L.kmax = o;  o = align_up(o + (size_t)n * sizeof(unsigned), 256);
   L.tbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
   L.qbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
   L.tiles = o; o = align_up(o + (size_t)L.ntmax * sizeof(int2), 256);
@@ -124,6 +142,33 @@ __device__ __forceinline__ void rope_cos_sin(int pos, double omega, float* c, fl
   rev -= rint(rev);
   sincosf((float)(rev * two_pi), s, c);
 }
+
+// acc + sum of the eight packed bf16 values in c (v_dot2 with (1, 1)).
+__device__ __forceinline__ float dot2_sum(const uint4& c, bf16x2_t ones, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, c.x), ones, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, c.y), ones, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, c.z), ones, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, c.w), ones, acc, false);
+  return acc;
+}
+
+// Sum of squares of eight packed bf16 values.
+__device__ __forceinline__ float sumsq8(const uint4& c) {
+  float x[8];
+  unpack8(c, x);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i] * x[i];
+  return s;
+}
+
+// LDS layouts of one tile (each row's 16-byte chunks permuted so that the
+// MFMA operand reads of 8 or 16 consecutive rows at one logical chunk hit
+// distinct banks, for 32 or 64 banks of 4 bytes):
+//   K' tile  [64 keys][16 chunks of 8 channels], chunk c of row r at c ^ (r & 15)
+//   V^T tile [128 channels][8 chunks of 8 keys],  chunk c of row d at c ^ vt_swizzle(d)
+__device__ __forceinline__ int k_swizzle(int r) { return r & 15; }
+__device__ __forceinline__ int vt_swizzle(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
 // Exclusive scan over the 1024 threads of a block; *total gets the sum.
 __device__ int block_excl_scan(int v, int* tmp, int* total) {
@@ -204,6 +249,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ 
     const int ex_t = block_excl_scan(nt, tmp, &tot_t);
     const int ex_q = block_excl_scan(nq, tmp, &tot_q);
     if (s < n) {
+      ws.kmax[s] = 0u;
       ws.seq[s] = make_int4(a, len, u, carry_t + ex_t);
       ws.tbase[s] = carry_t + ex_t;
       ws.qbase[s] = carry_q + ex_q;
@@ -327,11 +373,17 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
   }
   {
     uint4* krow = reinterpret_cast<uint4*>(tile + r * (kD * 2));
-    const int sw = r & 15;
-    krow[(2 * p) ^ sw] = pack8(x);
-    krow[(2 * p + 1) ^ sw] = pack8(x + 8);
-    krow[(8 + 2 * p) ^ sw] = pack8(x + 16);
-    krow[(9 + 2 * p) ^ sw] = pack8(x + 24);
+    const int sw = k_swizzle(r);
+    const uint4 w0 = pack8(x), w1 = pack8(x + 8), w2 = pack8(x + 16), w3 = pack8(x + 24);
+    krow[(2 * p) ^ sw] = w0;
+    krow[(2 * p + 1) ^ sw] = w1;
+    krow[(8 + 2 * p) ^ sw] = w2;
+    krow[(9 + 2 * p) ^ sw] = w3;
+    // |k'| of the rounded key, for the logit bound of the attention kernel
+    float n2 = sumsq8(w0) + sumsq8(w1) + sumsq8(w2) + sumsq8(w3);
+    n2 += __shfl_xor(n2, 1);
+    n2 += __shfl_xor(n2, 2);
+    if (p == 0 && valid) atomicMax(&ws.kmax[te.x], __float_as_uint(sqrtf(n2)));
   }
 
   // V: transpose through LDS; this thread owns channels [32p, 32p+32) of key r.
@@ -364,7 +416,7 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
     for (int i = 0; i < 4; ++i) {
       const int qv = tid + 256 * i;
       const int d = qv >> 3, c = qv & 7;
-      vtile[d * 8 + (c ^ (d & 7))] = *reinterpret_cast<const uint4*>(&vt[d * kBN + c * 8]);
+      vtile[d * 8 + (c ^ vt_swizzle(d))] = *reinterpret_cast<const uint4*>(&vt[d * kBN + c * 8]);
     }
   }
 
@@ -379,13 +431,38 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
 
 // ----------------------------------------------------------------- attention
 
+// Direct global->LDS copy of one 32 KiB tile into an LDS stage: each of the
+// 512 threads moves four 16-byte vectors; global_load_lds writes lane L's
+// vector at the wave-uniform LDS base + 16 L, so the tile lands in LDS with
+// the same (already swizzled) byte order it has in the workspace.
+__device__ __forceinline__ void load_tile_async(const uint4* src, uint4* stage, int tid, int wave) {
+#pragma unroll
+  for (int i = 0; i < kTileVec / kAttnThreads; ++i) {
+    const int v0 = i * kAttnThreads + wave * 64;
+    __builtin_amdgcn_global_load_lds(
+        src + v0 + (tid & 63),
+        (__attribute__((address_space(3))) void*)(stage + v0), 16, 0, 0);
+  }
+}
+
+// Workgroup barrier for the tile ring. Each wave first waits until at most
+// `keep` of its vector-memory loads are in flight (0, or 4 = the one tile
+// still streaming in) and its LDS reads are done; after the barrier every
+// wave's part of the older tiles is in LDS and nobody reads the stage that
+// the next load overwrites. Unlike __syncthreads() this does not wait for the
+// newest tile's loads.
+__device__ __forceinline__ void ring_barrier(bool keep_one_tile) {
+  if (keep_one_tile) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __restrict__ q,
                                                             const float* __restrict__ q_norm_w,
                                                             const float* __restrict__ sink,
                                                             const int* __restrict__ positions,
                                                             int window, int use_rope, float eps,
                                                             Ws ws, uint16_t* __restrict__ out) {
-  __shared__ uint4 smem[2][kTileVec];
+  __shared__ uint4 smem[kStages][kTileVec];
   const int g = blockIdx.x & (kG - 1);
   const int e = blockIdx.x / kG;
   if (e >= ws.hdr[2]) return;
@@ -401,14 +478,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   const int tile_lo = klo / kBN;
   const int ntiles = (khi + kBN - 1) / kBN - tile_lo;
   const uint4* kvbase =
-      reinterpret_cast<const uint4*>(ws.kv + ((size_t)g * ws.ntmax + meta.w) * kTileBytes);
+      reinterpret_cast<const uint4*>(ws.kv + ((size_t)g * ws.ntmax + meta.w) * kTileBytes) +
+      (size_t)tile_lo * kTileVec;
 
-  uint4 pre[kTileVec / kAttnThreads];
-  {
-    const uint4* src = kvbase + (size_t)tile_lo * kTileVec;
-#pragma unroll
-    for (int i = 0; i < kTileVec / kAttnThreads; ++i) pre[i] = src[tid + kAttnThreads * i];
-  }
+  load_tile_async(kvbase, smem[0], tid, wave);
+  if (ntiles > 1) load_tile_async(kvbase + kTileVec, smem[1], tid, wave);
 
   // Query prologue: lane (col, half) holds channels 16kk + 8half + [0,8) of
   // token t0 + col, which is the MFMA B-operand layout of Q^T.
@@ -416,6 +490,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   const bool qvalid = qrow < u;
   const size_t tq = (size_t)start + qrow;
   bf16x8 qf[8];
+  float qnorm;
   {
     float x[64];
     if (qvalid) {
@@ -450,44 +525,63 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     }
     // logits in log2 units: q . k / sqrt(128) * log2(e)
     const float scale = kLog2e * 0.08838834764831845f;
+    float n2 = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[8 * kk + j] *= scale;
-      qf[kk] = __builtin_bit_cast(bf16x8, pack8(x + 8 * kk));
+      const uint4 w = pack8(x + 8 * kk);
+      n2 += sumsq8(w);
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
     }
+    n2 += __shfl_xor(n2, 32);
+    qnorm = sqrtf(n2);
   }
 
-#pragma unroll
-  for (int i = 0; i < kTileVec / kAttnThreads; ++i) smem[0][tid + kAttnThreads * i] = pre[i];
-  __syncthreads();
-
-  float m = sink[h] * kLog2e;                    // running max, seeded by the sink
-  float l = (half == 0 && m != -INFINITY) ? 1.f : 0.f;  // exp2(sink - m), counted once per query
+  // Softmax shift (see the file header): fixed when the logit bound allows.
+  const float sk = sink[h] * kLog2e;
+  const float bound = qnorm * __uint_as_float(ws.kmax[item.x]) * 1.0001f;
+  const bool online = __any(!(bound <= kStaticBound));
+  float m = online ? sk : fmaxf(sk, bound);  // current shift (-INF only when online)
+  float l = (half == 0 && sk != -INFINITY) ? __builtin_amdgcn_exp2f(sk - m) : 0.f;
+  float l1 = 0.f;
   f32x16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+
+  ring_barrier(ntiles > 1);
+
+  // -m in every lane of a 16-register vector: the first MFMA of each logit
+  // block starts from it, so the accumulator holds s - m.
+  f32x16 sinit;
+  {
+    const float mref = m == -INFINITY ? 0.f : m;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sinit[i] = -mref;
+  }
 
   for (int it = 0; it < ntiles; ++it) {
     const int j = tile_lo + it;
-    const bool more = it + 1 < ntiles;
-    if (more) {
-      const uint4* src = kvbase + (size_t)(j + 1) * kTileVec;
-#pragma unroll
-      for (int i = 0; i < kTileVec / kAttnThreads; ++i) pre[i] = src[tid + kAttnThreads * i];
-    }
-    const uint4* kt = smem[it & 1];
-    const uint4* vt = smem[it & 1] + kTileVec / 2;
+    if (it + 2 < ntiles) load_tile_async(kvbase + (size_t)(it + 2) * kTileVec, smem[(it + 2) % kStages], tid, wave);
+    const uint4* kt = smem[it % kStages];
+    const uint4* vt = kt + kTileVec / 2;
 
-    // S^T[key, query] for keys [0,32) and [32,64) of the tile
+    // S^T[key, query] - m for keys [0,32) and [32,64) of the tile
+    const float mref = m == -INFINITY ? 0.f : m;
     f32x16 s0, s1;
+    const int ksw = k_swizzle(col);
+    {
+      const int ch = half ^ ksw;
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, kt[col * 16 + ch]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, kt[(32 + col) * 16 + ch]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[0], sinit, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[0], sinit, 0, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
-    const int ksw = col & 15;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 1; kk < 8; ++kk) {
       const int ch = (2 * kk + half) ^ ksw;
       const bf16x8 a0 = __builtin_bit_cast(bf16x8, kt[col * 16 + ch]);
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, kt[(32 + col) * 16 + ch]);
@@ -510,78 +604,89 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
       }
     }
 
-    float mx = s0[0];
+    if (online) {
+      float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[i]);
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = (m == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
+      if (__any(need)) {
+        const float delta = need ? mx : 0.f;
+        const float alpha = need ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-delta)) : 1.f;
+        m = need ? mref + delta : m;
+        const float mref2 = m == -INFINITY ? 0.f : m;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const bool resc = m_new > m + kRescaleSlack;
-    if (__any(resc)) {
-      const float alpha = resc ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-      m = resc ? m_new : m;
-      l *= alpha;
+        for (int i = 0; i < 16; ++i) sinit[i] = -mref2;
+        l *= alpha;
+        l1 *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { s0[i] -= delta; s1[i] -= delta; }
+      }
     }
-    const float msub = m == -INFINITY ? 0.f : m;
 
+    // P = exp2(S - m) in bf16 (the MFMA B operand); l sums the same rounded values
     bf16x8 pk[4];
     {
       float p[16];
-      float ls = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(s0[i] - msub);
-        ls += p[i];
-      }
-      pk[0] = __builtin_bit_cast(bf16x8, pack8(p));
-      pk[1] = __builtin_bit_cast(bf16x8, pack8(p + 8));
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(s0[i]);
+      const uint4 w0 = pack8(p), w1 = pack8(p + 8);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(s1[i] - msub);
-        ls += p[i];
-      }
-      pk[2] = __builtin_bit_cast(bf16x8, pack8(p));
-      pk[3] = __builtin_bit_cast(bf16x8, pack8(p + 8));
-      l += ls;
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(s1[i]);
+      const uint4 w2 = pack8(p), w3 = pack8(p + 8);
+      pk[0] = __builtin_bit_cast(bf16x8, w0);
+      pk[1] = __builtin_bit_cast(bf16x8, w1);
+      pk[2] = __builtin_bit_cast(bf16x8, w2);
+      pk[3] = __builtin_bit_cast(bf16x8, w3);
+      l = dot2_sum(w0, ones, l);
+      l1 = dot2_sum(w1, ones, l1);
+      l = dot2_sum(w2, ones, l);
+      l1 = dot2_sum(w3, ones, l1);
     }
 
     // O^T[d, query] += V^T[d, keys] P^T[keys, query]
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int row = 32 * db + col;
+      const int vsw = vt_swizzle(row);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, vt[row * 8 + ((2 * kk + half) ^ (row & 7))]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, vt[row * 8 + ((2 * kk + half) ^ vsw)]);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], acc[db], 0, 0, 0);
       }
     }
 
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < kTileVec / kAttnThreads; ++i)
-        smem[(it + 1) & 1][tid + kAttnThreads * i] = pre[i];
-    }
-    __syncthreads();
+    ring_barrier(it + 2 < ntiles);
   }
 
-  const float lt = l + __shfl_xor(l, 32);
+  // Epilogue: O = acc / l, staged through LDS so each token row (256 bytes of
+  // one head) leaves in full 16-byte vectors.
+  const float lt = (l + l1) + __shfl_xor(l + l1, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (qvalid) {
-    uint16_t* dst = out + (tq * kH + h) * kD;
+  uint2* orow = reinterpret_cast<uint2*>(reinterpret_cast<char*>(&smem[0][0]) + wave * (kBM * kD * 2));
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d = 32 * db + 8 * rg + 4 * half;
-        const uint2 w = make_uint2(pack2(acc[db][4 * rg] * inv, acc[db][4 * rg + 1] * inv),
-                                   pack2(acc[db][4 * rg + 2] * inv, acc[db][4 * rg + 3] * inv));
-        *reinterpret_cast<uint2*>(dst + d) = w;
-      }
+    for (int rg = 0; rg < 4; ++rg) {
+      const int chunk = (4 * db + rg) ^ k_swizzle(col);
+      const uint2 w = make_uint2(pack2(acc[db][4 * rg] * inv, acc[db][4 * rg + 1] * inv),
+                                 pack2(acc[db][4 * rg + 2] * inv, acc[db][4 * rg + 3] * inv));
+      orow[col * 32 + chunk * 2 + half] = w;
+    }
+  __syncthreads();
+  const uint4* ostage = reinterpret_cast<const uint4*>(orow);
+#pragma unroll
+  for (int i = 0; i < kBM * 16 / 64; ++i) {
+    const int idx = i * 64 + lane;
+    const int r = idx >> 4, c = idx & 15;
+    if (t0 + r < u) {
+      const uint4 w = ostage[r * 16 + (c ^ k_swizzle(r))];
+      reinterpret_cast<uint4*>(out + (((size_t)start + t0 + r) * kH + h) * kD)[c] = w;
+    }
   }
 }
 
@@ -665,13 +770,16 @@ extern "C" int flint_attn_device_status(const void* workspace, void* stream, int
   return host ? FLINT_ERR_DEVICE_DATA : FLINT_OK;
 }
 
-extern "C" int flint_attn_fwd(const void* q, const void* k, const void* v, const float* q_norm_w,
-                              const float* k_norm_w, const float* sink, const int32_t* positions,
-                              const int32_t* cu_seqlens, const int32_t* seqused, int32_t n_seqs,
-                              int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t window,
-                              int32_t use_rope, float rope_theta, float eps, void* workspace,
-                              size_t workspace_bytes, void* out, void* stream) {
+extern "C" int flint_attn_fwd_phases(const void* q, const void* k, const void* v,
+                                     const float* q_norm_w, const float* k_norm_w,
+                                     const float* sink, const int32_t* positions,
+                                     const int32_t* cu_seqlens, const int32_t* seqused,
+                                     int32_t n_seqs, int32_t max_seqlen, int32_t total_tokens,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t window, int32_t use_rope, float rope_theta, float eps,
+                                     void* workspace, size_t workspace_bytes, void* out,
+                                     void* stream, int32_t phases) {
+  if (phases <= 0 || (phases & ~FLINT_PHASE_ALL)) return FLINT_ERR_VALUE;
   if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return FLINT_ERR_SHAPE;
   if (num_q_heads != kH || num_kv_heads != kG || head_dim != kD) return FLINT_ERR_UNSUPPORTED;
   if (window < 0 || !(eps > 0.f) || !isfinite(eps)) return FLINT_ERR_VALUE;
@@ -694,6 +802,7 @@ extern "C" int flint_attn_fwd(const void* q, const void* k, const void* v, const
   ws.hdr = reinterpret_cast<int*>(base + L.hdr);
   ws.omega = reinterpret_cast<double*>(base + L.omega);
   ws.seq = reinterpret_cast<int4*>(base + L.seq);
+  ws.kmax = reinterpret_cast<unsigned*>(base + L.kmax);
   ws.tbase = reinterpret_cast<int*>(base + L.tbase);
   ws.qbase = reinterpret_cast<int*>(base + L.qbase);
   ws.tiles = reinterpret_cast<int2*>(base + L.tiles);
@@ -710,18 +819,34 @@ extern "C" int flint_attn_fwd(const void* q, const void* k, const void* v, const
   const int* pos = rope ? positions : nullptr;
 
   (void)hipGetLastError();
-  schedule_kernel<<<1, 1024, 0, st>>>(cu_seqlens, seqused, n_seqs, total_tokens, max_seqlen,
-                                      window, (double)rope_theta, ws);
-  kv_prologue_kernel<<<dim3((unsigned)L.ntmax, kG), 256, 0, st>>>(kh, vh, k_norm_w, pos, eps, rope,
-                                                                  ws, oh);
-  attn_kernel<<<(unsigned)(L.nqmax * kG), kAttnThreads, 0, st>>>(qh, q_norm_w, sink, pos, window,
-                                                                 rope, eps, ws, oh);
+  if (phases & FLINT_PHASE_SCHEDULE)
+    schedule_kernel<<<1, 1024, 0, st>>>(cu_seqlens, seqused, n_seqs, total_tokens, max_seqlen,
+                                        window, (double)rope_theta, ws);
+  if (phases & FLINT_PHASE_KV)
+    kv_prologue_kernel<<<dim3((unsigned)L.ntmax, kG), 256, 0, st>>>(kh, vh, k_norm_w, pos, eps,
+                                                                    rope, ws, oh);
+  if (phases & FLINT_PHASE_ATTEND)
+    attn_kernel<<<(unsigned)(L.nqmax * kG), kAttnThreads, 0, st>>>(qh, q_norm_w, sink, pos,
+                                                                   window, rope, eps, ws, oh);
   if (hipGetLastError() != hipSuccess) return FLINT_ERR_HIP;
   if (debug_sync()) {
     int32_t flags = 0;
     return flint_attn_device_status(workspace, stream, &flags);
   }
   return FLINT_OK;
+}
+
+extern "C" int flint_attn_fwd(const void* q, const void* k, const void* v, const float* q_norm_w,
+                              const float* k_norm_w, const float* sink, const int32_t* positions,
+                              const int32_t* cu_seqlens, const int32_t* seqused, int32_t n_seqs,
+                              int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                              int32_t use_rope, float rope_theta, float eps, void* workspace,
+                              size_t workspace_bytes, void* out, void* stream) {
+  return flint_attn_fwd_phases(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused,
+                               n_seqs, max_seqlen, total_tokens, num_q_heads, num_kv_heads,
+                               head_dim, window, use_rope, rope_theta, eps, workspace,
+                               workspace_bytes, out, stream, FLINT_PHASE_ALL);
 }
 
 extern "C" int flint_attn_seqused_from_mask(const uint8_t* mask, int32_t batch, int32_t seqlen,

@@ -1,0 +1,281 @@
+"""Benchmark of the Flint sink-attention prefill on one MI355X.
+
+Metric: sink-attention prefill TFLOP/s counting only unmasked FLOPs (QK^T and
+PV: 4 * head_dim FLOPs per (query head, allowed key) pair, 32 query heads),
+and the attention kernel's fraction of the bf16 dense MFMA peak.
+
+Default workload: full-attention NoPE prefill, batch 1, S = 8192, 32 query /
+4 key-value heads, head dim 128, FP32 sinks ~N(0,1), bf16 inputs ~N(0,1) from
+a seeded generator, resident in HBM before the timed region. One step = one
+flint_attn_fwd call (schedule, K/V prologue, attention kernel).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config tstar|c1|c2|c3|c4|c4full|c5]
+       python bench.py --copy-probe     (plain device copy of known size, for
+                                          calibrating FETCH_SIZE / WRITE_SIZE)
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sink-attention prefill TFLOP/s (unmasked FLOPs) & % bf16 MFMA peak, 1 GPU"
+BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "attention_head_rmsnorm_amd", "csrc", "flint_attn.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_kernel_s8192_full_nope_traffic.md")
+COPY_PROBE_BYTES = 1 << 30
+
+
+def unmasked_pairs(cu, seqused, window):
+    """Sum over valid tokens of the number of allowed keys."""
+    cu = np.asarray(cu, np.int64)
+    total = 0
+    for s in range(len(cu) - 1):
+        L = int(cu[s + 1] - cu[s])
+        u = L if seqused is None else int(seqused[s])
+        ell = np.arange(u, dtype=np.int64)
+        n = ell + 1 if window == 0 else np.minimum(ell + 1, window)
+        total += int(n.sum())
+    return total
+
+
+def pairs_of_rows(cu, seqused, window, rows):
+    cu = np.asarray(cu, np.int64)
+    rows = np.asarray(rows, np.int64)
+    s = np.searchsorted(cu, rows, side="right") - 1
+    ell = rows - cu[s]
+    u = (cu[s + 1] - cu[s]) if seqused is None else np.asarray(seqused, np.int64)[s]
+    n = np.where(ell < u, ell + 1 if window == 0 else np.minimum(ell + 1, window), 0)
+    return int(n.sum())
+
+
+def source_sha256():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profile():
+    """HBM bytes per attention-kernel launch from the committed PMC summary.
+
+    The summary records the kernel source hash it was taken with; a different
+    current source means the counters no longer describe this kernel -> None.
+    """
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    mh = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    mb = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not mh or not mb or mh.group(1) != source_sha256():
+        return None
+    return float(mb.group(1))
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, layer, budget_rows):
+    """Times the FP64 oracle on an evenly spaced row sample of the workload."""
+    from oracle import flint_attention
+
+    T = wl.total_tokens
+    step = max(1, T // budget_rows)
+    rows = np.arange(step // 2, T, step, dtype=np.int64)[:budget_rows]
+    args = dict(q=wl.q.double().numpy(), k=wl.k.double().numpy(), v=wl.v.double().numpy(),
+                q_norm_w=wl.q_norm_w.double().numpy(), k_norm_w=wl.k_norm_w.double().numpy(),
+                sinks=wl.sinks.double().numpy(), cu_seqlens=wl.cu_seqlens.numpy(),
+                seqused=None if wl.seqused is None else wl.seqused.numpy(),
+                positions=None if wl.positions is None else wl.positions.numpy(),
+                window=layer.window, use_rope=layer.use_rope, theta=layer.theta, eps=layer.eps)
+    t0 = time.perf_counter()
+    flint_attention(rows=rows, **args)
+    dt = time.perf_counter() - t0
+    pairs = pairs_of_rows(wl.cu_seqlens.numpy(), None if wl.seqused is None else wl.seqused.numpy(),
+                          layer.window, rows)
+    flops = 16384.0 * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} evenly spaced query rows of {T} (all 32 heads), "
+                      f"{pairs} unmasked token pairs, {dt:.2f} s, FP64 NumPy",
+            "seconds": dt}
+
+
+def copy_probe():
+    import torch
+
+    n = COPY_PROBE_BYTES // 2
+    x = torch.randn(n, device="cuda").to(torch.bfloat16)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="tstar")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import attention_head_rmsnorm_amd as fa
+    from workload import make_workload
+
+    cfg = args.config
+    li = 0
+    if cfg == "c4full":
+        cfg, li = "c4", 1
+    wl = make_workload(cfg)
+    layer = wl.layers[li]
+    dev = torch.device("cuda", 0)
+    fa.load_library()
+
+    q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
+    qw, kw, sk = wl.q_norm_w.to(dev), wl.k_norm_w.to(dev), wl.sinks.to(dev)
+    cu = wl.cu_seqlens.to(dev)
+    su = None if wl.seqused is None else wl.seqused.to(dev)
+    pos = None if wl.positions is None else wl.positions.to(dev)
+    T, n, mx = wl.total_tokens, wl.n_seqs, wl.max_seqlen
+    out = torch.empty_like(q)
+    nbytes = fa.flint_attn_workspace_bytes(T, n, mx)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+    p = lambda t: 0 if t is None else int(t.data_ptr())  # noqa: E731
+    call_args = [p(q), p(k), p(v), p(qw), p(kw), p(sk), p(pos), p(cu), p(su), n, mx, T, 32, 4, 128,
+                 layer.window, int(layer.use_rope), layer.theta, layer.eps, p(ws), nbytes, p(out), sh]
+
+    def step(ev=None):
+        if ev is None:
+            st = fa.flint_attn_fwd_phases(*call_args, fa.FLINT_PHASE_ALL)
+        else:
+            st = fa.flint_attn_fwd_phases(*call_args, fa.FLINT_PHASE_SCHEDULE | fa.FLINT_PHASE_KV)
+            ev[0].record(stream)
+            st |= fa.flint_attn_fwd_phases(*call_args, fa.FLINT_PHASE_ATTEND)
+            ev[1].record(stream)
+        if st != 0:
+            raise RuntimeError(f"flint_attn_fwd_phases failed: {fa.flint_attn_strerror(st)}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st, flags = fa.flint_attn_device_status(p(ws), sh)
+    if st != 0:
+        raise RuntimeError(f"device data error flags {flags}")
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / K
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    pairs = unmasked_pairs(wl.cu_seqlens.numpy(), None if wl.seqused is None else wl.seqused.numpy(),
+                           layer.window)
+    flops = 16384.0 * pairs
+    value = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    alg_bytes = 18432.0 * T
+    traffic = traffic_from_profile() if cfg == "tstar" else None
+    bound = "mfma" if layer.window == 0 else "mfma"
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v, N(1,0.1) norm weights, N(0,1) FP32 sinks)",
+        "config": {
+            "workload": wl.description,
+            "name": wl.name,
+            "layer": layer.name,
+            "batch": wl.batch if wl.layout == "bshd" else None,
+            "seq_len": wl.seqlen if wl.layout == "bshd" else None,
+            "total_tokens": T,
+            "n_seqs": n,
+            "window": layer.window,
+            "use_rope": layer.use_rope,
+            "q_heads": 32,
+            "kv_heads": 4,
+            "head_dim": 128,
+            "parallelism": "single GPU",
+        },
+        "pct_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
+        "unmasked_flops": flops,
+        "attn_kernel_ms": round(attn_ms, 5),
+        "prologue_ms": round(ms_step - attn_ms, 5),
+        "roofline": {
+            "bound": bound,
+            "achieved": round(attn_tflops, 3),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "attn_kernel",
+            "algorithmic_bytes": alg_bytes,
+            "algorithmic_GBs": round(alg_bytes / (attn_ms * 1e-3) / 1e9, 1),
+        },
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, layer, args.cpu_rows)
+        rec["cpu_baseline"] = {k2: (round(v2, 6) if isinstance(v2, float) else v2)
+                               for k2, v2 in cb.items() if k2 != "seconds"}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

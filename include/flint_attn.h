@@ -128,6 +128,30 @@ int flint_attn_fwd(const void* q, const void* k, const void* v, const float* q_n
                    float rope_theta, float eps, void* workspace, size_t workspace_bytes, void* out,
                    void* stream);
 
+/* Phases of flint_attn_fwd, in the order they must run on one stream. */
+#define FLINT_PHASE_SCHEDULE 1 /* check cu_seqlens/seqused; lay out tiles and query blocks */
+#define FLINT_PHASE_KV 2       /* normalize + rotate K, transpose V into the workspace;
+                                  zero the padded rows of out                        */
+#define FLINT_PHASE_ATTEND 4   /* the attention kernel; writes the valid rows of out  */
+#define FLINT_PHASE_ALL 7
+
+/*
+ * flint_attn_fwd split into its phases: the same arguments plus a bit set of
+ * FLINT_PHASE_* values; the selected phases are enqueued in order. Running
+ * the phases of one call in several calls (same arguments and workspace, same
+ * stream, in phase order) gives the same result as flint_attn_fwd; this lets
+ * a caller time or overlap the phases. FLINT_PHASE_KV and FLINT_PHASE_ATTEND
+ * read what the earlier phases left in the workspace. phases outside 1..7
+ * return FLINT_ERR_VALUE.
+ */
+int flint_attn_fwd_phases(const void* q, const void* k, const void* v, const float* q_norm_w,
+                          const float* k_norm_w, const float* sink, const int32_t* positions,
+                          const int32_t* cu_seqlens, const int32_t* seqused, int32_t n_seqs,
+                          int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                          int32_t use_rope, float rope_theta, float eps, void* workspace,
+                          size_t workspace_bytes, void* out, void* stream, int32_t phases);
+
 /*
  * Turns a binary BSHD attention mask into per-sequence valid lengths. The
  * mask is uint8 [batch, seqlen] (device), non-zero = valid token. TE's BSHD
