@@ -28,16 +28,15 @@
 //                     the tiles inside the causal window only.
 //
 // Softmax shift. The QK RMSNorm bounds every logit: by Cauchy-Schwarz
-// s = q'.k' <= |q'| max|k'| = B for the rounded operands the MFMA multiplies.
-// A row whose bound B is small enough (B <= kStaticBound, log2 units) uses the
-// fixed shift M = max(sink, B): the MFMA accumulator starts at -M, so the
-// accumulator already holds s - M and P = exp2(acc) needs no running max, no
-// per-tile max reduction and no rescaling; every exp2 argument is <= 0 and
-// the largest key term stays above 2^-2B, far from underflow. Rows with a
-// larger bound take the streaming path, whose running max starts at the sink
-// (m = sink, l = 1) and rescales lazily. Both give softmax over
-// [sink, allowed logits] exactly up to rounding, since softmax is invariant to
-// the shift.
+// |s| = |q'.k'| <= |q'| max|k'| = B for the rounded operands the MFMA
+// multiplies (s in log2 units). A wave whose rows all have B <= kStaticBound
+// needs no shift at all: P = exp2(s) stays within [2^-B, 2^B], far from FP32
+// and bf16 overflow and underflow, the sink adds exp2(sink) to the
+// denominator, and O = sum P v / l is the same ratio as with any shift. The
+// MFMA accumulators start at zero and P = exp2(acc) needs no running max, no
+// per-tile max reduction and no rescaling. Waves with a larger bound take the
+// streaming path: a running max that starts at the sink (m = sink, l = 1),
+// subtracted before exp2 and raised lazily with rescaling.
 
 #include <hip/hip_runtime.h>
 
@@ -65,9 +64,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Keep a stale running max until a tile's max exceeds it by this much (log2
 // units): exp2 values then stay below 2^8, and the final O / l is unchanged.
 constexpr float kRescaleSlack = 8.0f;
-// Largest logit bound (log2 units) that takes the fixed-shift path.
-constexpr float kStaticBound = 48.0f;
-constexpr int kStages = 3;  // LDS ring depth of the attention kernel
+// Largest logit bound (log2 units) that takes the unshifted path: P <= 2^56
+// and l <= 2^56 * 2^18 keys leave FP32 headroom for |v| up to ~2^50.
+constexpr float kStaticBound = 56.0f;
+constexpr int kStages = 4;  // LDS ring depth of the attention kernel
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
@@ -162,13 +162,20 @@ __device__ __forceinline__ float sumsq8(const uint4& c) {
   return s;
 }
 
-// LDS layouts of one tile (each row's 16-byte chunks permuted so that the
-// MFMA operand reads of 8 or 16 consecutive rows at one logical chunk hit
-// distinct banks, for 32 or 64 banks of 4 bytes):
-//   K' tile  [64 keys][16 chunks of 8 channels], chunk c of row r at c ^ (r & 15)
-//   V^T tile [128 channels][8 chunks of 8 keys],  chunk c of row d at c ^ vt_swizzle(d)
-__device__ __forceinline__ int k_swizzle(int r) { return r & 15; }
-__device__ __forceinline__ int vt_swizzle(int d) { return (d & 7) ^ ((d >> 3) & 1); }
+// Tile layout (workspace and LDS alike), in 16-byte vectors, "fragment
+// order": every MFMA operand fragment of the attention kernel is one run of
+// 64 vectors, vector `lane` being what MFMA lane `lane` = 32 half + col
+// supplies, so each operand read is one contiguous, conflict-free 1 KiB.
+//   K' part  [2 key blocks b][8 channel steps kk][64 lanes]:
+//            K'[32b + col][16kk + 8half .. +8)
+//   V^T part [4 channel blocks db][4 key steps kk][64 lanes]:
+//            V^T[32db + col][slots 16kk + 8half .. +8), slot s holding key vt_slot(s)
+__device__ __forceinline__ int frag_index(int blk, int steps, int kk, int half, int col) {
+  return (blk * steps + kk) * 64 + half * 32 + col;
+}
+
+// Swizzle of the 32-row x 256-byte output staging area (16-byte chunks).
+__device__ __forceinline__ int o_swizzle(int r) { return (r & 15) ^ ((r >> 4) & 1); }
 
 // Exclusive scan over the 1024 threads of a block; *total gets the sum.
 __device__ int block_excl_scan(int v, int* tmp, int* total) {
@@ -372,13 +379,13 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
     }
   }
   {
-    uint4* krow = reinterpret_cast<uint4*>(tile + r * (kD * 2));
-    const int sw = k_swizzle(r);
+    uint4* kfrag = reinterpret_cast<uint4*>(tile);
+    const int b = r >> 5, col = r & 31;
     const uint4 w0 = pack8(x), w1 = pack8(x + 8), w2 = pack8(x + 16), w3 = pack8(x + 24);
-    krow[(2 * p) ^ sw] = w0;
-    krow[(2 * p + 1) ^ sw] = w1;
-    krow[(8 + 2 * p) ^ sw] = w2;
-    krow[(9 + 2 * p) ^ sw] = w3;
+    kfrag[frag_index(b, 8, p, 0, col)] = w0;      // channels 16p .. 16p+7
+    kfrag[frag_index(b, 8, p, 1, col)] = w1;      // 16p+8 .. 16p+15
+    kfrag[frag_index(b, 8, 4 + p, 0, col)] = w2;  // 64+16p .. 64+16p+7
+    kfrag[frag_index(b, 8, 4 + p, 1, col)] = w3;  // 64+16p+8 .. 64+16p+15
     // |k'| of the rounded key, for the logit bound of the attention kernel
     float n2 = sumsq8(w0) + sumsq8(w1) + sumsq8(w2) + sumsq8(w3);
     n2 += __shfl_xor(n2, 1);
@@ -416,7 +423,8 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
     for (int i = 0; i < 4; ++i) {
       const int qv = tid + 256 * i;
       const int d = qv >> 3, c = qv & 7;
-      vtile[d * 8 + (c ^ vt_swizzle(d))] = *reinterpret_cast<const uint4*>(&vt[d * kBN + c * 8]);
+      vtile[frag_index(d >> 5, 4, c >> 1, c & 1, d & 31)] =
+          *reinterpret_cast<const uint4*>(&vt[d * kBN + c * 8]);
     }
   }
 
@@ -433,29 +441,154 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
 
 // Direct global->LDS copy of one 32 KiB tile into an LDS stage: each of the
 // 512 threads moves four 16-byte vectors; global_load_lds writes lane L's
-// vector at the wave-uniform LDS base + 16 L, so the tile lands in LDS with
-// the same (already swizzled) byte order it has in the workspace.
-__device__ __forceinline__ void load_tile_async(const uint4* src, uint4* stage, int tid, int wave) {
+// vector at the wave-uniform LDS base (M0) + 16 L, so the tile lands in LDS
+// with the byte order it has in the workspace. `src` and `stage` are uniform
+// and `wave` is a scalar, so the addresses are a scalar base plus a constant
+// per-lane offset.
+__device__ __forceinline__ void load_tile_async(const char* src, uint4* stage, int lane, int wave) {
 #pragma unroll
   for (int i = 0; i < kTileVec / kAttnThreads; ++i) {
     const int v0 = i * kAttnThreads + wave * 64;
     __builtin_amdgcn_global_load_lds(
-        src + v0 + (tid & 63),
+        reinterpret_cast<const uint4*>(src + (size_t)v0 * 16) + lane,
         (__attribute__((address_space(3))) void*)(stage + v0), 16, 0, 0);
   }
 }
 
 // Workgroup barrier for the tile ring. Each wave first waits until at most
-// `keep` of its vector-memory loads are in flight (0, or 4 = the one tile
-// still streaming in) and its LDS reads are done; after the barrier every
-// wave's part of the older tiles is in LDS and nobody reads the stage that
-// the next load overwrites. Unlike __syncthreads() this does not wait for the
-// newest tile's loads.
+// one tile of its direct-to-LDS loads (4 per thread) is still in flight, or
+// none, and its LDS reads are done. Unlike __syncthreads() it does not wait
+// for the newest tile's loads.
 __device__ __forceinline__ void ring_barrier(bool keep_one_tile) {
   if (keep_one_tile) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+struct RowState {
+  f32x16 acc[4];  // O^T accumulators: channels 32db + ..., query col
+  float m;        // streaming path: running max (log2 units), may be -INF
+  float l0, l1;   // partial denominators (this lane's keys)
+  bool online;    // streaming path for this wave
+};
+
+// S^T for the 64 keys of a tile: two 32x32 logit blocks, accumulators from
+// zero. Operand fragments are read four MFMAs ahead of their use.
+__device__ __forceinline__ void tile_logits(const uint4* kt, int lane, const bf16x8* qf,
+                                            f32x16& s0, f32x16& s1) {
+  bf16x8 f[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f[i] = __builtin_bit_cast(bf16x8, kt[((i & 1) * 8 + (i >> 1)) * 64 + lane]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first four reads
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + 4 < 16) {
+      const int j = i + 4;
+      f[j] = __builtin_bit_cast(bf16x8, kt[((j & 1) * 8 + (j >> 1)) * 64 + lane]);
+    }
+    const int kk = i >> 1;
+    if (i & 1) {
+      s1 = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[kk], f32x16{}, 0, 0, 0)
+                   : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[kk], s1, 0, 0, 0);
+    } else {
+      s0 = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[kk], f32x16{}, 0, 0, 0)
+                   : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[kk], s0, 0, 0, 0);
+    }
+    if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // this MFMA
+  }
+}
+
+// Mask, (streaming path) running max, and P = exp2(S - m) as the bf16 B
+// operand of the PV product; the denominators sum the same rounded values.
+__device__ __forceinline__ void tile_softmax(f32x16& s0, f32x16& s1, RowState& st, bf16x8* pk,
+                                             int k0, int t0, int qrow, int u, int window, int half) {
+  const bool need_mask =
+      (k0 + kBN - 1 > t0) || (k0 + kBN > u) || (window > 0 && t0 + kBM - 1 - k0 > window - 1);
+  if (need_mask) {
+    // allowed keys of this query: [lo, hi]; element i of block b holds key
+    // k0 + 32b + 4half + c_i with c_i = 8(i>>2) + (i&3)
+    const int hi = min(qrow, u - 1);
+    const int lo = window > 0 ? max(0, qrow - (window - 1)) : 0;
+    const int kb = k0 + 4 * half;
+    const bool empty = hi < lo;
+    const int a = empty ? (1 << 30) : lo - kb;
+    const unsigned range = empty ? 0u : (unsigned)(hi - lo);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 8 * (i >> 2) + (i & 3);
+      s0[i] = (unsigned)(c - a) <= range ? s0[i] : -INFINITY;
+      s1[i] = (unsigned)(c + 32 - a) <= range ? s1[i] : -INFINITY;
+    }
+  }
+  if (st.online) {
+    // s - m relative to the current (finite) shift; a -INF max means no
+    // shift yet, and the first finite tile max becomes the shift.
+    const float mref = st.m == -INFINITY ? 0.f : st.m;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] -= mref;
+      s1[i] -= mref;
+      mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = (st.m == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
+    if (__any(need)) {
+      const float delta = need ? mx : 0.f;
+      const float alpha = need ? (st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-delta)) : 1.f;
+      st.m = need ? mref + delta : st.m;
+      st.l0 *= alpha;
+      st.l1 *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.acc[db][i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { s0[i] -= delta; s1[i] -= delta; }
+    }
+  }
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(s0[i]);
+  const uint4 w0 = pack8(p), w1 = pack8(p + 8);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(s1[i]);
+  const uint4 w2 = pack8(p), w3 = pack8(p + 8);
+  pk[0] = __builtin_bit_cast(bf16x8, w0);
+  pk[1] = __builtin_bit_cast(bf16x8, w1);
+  pk[2] = __builtin_bit_cast(bf16x8, w2);
+  pk[3] = __builtin_bit_cast(bf16x8, w3);
+  st.l0 = dot2_sum(w0, ones, st.l0);
+  st.l1 = dot2_sum(w1, ones, st.l1);
+  st.l0 = dot2_sum(w2, ones, st.l0);
+  st.l1 = dot2_sum(w3, ones, st.l1);
+}
+
+// O^T[d, query] += V^T[d, keys] P^T[keys, query]; fragments read four
+// MFMAs ahead.
+__device__ __forceinline__ void tile_pv(const uint4* vt, int lane, const bf16x8* pk, RowState& st) {
+  bf16x8 f[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(bf16x8, vt[i * 64 + lane]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + 4 < 16) f[i + 4] = __builtin_bit_cast(bf16x8, vt[(i + 4) * 64 + lane]);
+    const int db = i >> 2, kk = i & 3;
+    st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], pk[kk], st.acc[db], 0, 0, 0);
+    if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+}
+
+// One work item = 32 query tokens x the 8 query heads of one kv head. The 8
+// waves (one per head) run in two groups, waves 0-3 (A) and 4-7 (B); the
+// hardware places waves w and w+4 on the same SIMD. Group B runs half a
+// tile behind group A, so on each SIMD one wave feeds the matrix cores while
+// the other runs its softmax. Tile k+2 streams into the 4-stage LDS ring
+// meanwhile.
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __restrict__ q,
                                                             const float* __restrict__ q_norm_w,
                                                             const float* __restrict__ sink,
@@ -469,20 +602,20 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   const int2 item = ws.items[e];
   const int4 meta = ws.seq[item.x];
   const int start = meta.x, u = meta.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int col = lane & 31, half = lane >> 5;
   const int h = g * kHpg + wave;
+  const bool group_b = wave >= 4;
   const int t0 = item.y * kBM;
   int klo, khi;
   block_keys(u, item.y, window, &klo, &khi);
   const int tile_lo = klo / kBN;
   const int ntiles = (khi + kBN - 1) / kBN - tile_lo;
-  const uint4* kvbase =
-      reinterpret_cast<const uint4*>(ws.kv + ((size_t)g * ws.ntmax + meta.w) * kTileBytes) +
-      (size_t)tile_lo * kTileVec;
+  const char* kvbase = ws.kv + ((size_t)g * ws.ntmax + meta.w + tile_lo) * kTileBytes;
 
-  load_tile_async(kvbase, smem[0], tid, wave);
-  if (ntiles > 1) load_tile_async(kvbase + kTileVec, smem[1], tid, wave);
+  load_tile_async(kvbase, smem[0], lane, wave);
+  if (ntiles > 1) load_tile_async(kvbase + kTileBytes, smem[1], lane, wave);
 
   // Query prologue: lane (col, half) holds channels 16kk + 8half + [0,8) of
   // token t0 + col, which is the MFMA B-operand layout of Q^T.
@@ -539,142 +672,56 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   }
 
   // Softmax shift (see the file header): fixed when the logit bound allows.
-  const float sk = sink[h] * kLog2e;
-  const float bound = qnorm * __uint_as_float(ws.kmax[item.x]) * 1.0001f;
-  const bool online = __any(!(bound <= kStaticBound));
-  float m = online ? sk : fmaxf(sk, bound);  // current shift (-INF only when online)
-  float l = (half == 0 && sk != -INFINITY) ? __builtin_amdgcn_exp2f(sk - m) : 0.f;
-  float l1 = 0.f;
-  f32x16 acc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-
-  ring_barrier(ntiles > 1);
-
-  // -m in every lane of a 16-register vector: the first MFMA of each logit
-  // block starts from it, so the accumulator holds s - m.
-  f32x16 sinit;
+  RowState st;
   {
-    const float mref = m == -INFINITY ? 0.f : m;
+    const float sk = sink[h] * kLog2e;
+    const float bound = qnorm * __uint_as_float(ws.kmax[item.x]) * 1.0001f;
+    st.online = __any(!(bound <= kStaticBound));
+    // the sink's share of the denominator, counted once per query (lane half 0)
+    st.m = st.online ? sk : 0.f;
+    st.l0 = (half == 0 && sk != -INFINITY) ? __builtin_amdgcn_exp2f(sk - st.m) : 0.f;
+    st.l1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sinit[i] = -mref;
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.acc[db][i] = 0.f;
   }
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int j = tile_lo + it;
-    if (it + 2 < ntiles) load_tile_async(kvbase + (size_t)(it + 2) * kTileVec, smem[(it + 2) % kStages], tid, wave);
-    const uint4* kt = smem[it % kStages];
-    const uint4* vt = kt + kTileVec / 2;
-
-    // S^T[key, query] - m for keys [0,32) and [32,64) of the tile
-    const float mref = m == -INFINITY ? 0.f : m;
-    f32x16 s0, s1;
-    const int ksw = k_swizzle(col);
-    {
-      const int ch = half ^ ksw;
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, kt[col * 16 + ch]);
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, kt[(32 + col) * 16 + ch]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[0], sinit, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[0], sinit, 0, 0, 0);
+  // Both groups run the same pipelined body - softmax and PV of tile k-1,
+  // then the logits of tile k - but group A passes the ring barrier just
+  // before the logits and group B at the top of the body. Between barriers k
+  // and k+1 group A therefore computes logits, softmax and PV of tile k while
+  // group B computes softmax and PV of tile k-1 and the logits of tile k.
+  f32x16 s0, s1;
+  bf16x8 pk[4];
+  for (int k = 0; k < ntiles; ++k) {
+    if (group_b) ring_barrier(k + 1 < ntiles);
+    if (k > 0) {
+      tile_softmax(s0, s1, st, pk, (tile_lo + k - 1) * kBN, t0, qrow, u, window, half);
+      tile_pv(smem[(k - 1) % kStages] + kTileVec / 2, lane, pk, st);
     }
-#pragma unroll
-    for (int kk = 1; kk < 8; ++kk) {
-      const int ch = (2 * kk + half) ^ ksw;
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, kt[col * 16 + ch]);
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, kt[(32 + col) * 16 + ch]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s1, 0, 0, 0);
-    }
-
-    const int k0 = j * kBN;
-    const bool need_mask =
-        (k0 + kBN - 1 > t0) || (k0 + kBN > u) || (window > 0 && t0 + kBM - 1 - k0 > window - 1);
-    if (need_mask) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        const bool ok0 = key <= qrow && key < u && (window == 0 || qrow - key <= window - 1);
-        const bool ok1 =
-            key + 32 <= qrow && key + 32 < u && (window == 0 || qrow - key - 32 <= window - 1);
-        s0[i] = ok0 ? s0[i] : -INFINITY;
-        s1[i] = ok1 ? s1[i] : -INFINITY;
-      }
-    }
-
-    if (online) {
-      float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool need = (m == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
-      if (__any(need)) {
-        const float delta = need ? mx : 0.f;
-        const float alpha = need ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-delta)) : 1.f;
-        m = need ? mref + delta : m;
-        const float mref2 = m == -INFINITY ? 0.f : m;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sinit[i] = -mref2;
-        l *= alpha;
-        l1 *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { s0[i] -= delta; s1[i] -= delta; }
-      }
-    }
-
-    // P = exp2(S - m) in bf16 (the MFMA B operand); l sums the same rounded values
-    bf16x8 pk[4];
-    {
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(s0[i]);
-      const uint4 w0 = pack8(p), w1 = pack8(p + 8);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(s1[i]);
-      const uint4 w2 = pack8(p), w3 = pack8(p + 8);
-      pk[0] = __builtin_bit_cast(bf16x8, w0);
-      pk[1] = __builtin_bit_cast(bf16x8, w1);
-      pk[2] = __builtin_bit_cast(bf16x8, w2);
-      pk[3] = __builtin_bit_cast(bf16x8, w3);
-      l = dot2_sum(w0, ones, l);
-      l1 = dot2_sum(w1, ones, l1);
-      l = dot2_sum(w2, ones, l);
-      l1 = dot2_sum(w3, ones, l1);
-    }
-
-    // O^T[d, query] += V^T[d, keys] P^T[keys, query]
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int row = 32 * db + col;
-      const int vsw = vt_swizzle(row);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, vt[row * 8 + ((2 * kk + half) ^ vsw)]);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kk], acc[db], 0, 0, 0);
-      }
-    }
-
-    ring_barrier(it + 2 < ntiles);
+    if (!group_b) ring_barrier(k + 1 < ntiles);  // tile k is in LDS; stage (k+2)%4 is free
+    if (k + 2 < ntiles)
+      load_tile_async(kvbase + (size_t)(k + 2) * kTileBytes, smem[(k + 2) % kStages], lane, wave);
+    tile_logits(smem[k % kStages], lane, qf, s0, s1);
   }
+  tile_softmax(s0, s1, st, pk, (tile_lo + ntiles - 1) * kBN, t0, qrow, u, window, half);
+  tile_pv(smem[(ntiles - 1) % kStages] + kTileVec / 2, lane, pk, st);
+  __syncthreads();
 
   // Epilogue: O = acc / l, staged through LDS so each token row (256 bytes of
   // one head) leaves in full 16-byte vectors.
-  const float lt = (l + l1) + __shfl_xor(l + l1, 32);
+  const float lsum = st.l0 + st.l1;
+  const float lt = lsum + __shfl_xor(lsum, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   uint2* orow = reinterpret_cast<uint2*>(reinterpret_cast<char*>(&smem[0][0]) + wave * (kBM * kD * 2));
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      const int chunk = (4 * db + rg) ^ k_swizzle(col);
-      const uint2 w = make_uint2(pack2(acc[db][4 * rg] * inv, acc[db][4 * rg + 1] * inv),
-                                 pack2(acc[db][4 * rg + 2] * inv, acc[db][4 * rg + 3] * inv));
+      const int chunk = (4 * db + rg) ^ o_swizzle(col);
+      const uint2 w = make_uint2(pack2(st.acc[db][4 * rg] * inv, st.acc[db][4 * rg + 1] * inv),
+                                 pack2(st.acc[db][4 * rg + 2] * inv, st.acc[db][4 * rg + 3] * inv));
       orow[col * 32 + chunk * 2 + half] = w;
     }
   __syncthreads();
@@ -684,7 +731,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     const int idx = i * 64 + lane;
     const int r = idx >> 4, c = idx & 15;
     if (t0 + r < u) {
-      const uint4 w = ostage[r * 16 + (c ^ k_swizzle(r))];
+      const uint4 w = ostage[r * 16 + (c ^ o_swizzle(r))];
       reinterpret_cast<uint4*>(out + (((size_t)start + t0 + r) * kH + h) * kD)[c] = w;
     }
   }
