@@ -75,9 +75,9 @@ typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 
 struct Ws {
   int* hdr;       // [0] device-data error bits, [1] key tiles, [2] query blocks
-  double* omega;  // [64] RoPE frequencies theta^(-c/64)
+  unsigned long long* rope_r;  // [64] theta^(-c/64) / (2 pi) as a 0.64 fixed-point fraction
   int4* seq;      // [n] {start, length, valid length, first tile}
-  unsigned* kmax; // [n] max |k'| over the sequence's keys (float bits)
+  float* tmax;    // [kG][ntmax] max |k'| over the keys of each tile
   int* tbase;     // [n+1] first key tile of each sequence
   int* qbase;     // [n+1] first query block of each sequence
   int2* tiles;    // [ntmax] {sequence, tile in sequence}
@@ -87,7 +87,7 @@ struct Ws {
 };
 
 struct Layout {
-  size_t hdr, omega, seq, kmax, tbase, qbase, tiles, items, kv, total;
+  size_t hdr, rope_r, seq, tmax, tbase, qbase, tiles, items, kv, total;
   int64_t ntmax, nqmax;
 };
 
@@ -99,9 +99,9 @@ static Layout make_layout(int64_t T, int64_t n) {
   L.nqmax = (T + kBM - 1) / kBM + n;
   size_t o = 0;
   L.hdr = o;   o = align_up(o + 64 * sizeof(int), 256);
-  L.omega = o; o = align_up(o + 64 * sizeof(double), 256);
+  L.rope_r = o; o = align_up(o + 64 * sizeof(unsigned long long), 256);
   L.seq = o;   o = align_up(o + (size_t)n * sizeof(int4), 256);
-  L.kmax = o;  o = align_up(o + (size_t)n * sizeof(unsigned), 256);
+  L.tmax = o;  o = align_up(o + (size_t)kG * L.ntmax * sizeof(float), 256);
   L.tbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
   L.qbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
   L.tiles = o; o = align_up(o + (size_t)L.ntmax * sizeof(int2), 256);
@@ -134,13 +134,16 @@ __device__ __forceinline__ uint4 pack8(const float* x) {
   return make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
 }
 
-// cos and sin of pos * omega, with the angle reduced to [-pi, pi] in FP64 so
-// that positions up to 2^18 keep full FP32 accuracy.
-__device__ __forceinline__ void rope_cos_sin(int pos, double omega, float* c, float* s) {
-  const double two_pi = 6.283185307179586476925286766559;
-  double rev = (double)pos * omega * (1.0 / two_pi);
-  rev -= rint(rev);
-  sincosf((float)(rev * two_pi), s, c);
+// cos and sin of the RoPE angle pos * omega_c. The angle in revolutions,
+// pos * omega_c / (2 pi), is reduced exactly: with R = omega_c / (2 pi) as a
+// 0.64 fixed-point fraction, pos * R mod 2^64 is the fractional revolution,
+// whose top 32 bits (as a signed value in [-1/2, 1/2)) feed the hardware
+// sine and cosine, which take revolutions and are accurate to ~1.3e-7.
+__device__ __forceinline__ void rope_cos_sin(int pos, unsigned long long r, float* c, float* s) {
+  const unsigned long long prod = (unsigned long long)(long long)pos * r;
+  const float rev = (float)(int)(unsigned)(prod >> 32) * 2.3283064365386963e-10f;  // 2^-32
+  *s = __builtin_amdgcn_sinf(rev);
+  *c = __builtin_amdgcn_cosf(rev);
 }
 
 // acc + sum of the eight packed bf16 values in c (v_dot2 with (1, 1)).
@@ -178,20 +181,31 @@ __device__ __forceinline__ int frag_index(int blk, int steps, int kk, int half, 
 __device__ __forceinline__ int o_swizzle(int r) { return (r & 15) ^ ((r >> 4) & 1); }
 
 // Exclusive scan over the 1024 threads of a block; *total gets the sum.
+// Wave-level shuffle scans, then a scan of the 16 wave totals.
 __device__ int block_excl_scan(int v, int* tmp, int* total) {
-  const int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int x = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += x;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  const int incl = tmp[tid];
-  *total = tmp[1023];
+  if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  return incl - v;
+  if (wave == 0) {
+    int w = lane < 16 ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int y = __shfl_up(w, off);
+      if (lane >= off) w += y;
+    }
+    if (lane < 16) tmp[lane] = w;
+  }
+  __syncthreads();
+  const int base = wave > 0 ? tmp[wave - 1] : 0;
+  *total = tmp[15];
+  __syncthreads();
+  return base + x - v;
 }
 
 // Largest s in [0, n) with base[s] <= e (base non-decreasing, base[0] = 0).
@@ -228,7 +242,11 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ 
   __shared__ int sflags;
   const int tid = threadIdx.x;
   if (tid == 0) sflags = 0;
-  if (tid < 64) ws.omega[tid] = pow(theta, -(double)tid / 64.0);
+  if (tid < 64) {
+    // theta^(-c/64) / (2 pi) < 1/(2 pi): scaled by 2^64 it fits an unsigned 64-bit integer
+    const double r = pow(theta, -(double)tid / 64.0) * 0.15915494309189533577;
+    ws.rope_r[tid] = (unsigned long long)(r * 18446744073709551616.0);
+  }
   __syncthreads();
 
   int flags = 0;
@@ -256,7 +274,6 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ 
     const int ex_t = block_excl_scan(nt, tmp, &tot_t);
     const int ex_q = block_excl_scan(nq, tmp, &tot_q);
     if (s < n) {
-      ws.kmax[s] = 0u;
       ws.seq[s] = make_int4(a, len, u, carry_t + ex_t);
       ws.tbase[s] = carry_t + ex_t;
       ws.qbase[s] = carry_q + ex_q;
@@ -333,6 +350,7 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
                                                           float eps, int use_rope, Ws ws,
                                                           uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t vt[kD * kBN];
+  __shared__ float red[4];
   const int e = blockIdx.x, g = blockIdx.y;
   if (e >= ws.hdr[1]) return;
   const int2 te = ws.tiles[e];
@@ -372,7 +390,7 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float c, s;
-      rope_cos_sin(pos, ws.omega[16 * p + i], &c, &s);
+      rope_cos_sin(pos, ws.rope_r[16 * p + i], &c, &s);
       const float a = x[i], b = x[16 + i];
       x[i] = a * c - b * s;
       x[16 + i] = b * c + a * s;
@@ -390,7 +408,11 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
     float n2 = sumsq8(w0) + sumsq8(w1) + sumsq8(w2) + sumsq8(w3);
     n2 += __shfl_xor(n2, 1);
     n2 += __shfl_xor(n2, 2);
-    if (p == 0 && valid) atomicMax(&ws.kmax[te.x], __float_as_uint(sqrtf(n2)));
+    // tile max of |k'|: wave max, then across the four waves
+    float kn = sqrtf(n2);
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) kn = fmaxf(kn, __shfl_xor(kn, off));
+    if ((tid & 63) == 0) red[tid >> 6] = kn;
   }
 
   // V: transpose through LDS; this thread owns channels [32p, 32p+32) of key r.
@@ -417,6 +439,8 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
     }
   }
   __syncthreads();
+  if (tid == 0)
+    ws.tmax[(size_t)g * ws.ntmax + meta.w + te.y] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   {
     uint4* vtile = reinterpret_cast<uint4*>(tile + kHalfTile);
 #pragma unroll
@@ -650,7 +674,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           float c, s;
-          rope_cos_sin(pos, ws.omega[16 * kk + 8 * half + j], &c, &s);
+          rope_cos_sin(pos, ws.rope_r[16 * kk + 8 * half + j], &c, &s);
           const float a = x[8 * kk + j], b = x[8 * (kk + 4) + j];
           x[8 * kk + j] = a * c - b * s;
           x[8 * (kk + 4) + j] = b * c + a * s;
@@ -671,11 +695,26 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     qnorm = sqrtf(n2);
   }
 
-  // Softmax shift (see the file header): fixed when the logit bound allows.
+  // max |k'| over the tiles this item visits (a block-wide max)
+  __shared__ float kred[kAttnThreads / 64];
+  {
+    const float* tm = ws.tmax + (size_t)g * ws.ntmax + meta.w + tile_lo;
+    float km = 0.f;
+    for (int i = tid; i < ntiles; i += kAttnThreads) km = fmaxf(km, tm[i]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) km = fmaxf(km, __shfl_xor(km, off));
+    if (lane == 0) kred[wave] = km;
+  }
+  __syncthreads();
+  float kmax = kred[0];
+#pragma unroll
+  for (int w = 1; w < kAttnThreads / 64; ++w) kmax = fmaxf(kmax, kred[w]);
+
+  // Softmax shift (see the file header): none when the logit bound allows.
   RowState st;
   {
     const float sk = sink[h] * kLog2e;
-    const float bound = qnorm * __uint_as_float(ws.kmax[item.x]) * 1.0001f;
+    const float bound = qnorm * kmax * 1.0001f;
     st.online = __any(!(bound <= kStaticBound));
     // the sink's share of the denominator, counted once per query (lane half 0)
     st.m = st.online ? sk : 0.f;
@@ -847,9 +886,9 @@ extern "C" int flint_attn_fwd_phases(const void* q, const void* k, const void* v
   char* base = static_cast<char*>(workspace);
   Ws ws;
   ws.hdr = reinterpret_cast<int*>(base + L.hdr);
-  ws.omega = reinterpret_cast<double*>(base + L.omega);
+  ws.rope_r = reinterpret_cast<unsigned long long*>(base + L.rope_r);
   ws.seq = reinterpret_cast<int4*>(base + L.seq);
-  ws.kmax = reinterpret_cast<unsigned*>(base + L.kmax);
+  ws.tmax = reinterpret_cast<float*>(base + L.tmax);
   ws.tbase = reinterpret_cast<int*>(base + L.tbase);
   ws.qbase = reinterpret_cast<int*>(base + L.qbase);
   ws.tiles = reinterpret_cast<int2*>(base + L.tiles);
