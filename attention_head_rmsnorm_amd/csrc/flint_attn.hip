@@ -496,9 +496,12 @@ struct RowState {
 };
 
 // S^T for the 64 keys of a tile: two 32x32 logit blocks, accumulators from
-// zero. Operand fragments are read four MFMAs ahead of their use.
+// zero. Operand fragments are read four MFMAs ahead of their use. When
+// `lsrc` is set, this wave's four direct-to-LDS loads of a later tile (into
+// `lstage`) are spread over the MFMAs, one after every fourth, so the loads
+// of all waves do not reach the texture unit in one burst.
 __device__ __forceinline__ void tile_logits(const uint4* kt, int lane, const bf16x8* qf,
-                                            f32x16& s0, f32x16& s1) {
+                                            f32x16& s0, f32x16& s1, const char* lsrc, uint4* lstage, int wave) {
   bf16x8 f[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -520,6 +523,12 @@ __device__ __forceinline__ void tile_logits(const uint4* kt, int lane, const bf1
     }
     if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // this MFMA
+    if ((i & 3) == 3 && lsrc) {
+      const int v0 = (i >> 2) * kAttnThreads + wave * 64;
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const uint4*>(lsrc + (size_t)v0 * 16) + lane,
+          (__attribute__((address_space(3))) void*)(lstage + v0), 16, 0, 0);
+    }
   }
 }
 
@@ -740,9 +749,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
       tile_pv(smem[(k - 1) % kStages] + kTileVec / 2, lane, pk, st);
     }
     if (!group_b) ring_barrier(k + 1 < ntiles);  // tile k is in LDS; stage (k+2)%4 is free
-    if (k + 2 < ntiles)
-      load_tile_async(kvbase + (size_t)(k + 2) * kTileBytes, smem[(k + 2) % kStages], lane, wave);
-    tile_logits(smem[k % kStages], lane, qf, s0, s1);
+    tile_logits(smem[k % kStages], lane, qf, s0, s1,
+                k + 2 < ntiles ? kvbase + (size_t)(k + 2) * kTileBytes : nullptr,
+                smem[(k + 2) % kStages], wave);
   }
   tile_softmax(s0, s1, st, pk, (tile_lo + ntiles - 1) * kBN, t0, qrow, u, window, half);
   tile_pv(smem[(ntiles - 1) % kStages] + kTileVec / 2, lane, pk, st);

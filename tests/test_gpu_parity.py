@@ -83,6 +83,17 @@ def test_small_parity(name, wl, layer):
     _log(f"      {stats}")
 
 
+@pytest.mark.parametrize("scale", [1.6, 2.2, 3.0])
+def test_large_logits_streaming_path(scale):
+    """Norm weights that push the logit bound past the unshifted range take the
+    streaming (running-max) path; sharp, near one-hot rows must still match."""
+    wl = make_custom(240 + int(scale * 10), [700, 130], layout="thd", norm_scale=scale)
+    _log(f"[gpu] large logits, norm weights x{scale}")
+    for layer in (SLIDING, FULL):
+        check_against_oracle(wl, layer)
+        check_against_oracle(wl, layer, sinks=np.full(32, -np.inf, np.float32))
+
+
 def test_sink_minus_inf():
     wl = make_custom(220, [300, 45], layout="thd")
     _log("[gpu] sink = -inf")

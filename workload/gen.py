@@ -193,13 +193,14 @@ def make_workload(name: str) -> Workload:
 
 def make_custom(seed: int, lengths: Sequence[int], *, layout: str = "thd", seqused=None,
                 layers=(SLIDING,), sink_std: float = 1.0, positions: str = "local",
-                q_scale: float = 1.0) -> Workload:
+                q_scale: float = 1.0, norm_scale: float = 1.0) -> Workload:
     """A small seeded workload for tests.
 
     ``lengths`` are sequence lengths (BSHD needs equal lengths). ``seqused``
     gives trailing-padding valid lengths. ``positions`` is "local" (index in the
     sequence, passed explicitly), "none" (argument left out) or "random"
-    (arbitrary non-negative integers).
+    (arbitrary non-negative integers). ``norm_scale`` multiplies both RMSNorm
+    weights (large weights give large logits).
     """
     rng = np.random.default_rng(seed)
     lengths = [int(x) for x in lengths]
@@ -208,6 +209,9 @@ def make_custom(seed: int, lengths: Sequence[int], *, layout: str = "thd", sequs
     if q_scale != 1.0:
         q *= np.float32(q_scale)
     qw, kw, sinks = _draw_params(rng, sink_std)
+    if norm_scale != 1.0:
+        qw = qw * np.float32(norm_scale)
+        kw = kw * np.float32(norm_scale)
     cu = np.zeros(len(lengths) + 1, np.int64)
     cu[1:] = np.cumsum(lengths)
     if positions == "local":
