@@ -139,7 +139,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="tstar")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
 
