@@ -15,28 +15,35 @@
 //                     64-token key tiles of every sequence and the 32-token
 //                     query blocks, and orders the blocks by decreasing work.
 //   kv_prologue_kernel  per (key tile, kv head): RMSNorm + RoPE of K in FP32,
-//                     one bf16 rounding, stored as an MFMA-ready swizzled tile;
-//                     V transposed and key-permuted into the PV operand order;
-//                     zeros for padded keys; zero rows of `out` for padded
-//                     queries.
-//   attn_kernel       per (query block, kv head): 8 waves, one per query head
-//                     of the group, share each K/V tile, which arrives in a
-//                     3-stage LDS ring by direct global->LDS loads. The query
-//                     prologue (RMSNorm, RoPE, softmax scale in log2 units,
-//                     bf16) is fused in. S^T = K Q^T and O^T += V^T P^T run on
-//                     v_mfma_f32_32x32x16_bf16 with FP32 accumulation, over
-//                     the tiles inside the causal window only.
+//                     one bf16 rounding, stored as an MFMA-ready tile in
+//                     operand-fragment order; V transposed and key-permuted
+//                     into the PV operand order; zeros for padded keys; zero
+//                     rows of `out` for padded queries; the kv head's largest
+//                     |k'| into the workspace header.
+//   attn_kernel       persistent: one workgroup per CU, each running a list
+//                     of work items (32 query tokens x the 8 query heads of one
+//                     kv head). Its 8 waves, one per query head, share each
+//                     K/V tile, which arrives in a 4-stage LDS ring by direct
+//                     global->LDS loads; the ring runs across item boundaries,
+//                     and the next item's query rows are fetched during the
+//                     current one. The query prologue (RMSNorm, RoPE, softmax
+//                     scale in log2 units, bf16) is fused in. S^T = K Q^T and
+//                     O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with FP32
+//                     accumulation, over the tiles inside the causal window
+//                     only.
 //
 // Softmax shift. The QK RMSNorm bounds every logit: by Cauchy-Schwarz
 // |s| = |q'.k'| <= |q'| max|k'| = B for the rounded operands the MFMA
 // multiplies (s in log2 units). A wave whose rows all have B <= kStaticBound
-// needs no shift at all: P = exp2(s) stays within [2^-B, 2^B], far from FP32
-// and bf16 overflow and underflow, the sink adds exp2(sink) to the
-// denominator, and O = sum P v / l is the same ratio as with any shift. The
-// MFMA accumulators start at zero and P = exp2(acc) needs no running max, no
-// per-tile max reduction and no rescaling. Waves with a larger bound take the
-// streaming path: a running max that starts at the sink (m = sink, l = 1),
-// subtracted before exp2 and raised lazily with rescaling.
+// (and whose sink stays within it too) needs no shift at all: P = exp2(s)
+// stays within [2^-B, 2^B], far from FP32 and bf16 overflow and underflow,
+// the sink adds exp2(sink) to the denominator, and O = sum P v / l is the
+// same ratio as with any shift. The MFMA accumulators start at zero and
+// P = exp2(acc) needs no running max, no per-tile max reduction and no
+// rescaling. Waves with a larger bound take the streaming path: a running max
+// that starts at the sink (m = sink, l = 1), subtracted before exp2 and
+// raised lazily with rescaling. max |k'| is taken over all keys of the kv
+// head, a bound for every item.
 
 #include <hip/hip_runtime.h>
 
@@ -68,16 +75,21 @@ constexpr float kRescaleSlack = 8.0f;
 // and l <= 2^56 * 2^18 keys leave FP32 headroom for |v| up to ~2^50.
 constexpr float kStaticBound = 56.0f;
 constexpr int kStages = 4;  // LDS ring depth of the attention kernel
+constexpr int kFragAhead = 4;
+constexpr int kHdrKMax = 4;  // header slots of the per-kv-head key-norm maxima  // MFMA operand fragments read ahead of their use
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs: 32-bit
+// data format, no swizzle, byte-granular range check against num_records.
+constexpr int kBufferWord3 = 0x00020000;
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 
 struct Ws {
-  int* hdr;       // [0] device-data error bits, [1] key tiles, [2] query blocks
+  int* hdr;       // [0] device-data error bits, [1] key tiles, [2] query blocks,
+                  // [kHdrKMax + g] max |k'| of kv head g (FP32 bits, set by the K/V prologue)
   unsigned long long* rope_r;  // [64] theta^(-c/64) / (2 pi) as a 0.64 fixed-point fraction
   int4* seq;      // [n] {start, length, valid length, first tile}
-  float* tmax;    // [kG][ntmax] max |k'| over the keys of each tile
   int* tbase;     // [n+1] first key tile of each sequence
   int* qbase;     // [n+1] first query block of each sequence
   int2* tiles;    // [ntmax] {sequence, tile in sequence}
@@ -87,7 +99,7 @@ struct Ws {
 };
 
 struct Layout {
-  size_t hdr, rope_r, seq, tmax, tbase, qbase, tiles, items, kv, total;
+  size_t hdr, rope_r, seq, tbase, qbase, tiles, items, kv, total;
   int64_t ntmax, nqmax;
 };
 
@@ -101,7 +113,6 @@ static Layout make_layout(int64_t T, int64_t n) {
   L.hdr = o;   o = align_up(o + 64 * sizeof(int), 256);
   L.rope_r = o; o = align_up(o + 64 * sizeof(unsigned long long), 256);
   L.seq = o;   o = align_up(o + (size_t)n * sizeof(int4), 256);
-  L.tmax = o;  o = align_up(o + (size_t)kG * L.ntmax * sizeof(float), 256);
   L.tbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
   L.qbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
   L.tiles = o; o = align_up(o + (size_t)L.ntmax * sizeof(int2), 256);
@@ -242,6 +253,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ 
   __shared__ int sflags;
   const int tid = threadIdx.x;
   if (tid == 0) sflags = 0;
+  if (tid < kG) ws.hdr[kHdrKMax + tid] = 0;
   if (tid < 64) {
     // theta^(-c/64) / (2 pi) < 1/(2 pi): scaled by 2^64 it fits an unsigned 64-bit integer
     const double r = pow(theta, -(double)tid / 64.0) * 0.15915494309189533577;
@@ -440,7 +452,8 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
   }
   __syncthreads();
   if (tid == 0)
-    ws.tmax[(size_t)g * ws.ntmax + meta.w + te.y] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(reinterpret_cast<unsigned*>(&ws.hdr[kHdrKMax + g]),
+              __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
   {
     uint4* vtile = reinterpret_cast<uint4*>(tile + kHalfTile);
 #pragma unroll
@@ -464,28 +477,47 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
 // ----------------------------------------------------------------- attention
 
 // Direct global->LDS copy of one 32 KiB tile into an LDS stage: each of the
-// 512 threads moves four 16-byte vectors; global_load_lds writes lane L's
-// vector at the wave-uniform LDS base (M0) + 16 L, so the tile lands in LDS
-// with the byte order it has in the workspace. `src` and `stage` are uniform
-// and `wave` is a scalar, so the addresses are a scalar base plus a constant
-// per-lane offset.
-__device__ __forceinline__ void load_tile_async(const char* src, uint4* stage, int lane, int wave) {
-#pragma unroll
-  for (int i = 0; i < kTileVec / kAttnThreads; ++i) {
-    const int v0 = i * kAttnThreads + wave * 64;
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const uint4*>(src + (size_t)v0 * 16) + lane,
-        (__attribute__((address_space(3))) void*)(stage + v0), 16, 0, 0);
-  }
+// 512 threads moves four 16-byte vectors with buffer_load ... lds, which
+// writes lane L's vector at the wave-uniform LDS base (M0) + 16 L, so the tile
+// lands in LDS with the byte order it has in the workspace. `rsrc` covers this
+// item's tiles only (reads past it return zeros), `tile_off` is the tile's
+// byte offset in it and `voff` = 16 lane + 1024 wave.
+__device__ __forceinline__ void load_vec_async(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
+                                               uint4* stage, int i, int wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc,
+      (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(stage) + i * 8192 + wave * 1024),
+      16, voff, soff + i * 8192, 0, 0);
 }
 
-// Workgroup barrier for the tile ring. Each wave first waits until at most
-// one tile of its direct-to-LDS loads (4 per thread) is still in flight, or
-// none, and its LDS reads are done. Unlike __syncthreads() it does not wait
-// for the newest tile's loads.
-__device__ __forceinline__ void ring_barrier(bool keep_one_tile) {
-  if (keep_one_tile) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+__device__ __forceinline__ void load_tile_async(__amdgpu_buffer_rsrc_t rsrc, int voff, int tile_off,
+                                                uint4* stage, int wave) {
+#pragma unroll
+  for (int i = 0; i < kTileVec / kAttnThreads; ++i) load_vec_async(rsrc, voff, tile_off, stage, i, wave);
+}
+
+// Workgroup barrier for the tile ring. Vector-memory operations complete in
+// issue order, so a wave whose tile loads were followed by exactly `n` more
+// vector-memory operations has that tile in LDS once at most `n` remain in
+// flight; the wave also finishes its LDS reads, then joins the barrier.
+// Unlike __syncthreads() this leaves the newer loads in flight.
+template <int N>
+__device__ __forceinline__ void ring_barrier_n() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Inside an item, from its third slot on, the only newer operations are the
+// next slot's loads (4) or none. An item's first two slots were loaded before
+// the item's query rows; loads complete in issue order, so waiting for those
+// rows (n = the operations issued since: output stores, 8, and the third
+// slot's loads, 4) waits for the slots as well.
+__device__ __forceinline__ void ring_barrier(int n) {
+  switch (n) {
+    case 4: ring_barrier_n<4>(); break;
+    case 8: ring_barrier_n<8>(); break;
+    case 12: ring_barrier_n<12>(); break;
+    default: ring_barrier_n<0>(); break;
+  }
 }
 
 struct RowState {
@@ -496,21 +528,23 @@ struct RowState {
 };
 
 // S^T for the 64 keys of a tile: two 32x32 logit blocks, accumulators from
-// zero. Operand fragments are read four MFMAs ahead of their use. When
-// `lsrc` is set, this wave's four direct-to-LDS loads of a later tile (into
-// `lstage`) are spread over the MFMAs, one after every fourth, so the loads
-// of all waves do not reach the texture unit in one burst.
+// zero. Operand fragments are read kFragAhead MFMAs ahead of their use. When
+// `load` is set, this wave's four direct-to-LDS loads of a later tile (byte
+// offset `loff`, into `lstage`) are spread over the MFMAs, one after every
+// fourth, so the loads of all waves do not reach the texture unit in one burst.
 __device__ __forceinline__ void tile_logits(const uint4* kt, int lane, const bf16x8* qf,
-                                            f32x16& s0, f32x16& s1, const char* lsrc, uint4* lstage, int wave) {
+                                            f32x16& s0, f32x16& s1, bool load,
+                                            __amdgpu_buffer_rsrc_t rsrc, int voff, int loff,
+                                            uint4* lstage, int wave) {
   bf16x8 f[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFragAhead; ++i)
     f[i] = __builtin_bit_cast(bf16x8, kt[((i & 1) * 8 + (i >> 1)) * 64 + lane]);
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first four reads
+  __builtin_amdgcn_sched_group_barrier(0x100, kFragAhead, 0);  // the first reads
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    if (i + 4 < 16) {
-      const int j = i + 4;
+    if (i + kFragAhead < 16) {
+      const int j = i + kFragAhead;
       f[j] = __builtin_bit_cast(bf16x8, kt[((j & 1) * 8 + (j >> 1)) * 64 + lane]);
     }
     const int kk = i >> 1;
@@ -521,14 +555,9 @@ __device__ __forceinline__ void tile_logits(const uint4* kt, int lane, const bf1
       s0 = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[kk], f32x16{}, 0, 0, 0)
                    : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[kk], s0, 0, 0, 0);
     }
-    if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // this MFMA
-    if ((i & 3) == 3 && lsrc) {
-      const int v0 = (i >> 2) * kAttnThreads + wave * 64;
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const uint4*>(lsrc + (size_t)v0 * 16) + lane,
-          (__attribute__((address_space(3))) void*)(lstage + v0), 16, 0, 0);
-    }
+    if (i + kFragAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // this MFMA
+    if ((i & 3) == 3 && load) load_vec_async(rsrc, voff, loff, lstage, i >> 2, wave);
   }
 }
 
@@ -599,29 +628,156 @@ __device__ __forceinline__ void tile_softmax(f32x16& s0, f32x16& s1, RowState& s
   st.l1 = dot2_sum(w3, ones, st.l1);
 }
 
-// O^T[d, query] += V^T[d, keys] P^T[keys, query]; fragments read four
-// MFMAs ahead.
+// O^T[d, query] += V^T[d, keys] P^T[keys, query]; fragments read
+// kFragAhead MFMAs ahead.
 __device__ __forceinline__ void tile_pv(const uint4* vt, int lane, const bf16x8* pk, RowState& st) {
   bf16x8 f[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(bf16x8, vt[i * 64 + lane]);
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  for (int i = 0; i < kFragAhead; ++i) f[i] = __builtin_bit_cast(bf16x8, vt[i * 64 + lane]);
+  __builtin_amdgcn_sched_group_barrier(0x100, kFragAhead, 0);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    if (i + 4 < 16) f[i + 4] = __builtin_bit_cast(bf16x8, vt[(i + 4) * 64 + lane]);
+    if (i + kFragAhead < 16)
+      f[i + kFragAhead] = __builtin_bit_cast(bf16x8, vt[(i + kFragAhead) * 64 + lane]);
     const int db = i >> 2, kk = i & 3;
     st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], pk[kk], st.acc[db], 0, 0, 0);
-    if (i + 4 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i + kFragAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
 }
 
-// One work item = 32 query tokens x the 8 query heads of one kv head. The 8
-// waves (one per head) run in two groups, waves 0-3 (A) and 4-7 (B); the
-// hardware places waves w and w+4 on the same SIMD. Group B runs half a
-// tile behind group A, so on each SIMD one wave feeds the matrix cores while
-// the other runs its softmax. Tile k+2 streams into the 4-stage LDS ring
-// meanwhile.
+// One work item = 32 query tokens x the 8 query heads of one kv head. A
+// workgroup keeps the list of its items in LDS as {sequence start, valid
+// length, first query, first tile of the sequence}; the rest follows.
+constexpr int kMaxItemsPerGroup = 1024;
+
+struct Item {
+  int start;    // first token of the sequence
+  int u;        // valid length of the sequence
+  int t0;       // first query of the block (index in the sequence)
+  int tile_lo;  // first key tile visited (index in the sequence)
+  int ntiles;   // key tiles visited
+  int tfirst;   // workspace tile index of tile tile_lo
+};
+
+__device__ __forceinline__ Item item_from(int4 e, int window) {
+  Item r;
+  r.start = __builtin_amdgcn_readfirstlane(e.x);
+  r.u = __builtin_amdgcn_readfirstlane(e.y);
+  r.t0 = __builtin_amdgcn_readfirstlane(e.z);
+  int klo, khi;
+  block_keys(r.u, r.t0 / kBM, window, &klo, &khi);
+  r.tile_lo = klo / kBN;
+  r.ntiles = (khi + kBN - 1) / kBN - r.tile_lo;
+  r.tfirst = __builtin_amdgcn_readfirstlane(e.w) + r.tile_lo;
+  return r;
+}
+
+// Item j of workgroup w among nw (per kv head): a snake over the list sorted
+// by decreasing work, ranks w, 2nw-1-w, 2nw+w, ..., so the workgroups' totals
+// stay close.
+__device__ __forceinline__ int item_rank(int j, int w, int nw) {
+  return j * nw + ((j & 1) ? nw - 1 - w : w);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tiles_rsrc(const Ws& ws, int g, int tfirst, int ntiles) {
+  const char* base = ws.kv + ((size_t)g * ws.ntmax + tfirst) * kTileBytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, ntiles * kTileBytes, kBufferWord3);
+}
+
+// The query rows of an item for head h, lane (col, half): channels
+// 16kk + 8half + [0, 8) of token t0 + col, and its RoPE position. Rows at or
+// past the valid length read as zeros (buffer range check), so the number of
+// vector-memory operations is fixed: 8, plus 1 when positions are read.
+struct QRaw {
+  uint4 x[8];
+  int pos;
+};
+
+__device__ __forceinline__ void load_q(const uint16_t* q, const int* positions, bool qpos,
+                                       const Item& it, int h, int col, int half, QRaw& r) {
+  const int rows = min(it.u - it.t0, kBM);
+  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(q + ((size_t)(it.start + it.t0) * kH + h) * kD), 0,
+      rows * (kH * kD * 2), kBufferWord3);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    r.x[kk] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, col * (kH * kD * 2) + (2 * kk + half) * 16, 0, 0));
+  r.pos = it.t0 + col;
+  if (qpos) {
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int*>(positions + it.start + it.t0), 0, rows * 4, kBufferWord3);
+    r.pos = (int)__builtin_amdgcn_raw_buffer_load_b32(pr, col * 4, 0, 0);
+  }
+}
+
+// Query prologue: RMSNorm, RoPE, softmax scale in log2 units and one bf16
+// rounding, in the MFMA B-operand layout of Q^T; qmax = max |q'| over the
+// wave's 32 queries.
+__device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw,
+                                           const unsigned long long* s_rope, bool rope, float eps,
+                                           int half, bf16x8* qf, float& qmax) {
+  // The weight and frequency tables are re-read from LDS for every item; the
+  // empty asm hides that the offset is zero, so the reads are not hoisted and
+  // held in registers across the tile loop.
+  int z = 0;
+  asm volatile("" : "+s"(z));
+  s_qw += z;
+  s_rope += z;
+  float ss = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) ss += sumsq8(qraw.x[kk]);
+  ss += __shfl_xor(ss, 32);
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+  const float scale = kLog2e * 0.08838834764831845f;
+  float n2 = 0.f;
+  // channels 16kk + 8half + j pair with 16(kk+4) + 8half + j under RoPE
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    float a[8], b[8];
+    unpack8(qraw.x[kk], a);
+    unpack8(qraw.x[kk + 4], b);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      a[jj] *= rstd * s_qw[16 * kk + 8 * half + jj];
+      b[jj] *= rstd * s_qw[16 * (kk + 4) + 8 * half + jj];
+    }
+    if (rope) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        float c, sn;
+        rope_cos_sin(qraw.pos, s_rope[16 * kk + 8 * half + jj], &c, &sn);
+        const float x = a[jj], y = b[jj];
+        a[jj] = x * c - y * sn;
+        b[jj] = y * c + x * sn;
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      a[jj] *= scale;
+      b[jj] *= scale;
+    }
+    const uint4 wa = pack8(a), wb = pack8(b);
+    n2 += sumsq8(wa) + sumsq8(wb);
+    qf[kk] = __builtin_bit_cast(bf16x8, wa);
+    qf[kk + 4] = __builtin_bit_cast(bf16x8, wb);
+  }
+  n2 += __shfl_xor(n2, 32);
+  qmax = sqrtf(n2);
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+  qmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qmax)));
+}
+
+// Persistent attention kernel: one workgroup per CU and kv head group, each
+// running its items back to back. The 8 waves (one per query head) run in two
+// groups, waves 0-3 (A) and 4-7 (B); the hardware places waves w and w+4 on
+// the same SIMD. Group B runs half a tile behind group A, so on each SIMD one
+// wave feeds the matrix cores while the other runs its softmax. Key tiles
+// flow through a 4-stage LDS ring that does not stop at item boundaries: the
+// tile two slots ahead streams in meanwhile, and the next item's query rows
+// are fetched while the current item runs.
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __restrict__ q,
                                                             const float* __restrict__ q_norm_w,
                                                             const float* __restrict__ sink,
@@ -629,103 +785,96 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
                                                             int window, int use_rope, float eps,
                                                             Ws ws, uint16_t* __restrict__ out) {
   __shared__ uint4 smem[kStages][kTileVec];
+  __shared__ float s_qw[kD];                    // q_norm weights
+  __shared__ unsigned long long s_rope[kD / 2];  // RoPE frequencies, 0.64 fixed point
+  __shared__ int4 s_items[kMaxItemsPerGroup];
   const int g = blockIdx.x & (kG - 1);
-  const int e = blockIdx.x / kG;
-  if (e >= ws.hdr[2]) return;
-  const int2 item = ws.items[e];
-  const int4 meta = ws.seq[item.x];
-  const int start = meta.x, u = meta.z;
+  const int wg = blockIdx.x / kG, nwg = gridDim.x / kG;
+  // Items of this workgroup: the snake's ranks grow with j, so they are the
+  // first nj; the last, partial round holds ranks below nitems only. The
+  // launch keeps nj within kMaxItemsPerGroup.
+  const int nitems = ws.hdr[2];
+  const int rounds = nitems / nwg, rem = nitems - rounds * nwg;
+  const int nj = min(rounds + (((rounds & 1) ? nwg - 1 - wg : wg) < rem ? 1 : 0), kMaxItemsPerGroup);
+  if (nj == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int col = lane & 31, half = lane >> 5;
   const int h = g * kHpg + wave;
   const bool group_b = wave >= 4;
-  const int t0 = item.y * kBM;
-  int klo, khi;
-  block_keys(u, item.y, window, &klo, &khi);
-  const int tile_lo = klo / kBN;
-  const int ntiles = (khi + kBN - 1) / kBN - tile_lo;
-  const char* kvbase = ws.kv + ((size_t)g * ws.ntmax + meta.w + tile_lo) * kTileBytes;
-
-  load_tile_async(kvbase, smem[0], lane, wave);
-  if (ntiles > 1) load_tile_async(kvbase + kTileBytes, smem[1], lane, wave);
-
-  // Query prologue: lane (col, half) holds channels 16kk + 8half + [0,8) of
-  // token t0 + col, which is the MFMA B-operand layout of Q^T.
-  const int qrow = t0 + col;
-  const bool qvalid = qrow < u;
-  const size_t tq = (size_t)start + qrow;
-  bf16x8 qf[8];
-  float qnorm;
-  {
-    float x[64];
-    if (qvalid) {
-      const uint4* src = reinterpret_cast<const uint4*>(q + (tq * kH + h) * kD);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) unpack8(src[2 * kk + half], x + 8 * kk);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 64; ++i) x[i] = 0.f;
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
-    ss += __shfl_xor(ss, 32);
-    const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[8 * kk + j] *= rstd * q_norm_w[16 * kk + 8 * half + j];
-    if (use_rope && qvalid) {
-      const int pos = positions ? positions[tq] : qrow;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float c, s;
-          rope_cos_sin(pos, ws.rope_r[16 * kk + 8 * half + j], &c, &s);
-          const float a = x[8 * kk + j], b = x[8 * (kk + 4) + j];
-          x[8 * kk + j] = a * c - b * s;
-          x[8 * (kk + 4) + j] = b * c + a * s;
-        }
-    }
-    // logits in log2 units: q . k / sqrt(128) * log2(e)
-    const float scale = kLog2e * 0.08838834764831845f;
-    float n2 = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[8 * kk + j] *= scale;
-      const uint4 w = pack8(x + 8 * kk);
-      n2 += sumsq8(w);
-      qf[kk] = __builtin_bit_cast(bf16x8, w);
-    }
-    n2 += __shfl_xor(n2, 32);
-    qnorm = sqrtf(n2);
-  }
-
-  // max |k'| over the tiles this item visits (a block-wide max)
-  __shared__ float kred[kAttnThreads / 64];
-  {
-    const float* tm = ws.tmax + (size_t)g * ws.ntmax + meta.w + tile_lo;
-    float km = 0.f;
-    for (int i = tid; i < ntiles; i += kAttnThreads) km = fmaxf(km, tm[i]);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) km = fmaxf(km, __shfl_xor(km, off));
-    if (lane == 0) kred[wave] = km;
+  const int voff = lane * 16 + wave * 1024;
+  const bool rope = use_rope != 0;
+  const bool qpos = rope && positions;
+  const int q_ops = qpos ? 9 : 8;
+  const float sk = sink[h] * kLog2e;
+  const float kmax = __uint_as_float((unsigned)ws.hdr[kHdrKMax + g]);  // max |k'| of this kv head
+  if (tid < kD) s_qw[tid] = q_norm_w[tid];
+  if (tid < kD / 2) s_rope[tid] = ws.rope_r[tid];
+  for (int jj = tid; jj < nj; jj += kAttnThreads) {
+    const int2 it = ws.items[item_rank(jj, wg, nwg)];
+    const int4 meta = ws.seq[it.x];
+    s_items[jj] = make_int4(meta.x, meta.z, it.y * kBM, meta.w);
   }
   __syncthreads();
-  float kmax = kred[0];
-#pragma unroll
-  for (int w = 1; w < kAttnThreads / 64; ++w) kmax = fmaxf(kmax, kred[w]);
 
-  // Softmax shift (see the file header): none when the logit bound allows.
-  RowState st;
+  // Tile cursor: the next slot to load is tile ck of item cj (cn tiles from
+  // workspace tile ctf). Slot s of the ring lives in stage s % kStages; the
+  // tile in slot s + 2 is loaded while slot s is processed. `ops` counts this
+  // wave's vector-memory operations; end0 / end1 are its value after the loads
+  // of slots s / s + 1.
+  int cj = 0, ck = 0, cn, ctf;
   {
-    const float sk = sink[h] * kLog2e;
-    const float bound = qnorm * kmax * 1.0001f;
-    st.online = __any(!(bound <= kStaticBound));
-    // the sink's share of the denominator, counted once per query (lane half 0)
+    const Item c = item_from(s_items[0], window);
+    cn = c.ntiles;
+    ctf = c.tfirst;
+  }
+  int ops = 0, end0 = 0, end1 = 0;
+  int slot = 0;
+
+#define FLINT_NEXT_SLOT(LOAD, RSRC, LOFF)                       \
+  {                                                             \
+    LOAD = cj < nj;                                             \
+    if (LOAD) {                                                 \
+      RSRC = tiles_rsrc(ws, g, ctf, cn);                        \
+      LOFF = ck * kTileBytes;                                   \
+      ops += 4;                                                 \
+      if (++ck == cn) {                                         \
+        ck = 0;                                                 \
+        if (++cj < nj) {                                        \
+          const Item c = item_from(s_items[cj], window);        \
+          cn = c.ntiles;                                        \
+          ctf = c.tfirst;                                       \
+        }                                                       \
+      }                                                         \
+    }                                                           \
+  }
+
+  // Slots 0 and 1, then the first item's query rows.
+  Item it = item_from(s_items[0], window);
+  {
+    bool ld;
+    __amdgpu_buffer_rsrc_t r;
+    int lo = 0;
+    FLINT_NEXT_SLOT(ld, r, lo);
+    load_tile_async(r, voff, lo, smem[0], wave);
+    end0 = ops;
+    FLINT_NEXT_SLOT(ld, r, lo);
+    if (ld) load_tile_async(r, voff, lo, smem[1], wave);
+    end1 = ops;
+  }
+  QRaw qraw;
+  load_q(q, positions, qpos, it, h, col, half, qraw);
+  ops += q_ops;
+  int endq = ops;  // `ops` after the current item's query loads
+  bf16x8 qf[8];
+  float qmax;
+  q_prologue(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
+
+  for (int j = 0; j < nj; ++j) {
+    // Softmax shift: none when the logit bound |q'| max|k'| and the sink stay
+    // within kStaticBound; otherwise the streaming path.
+    RowState st;
+    st.online = !(sk <= kStaticBound) || !(qmax * kmax * 1.0001f <= kStaticBound);
     st.m = st.online ? sk : 0.f;
     st.l0 = (half == 0 && sk != -INFINITY) ? __builtin_amdgcn_exp2f(sk - st.m) : 0.f;
     st.l1 = 0.f;
@@ -733,56 +882,79 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) st.acc[db][i] = 0.f;
-  }
 
-  // Both groups run the same pipelined body - softmax and PV of tile k-1,
-  // then the logits of tile k - but group A passes the ring barrier just
-  // before the logits and group B at the top of the body. Between barriers k
-  // and k+1 group A therefore computes logits, softmax and PV of tile k while
-  // group B computes softmax and PV of tile k-1 and the logits of tile k.
-  f32x16 s0, s1;
-  bf16x8 pk[4];
-  for (int k = 0; k < ntiles; ++k) {
-    if (group_b) ring_barrier(k + 1 < ntiles);
-    if (k > 0) {
-      tile_softmax(s0, s1, st, pk, (tile_lo + k - 1) * kBN, t0, qrow, u, window, half);
-      tile_pv(smem[(k - 1) % kStages] + kTileVec / 2, lane, pk, st);
+    // Both groups run the same pipelined body - softmax and PV of tile k-1,
+    // then the logits of tile k - but group A passes the ring barrier just
+    // before the logits and group B at the top of the body.
+    const int qrow = it.t0 + col;
+    f32x16 s0, s1;
+    bf16x8 pk[4];
+    for (int k = 0; k < it.ntiles; ++k, ++slot) {
+      if (group_b) ring_barrier(k < 2 ? ops - endq : ops - end0);
+      if (k > 0) {
+        tile_softmax(s0, s1, st, pk, (it.tile_lo + k - 1) * kBN, it.t0, qrow, it.u, window, half);
+        tile_pv(smem[(slot - 1) % kStages] + kTileVec / 2, lane, pk, st);
+      }
+      if (!group_b) ring_barrier(k < 2 ? ops - endq : ops - end0);  // slot is in LDS; stage (slot+2)%4 is free
+      bool ld;
+      __amdgpu_buffer_rsrc_t r;
+      int lo = 0;
+      FLINT_NEXT_SLOT(ld, r, lo);
+      tile_logits(smem[slot % kStages], lane, qf, s0, s1, ld, r, voff, lo, smem[(slot + 2) % kStages],
+                  wave);
+      end0 = end1;
+      end1 = ops;
     }
-    if (!group_b) ring_barrier(k + 1 < ntiles);  // tile k is in LDS; stage (k+2)%4 is free
-    tile_logits(smem[k % kStages], lane, qf, s0, s1,
-                k + 2 < ntiles ? kvbase + (size_t)(k + 2) * kTileBytes : nullptr,
-                smem[(k + 2) % kStages], wave);
-  }
-  tile_softmax(s0, s1, st, pk, (tile_lo + ntiles - 1) * kBN, t0, qrow, u, window, half);
-  tile_pv(smem[(ntiles - 1) % kStages] + kTileVec / 2, lane, pk, st);
-  __syncthreads();
+    // The next item's query rows stream in during this item's last tile's
+    // softmax and PV.
+    const bool more = j + 1 < nj;
+    Item nx = it;
+    if (more) {
+      nx = item_from(s_items[j + 1], window);
+      load_q(q, positions, qpos, nx, h, col, half, qraw);
+      ops += q_ops;
+      endq = ops;
+    }
+    tile_softmax(s0, s1, st, pk, (it.tile_lo + it.ntiles - 1) * kBN, it.t0, qrow, it.u, window, half);
+    tile_pv(smem[(slot - 1) % kStages] + kTileVec / 2, lane, pk, st);
+    // Epilogue: O = acc / l in bf16. Lane (col, half) holds channels
+    // 32db + 8rg + 4half + [0, 4) of query t0 + col; one swap with the
+    // partner lane (col, 1 - half) gives it channels 32db + 16r2 + 8half +
+    // [0, 8) instead, 16 contiguous bytes per store.
+    const float lsum = st.l0 + st.l1;
+    const float lt = lsum + __shfl_xor(lsum, 32);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    uint4 ow[8];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2) {
+        const f32x16& c = st.acc[db];
+        const int o = 8 * r2;
+        const unsigned a0 = pack2(c[o] * inv, c[o + 1] * inv), a1 = pack2(c[o + 2] * inv, c[o + 3] * inv);
+        const unsigned b0 = pack2(c[o + 4] * inv, c[o + 5] * inv), b1 = pack2(c[o + 6] * inv, c[o + 7] * inv);
+        // lanes 32-63 of the first operand trade places with lanes 0-31 of the second
+        const auto x0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto x1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        ow[2 * db + r2] = make_uint4(x0[0], x1[0], x0[1], x1[1]);
+      }
+    // The next item's query prologue runs before this item's output stores,
+    // so its query loads are the newest vector-memory operations it waits on.
+    if (more) q_prologue(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
+    // Rows past the valid length fall outside the store range and are dropped.
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        out + ((size_t)(it.start + it.t0) * kH + h) * kD, 0, min(it.u - it.t0, kBM) * (kH * kD * 2),
+        kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, ow[i]), orsrc,
+          col * (kH * kD * 2) + (32 * (i >> 1) + 16 * (i & 1) + 8 * half) * 2, 0, 0);
+    ops += 8;
 
-  // Epilogue: O = acc / l, staged through LDS so each token row (256 bytes of
-  // one head) leaves in full 16-byte vectors.
-  const float lsum = st.l0 + st.l1;
-  const float lt = lsum + __shfl_xor(lsum, 32);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  uint2* orow = reinterpret_cast<uint2*>(reinterpret_cast<char*>(&smem[0][0]) + wave * (kBM * kD * 2));
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int chunk = (4 * db + rg) ^ o_swizzle(col);
-      const uint2 w = make_uint2(pack2(st.acc[db][4 * rg] * inv, st.acc[db][4 * rg + 1] * inv),
-                                 pack2(st.acc[db][4 * rg + 2] * inv, st.acc[db][4 * rg + 3] * inv));
-      orow[col * 32 + chunk * 2 + half] = w;
-    }
-  __syncthreads();
-  const uint4* ostage = reinterpret_cast<const uint4*>(orow);
-#pragma unroll
-  for (int i = 0; i < kBM * 16 / 64; ++i) {
-    const int idx = i * 64 + lane;
-    const int r = idx >> 4, c = idx & 15;
-    if (t0 + r < u) {
-      const uint4 w = ostage[r * 16 + (c ^ o_swizzle(r))];
-      reinterpret_cast<uint4*>(out + (((size_t)start + t0 + r) * kH + h) * kD)[c] = w;
-    }
+    it = nx;
   }
+#undef FLINT_NEXT_SLOT
 }
 
 // ----------------------------------------------------------------- mask helper
@@ -848,6 +1020,27 @@ extern "C" const char* flint_attn_strerror(int status) {
   }
 }
 
+// Workgroups per kv head of the persistent attention kernel: one per CU in
+// all (the LDS ring admits one workgroup per CU), more only when a
+// workgroup's item list would outgrow its LDS table, never more than the
+// query blocks.
+static int64_t attn_groups(int64_t nqmax) {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int n = (dev >= 0 && dev < 64) ? cus[dev] : 0;
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    if (dev >= 0 && dev < 64) cus[dev] = n;
+  }
+  int64_t per_head = n / kG > 0 ? n / kG : 1;
+  // each workgroup's item list fits its LDS table
+  const int64_t need = (nqmax + kMaxItemsPerGroup - 1) / kMaxItemsPerGroup;
+  if (per_head < need) per_head = need;
+  return nqmax < per_head ? nqmax : per_head;
+}
+
 static bool debug_sync() {
   const char* e = getenv("FLINT_ATTN_DEBUG");
   return e && e[0] == '1';
@@ -897,7 +1090,6 @@ extern "C" int flint_attn_fwd_phases(const void* q, const void* k, const void* v
   ws.hdr = reinterpret_cast<int*>(base + L.hdr);
   ws.rope_r = reinterpret_cast<unsigned long long*>(base + L.rope_r);
   ws.seq = reinterpret_cast<int4*>(base + L.seq);
-  ws.tmax = reinterpret_cast<float*>(base + L.tmax);
   ws.tbase = reinterpret_cast<int*>(base + L.tbase);
   ws.qbase = reinterpret_cast<int*>(base + L.qbase);
   ws.tiles = reinterpret_cast<int2*>(base + L.tiles);
@@ -921,8 +1113,8 @@ extern "C" int flint_attn_fwd_phases(const void* q, const void* k, const void* v
     kv_prologue_kernel<<<dim3((unsigned)L.ntmax, kG), 256, 0, st>>>(kh, vh, k_norm_w, pos, eps,
                                                                     rope, ws, oh);
   if (phases & FLINT_PHASE_ATTEND)
-    attn_kernel<<<(unsigned)(L.nqmax * kG), kAttnThreads, 0, st>>>(qh, q_norm_w, sink, pos,
-                                                                   window, rope, eps, ws, oh);
+    attn_kernel<<<(unsigned)(attn_groups(L.nqmax) * kG), kAttnThreads, 0, st>>>(
+        qh, q_norm_w, sink, pos, window, rope, eps, ws, oh);
   if (hipGetLastError() != hipSuccess) return FLINT_ERR_HIP;
   if (debug_sync()) {
     int32_t flags = 0;
