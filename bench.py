@@ -35,7 +35,10 @@ METRIC = "sink-attention prefill TFLOP/s (unmasked FLOPs) & % bf16 MFMA peak, 1 
 BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "attention_head_rmsnorm_amd", "csrc", "flint_attn.hip")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_kernel_s8192_full_nope_traffic.md")
+TRAFFIC_PROFILES = {
+    "tstar": os.path.join(ROOT, "profiles", "attn_kernel_s8192_full_nope_traffic.md"),
+    "c3": os.path.join(ROOT, "profiles", "attn_kernel_b8_s8192_sw513_rope_traffic.md"),
+}
 COPY_PROBE_BYTES = 1 << 30
 
 
@@ -67,15 +70,16 @@ def source_sha256():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_from_profile():
+def traffic_from_profile(cfg):
     """HBM bytes per attention-kernel launch from the committed PMC summary.
 
     The summary records the kernel source hash it was taken with; a different
     current source means the counters no longer describe this kernel -> None.
     """
-    if not os.path.exists(TRAFFIC_PROFILE):
+    path = TRAFFIC_PROFILES.get(cfg)
+    if path is None or not os.path.exists(path):
         return None
-    text = open(TRAFFIC_PROFILE).read()
+    text = open(path).read()
     mh = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     mb = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not mh or not mb or mh.group(1) != source_sha256():
@@ -221,8 +225,11 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     alg_bytes = 18432.0 * T
-    traffic = traffic_from_profile() if cfg == "tstar" else None
-    bound = "mfma" if layer.window == 0 else "mfma"
+    traffic = traffic_from_profile(wl.name if li == 0 else None)
+    # bf16 ridge: 2516.6 TFLOP/s / 8 TB/s = 315 FLOP per byte
+    intensity = flops / alg_bytes
+    bound = "mfma" if intensity >= BF16_PEAK_TFLOPS / (HBM_PEAK_GBS / 1000.0) else "hbm"
+    alg_gbs = alg_bytes / (attn_ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -257,14 +264,18 @@ def main():
         "prologue_ms": round(ms_step - attn_ms, 5),
         "roofline": {
             "bound": bound,
-            "achieved": round(attn_tflops, 3),
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
+            "achieved": round(attn_tflops if bound == "mfma" else alg_gbs, 3),
+            "peak": BF16_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+            "frac": round(attn_tflops / BF16_PEAK_TFLOPS if bound == "mfma" else alg_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": "attn_kernel",
             "algorithmic_bytes": alg_bytes,
-            "algorithmic_GBs": round(alg_bytes / (attn_ms * 1e-3) / 1e9, 1),
+            "algorithmic_flops": flops,
+            "intensity_flop_per_byte": round(intensity, 1),
+            "attn_tflops": round(attn_tflops, 3),
+            "algorithmic_GBs": round(alg_gbs, 1),
+            "traffic_GBs": None if traffic is None else round(traffic / (attn_ms * 1e-3) / 1e9, 1),
         },
         "wall_s_timed": round(wall, 4),
     }
