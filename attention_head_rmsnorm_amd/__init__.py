@@ -1,4 +1,4 @@
-"""Flint sink-aware attention forward (prefill) for AMD Instinct MI355X.
+"""Flint sink-aware attention forward (prefill and decode) for AMD Instinct MI355X.
 
 The compute path is the HIP library ``libflint_attn.so`` (C ABI in
 ``include/flint_attn.h``); this package only binds it.
@@ -6,6 +6,8 @@ The compute path is the HIP library ``libflint_attn.so`` (C ABI in
 
 from .binding import (  # noqa: F401
     EXPORTED,
+    FLINT_DEV_CACHE,
+    KVCache,
     FLINT_ERR_ALIGN,
     FLINT_ERR_DEVICE_DATA,
     FLINT_ERR_HIP,
@@ -21,9 +23,12 @@ from .binding import (  # noqa: F401
     FLINT_PHASE_SCHEDULE,
     FlintError,
     flint_attn,
+    flint_attn_decode,
+    flint_attn_decode_workspace_bytes,
     flint_attn_device_status,
     flint_attn_fwd,
     flint_attn_fwd_phases,
+    flint_attn_kv_append,
     flint_attn_seqused_from_mask,
     flint_attn_strerror,
     flint_attn_workspace_bytes,

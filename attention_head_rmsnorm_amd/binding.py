@@ -32,6 +32,8 @@ FLINT_ERR_ALIGN = -6
 FLINT_ERR_HIP = -7
 FLINT_ERR_DEVICE_DATA = -8
 
+FLINT_DEV_CACHE = 32
+
 FLINT_PHASE_SCHEDULE = 1
 FLINT_PHASE_KV = 2
 FLINT_PHASE_ATTEND = 4
@@ -44,6 +46,9 @@ EXPORTED = (
     "flint_attn_seqused_from_mask",
     "flint_attn_device_status",
     "flint_attn_strerror",
+    "flint_attn_decode_workspace_bytes",
+    "flint_attn_kv_append",
+    "flint_attn_decode",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -82,6 +87,14 @@ def load_library() -> ctypes.CDLL:
     lib.flint_attn_device_status.restype = ctypes.c_int
     lib.flint_attn_strerror.argtypes = [ctypes.c_int]
     lib.flint_attn_strerror.restype = ctypes.c_char_p
+    lib.flint_attn_decode_workspace_bytes.argtypes = [i32, i32]
+    lib.flint_attn_decode_workspace_bytes.restype = sz
+    lib.flint_attn_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32,
+                                         i32, f32, f32, vp, sz, vp]
+    lib.flint_attn_kv_append.restype = ctypes.c_int
+    lib.flint_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
+                                      i32, i32, i32, f32, f32, vp, sz, vp, vp]
+    lib.flint_attn_decode.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -133,6 +146,32 @@ def flint_attn_device_status(workspace, stream):
 
 def flint_attn_strerror(status: int) -> str:
     return load_library().flint_attn_strerror(int(status)).decode()
+
+
+def flint_attn_decode_workspace_bytes(batch: int, cache_cap: int) -> int:
+    return int(load_library().flint_attn_decode_workspace_bytes(batch, cache_cap))
+
+
+def flint_attn_kv_append(k, v, k_norm_w, positions, cache_len, batch, n_new, k_cache, vt_cache,
+                         cache_cap, num_kv_heads, head_dim, window, use_rope, rope_theta, eps,
+                         workspace, workspace_bytes, stream) -> int:
+    """The C entry point with pointer arguments as ints (0 = NULL); returns the status."""
+    return int(load_library().flint_attn_kv_append(k, v, k_norm_w, positions, cache_len, batch,
+                                                   n_new, k_cache, vt_cache, cache_cap,
+                                                   num_kv_heads, head_dim, window, use_rope,
+                                                   rope_theta, eps, workspace, workspace_bytes,
+                                                   stream))
+
+
+def flint_attn_decode(q, k, v, q_norm_w, k_norm_w, sink, positions, cache_len, batch, k_cache,
+                      vt_cache, cache_cap, num_q_heads, num_kv_heads, head_dim, window, use_rope,
+                      rope_theta, eps, workspace, workspace_bytes, out, stream) -> int:
+    """The C entry point with pointer arguments as ints (0 = NULL); returns the status."""
+    return int(load_library().flint_attn_decode(q, k, v, q_norm_w, k_norm_w, sink, positions,
+                                                cache_len, batch, k_cache, vt_cache, cache_cap,
+                                                num_q_heads, num_kv_heads, head_dim, window,
+                                                use_rope, rope_theta, eps, workspace,
+                                                workspace_bytes, out, stream))
 
 
 # ----------------------------------------------------------------- torch layer
@@ -250,3 +289,92 @@ def flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens
     if st != FLINT_OK:
         raise FlintError(st, "flint_attn_fwd")
     return out
+
+
+class KVCache:
+    """One layer's KV cache for decode, in the layout the C ABI documents.
+
+    ``k`` is [batch, 4, cap, 128] bf16 (normalized, rotated keys) and ``vt``
+    [batch, 4, 128, cap] bf16 (values, transposed); ``length`` int32 [batch]
+    counts the tokens each sequence holds. ``window`` > 0 makes it a ring of
+    the last ``window`` tokens (cap is rounded up to a multiple of 32);
+    ``window`` = 0 keeps ``max_tokens`` tokens.
+    """
+
+    def __init__(self, batch: int, window: int, max_tokens: int = 0, *, use_rope: bool = True,
+                 rope_theta: float = 1.0e6, eps: float = 1.0e-6, device="cuda"):
+        import torch
+
+        need = window if window > 0 else max_tokens
+        if need <= 0:
+            raise ValueError("a full-attention cache needs max_tokens > 0")
+        self.cap = (need + 31) // 32 * 32
+        self.batch, self.window = batch, window
+        self.use_rope, self.rope_theta, self.eps = use_rope, rope_theta, eps
+        self.k = torch.zeros(batch, NUM_KV_HEADS, self.cap, HEAD_DIM, dtype=torch.bfloat16,
+                             device=device)
+        self.vt = torch.zeros(batch, NUM_KV_HEADS, HEAD_DIM, self.cap, dtype=torch.bfloat16,
+                              device=device)
+        self.length = torch.zeros(batch, dtype=torch.int32, device=device)
+        nbytes = flint_attn_decode_workspace_bytes(batch, self.cap)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+    def _check(self, name, t, dtype, shape):
+        import torch
+
+        if t.dtype != dtype or not t.is_contiguous() or t.device != self.k.device:
+            raise TypeError(f"{name} must be a contiguous {dtype} tensor on {self.k.device}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+    def append(self, k, v, k_norm_w, positions=None):
+        """Appends k/v [batch, n_new, 4, 128] bf16 (before RMSNorm) to every sequence."""
+        import torch
+
+        B, n_new = k.shape[0], k.shape[1]
+        self._check("k", k, torch.bfloat16, (self.batch, n_new, NUM_KV_HEADS, HEAD_DIM))
+        self._check("v", v, torch.bfloat16, (self.batch, n_new, NUM_KV_HEADS, HEAD_DIM))
+        self._check("k_norm_w", k_norm_w, torch.float32, (HEAD_DIM,))
+        if positions is not None:
+            self._check("positions", positions, torch.int32, (self.batch, n_new))
+        st = flint_attn_kv_append(_ptr(k), _ptr(v), _ptr(k_norm_w), _ptr(positions),
+                                  _ptr(self.length), B, n_new, _ptr(self.k), _ptr(self.vt),
+                                  self.cap, NUM_KV_HEADS, HEAD_DIM, self.window,
+                                  int(bool(self.use_rope)), float(self.rope_theta),
+                                  float(self.eps), _ptr(self.workspace), self.workspace.numel(),
+                                  _stream_handle(k.device))
+        if st != FLINT_OK:
+            raise FlintError(st, "flint_attn_kv_append")
+        self.length += n_new
+
+    def decode(self, q, k, v, q_norm_w, k_norm_w, sinks, positions=None, out=None):
+        """One step: q [batch, 32, 128], k/v [batch, 4, 128] bf16 (before RMSNorm).
+
+        Appends the token, returns its attention output [batch, 32, 128] and
+        advances the lengths.
+        """
+        import torch
+
+        self._check("q", q, torch.bfloat16, (self.batch, NUM_Q_HEADS, HEAD_DIM))
+        self._check("k", k, torch.bfloat16, (self.batch, NUM_KV_HEADS, HEAD_DIM))
+        self._check("v", v, torch.bfloat16, (self.batch, NUM_KV_HEADS, HEAD_DIM))
+        for name, t in (("q_norm_w", q_norm_w), ("k_norm_w", k_norm_w)):
+            self._check(name, t, torch.float32, (HEAD_DIM,))
+        self._check("sinks", sinks, torch.float32, (NUM_Q_HEADS,))
+        if positions is not None:
+            self._check("positions", positions, torch.int32, (self.batch,))
+        if out is None:
+            out = torch.empty_like(q)
+        st = flint_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w),
+                               _ptr(sinks), _ptr(positions), _ptr(self.length), self.batch,
+                               _ptr(self.k), _ptr(self.vt), self.cap, NUM_Q_HEADS, NUM_KV_HEADS,
+                               HEAD_DIM, self.window, int(bool(self.use_rope)),
+                               float(self.rope_theta), float(self.eps), _ptr(self.workspace),
+                               self.workspace.numel(), _ptr(out), _stream_handle(q.device))
+        if st != FLINT_OK:
+            raise FlintError(st, "flint_attn_decode")
+        self.length += 1
+        return out
+
+    def device_status(self):
+        return flint_attn_device_status(_ptr(self.workspace), _stream_handle(self.k.device))

@@ -78,6 +78,8 @@ typedef enum flint_status {
 #define FLINT_DEV_CU_END 4       /* cu_seqlens[n_seqs] != total_tokens          */
 #define FLINT_DEV_MAX_SEQLEN 8   /* a sequence is longer than max_seqlen        */
 #define FLINT_DEV_SEQUSED 16     /* seqused[s] < 0 or > the sequence length     */
+#define FLINT_DEV_CACHE 32       /* decode: cache_len[b] < 0, or a full layer's cache
+                                    cannot hold the token (cache_len[b] >= cache_cap) */
 
 /*
  * Bytes of device workspace flint_attn_fwd needs for these sizes; 0 when the
@@ -174,6 +176,67 @@ int flint_attn_device_status(const void* workspace, void* stream, int32_t* flags
 
 /* A static, human-readable name of a flint_status value. */
 const char* flint_attn_strerror(int status);
+
+/* ------------------------------------------------------------------------
+ * Decode with a per-layer KV cache.
+ *
+ * One new token per sequence attends to the cached keys of its layer. The
+ * cache honours the layer's window (Hugging Face discussion #26, "Minor": a
+ * hybrid KV cache in which the per-layer window sizes must be honoured): a
+ * sliding layer keeps the last `window` tokens in a ring, a full layer keeps
+ * all of them. The result for the new token t = cache_len[b] is exactly row t
+ * of flint_attn_fwd over the sequence's tokens 0..t with the same weights,
+ * sinks, window, positions and flags.
+ *
+ * Cache layout (caller-owned device memory, one pair per layer), head-major so
+ * that every (sequence, kv head) streams one contiguous region:
+ *   k_cache  [batch][4][cache_cap][128] bf16: RMSNorm-ed, RoPE-rotated keys
+ *            (as flint_attn_fwd forms them before its bf16 rounding);
+ *   vt_cache [batch][4][128][cache_cap] bf16: values, transposed.
+ * Token t of a sequence sits in slot t of a full layer (window = 0) and in
+ * slot t % cache_cap of a sliding layer, which needs cache_cap >= window.
+ * cache_cap must be a positive multiple of 32; both pointers 16-byte aligned.
+ * The caller owns cache_len (tokens already in the cache, per sequence) and
+ * advances it after a call; the library never writes it.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace size in bytes for flint_attn_kv_append / flint_attn_decode with
+ * `batch` sequences and a cache of `cache_cap` slots. */
+size_t flint_attn_decode_workspace_bytes(int32_t batch, int32_t cache_cap);
+
+/* Appends n_new tokens to each sequence's cache: token cache_len[b] + i of
+ * sequence b, for i < n_new, from k/v [batch][n_new][4][128] bf16 (projected,
+ * before RMSNorm). positions [batch][n_new] int32 gives the RoPE position of
+ * each (NULL: the token index cache_len[b] + i; read only when use_rope).
+ * Fills a cache from a prompt, or adds the current token. A sliding layer
+ * takes n_new <= cache_cap. Errors: FLINT_ERR_NULL, FLINT_ERR_SHAPE
+ * (batch < 1, n_new < 1, cache_cap not a positive multiple of 32, a sliding
+ * cache smaller than the window), FLINT_ERR_UNSUPPORTED (head layout),
+ * FLINT_ERR_VALUE, FLINT_ERR_ALIGN, FLINT_ERR_WORKSPACE, FLINT_ERR_HIP.
+ * Device-data errors (FLINT_DEV_CACHE) leave that sequence's cache unchanged
+ * and are read with flint_attn_device_status(workspace, ...). */
+int flint_attn_kv_append(const void* k, const void* v, const float* k_norm_w,
+                         const int32_t* positions, const int32_t* cache_len, int32_t batch,
+                         int32_t n_new, void* k_cache, void* vt_cache, int32_t cache_cap,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                         int32_t use_rope, float rope_theta, float eps, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* One decode step: appends the new token (q [batch][32][128], k/v
+ * [batch][4][128] bf16, projected, before RMSNorm; positions [batch] or NULL
+ * = cache_len[b]) to the cache as flint_attn_kv_append does, then writes its
+ * attention output out [batch][32][128] bf16 over tokens
+ * max(0, t - window + 1) .. t (window > 0) or 0 .. t (window = 0),
+ * t = cache_len[b], with the sink. Split over the keys (256 per split) and
+ * merged, so one sequence spreads over the GPU. Errors as for
+ * flint_attn_kv_append; a sequence with a device-data error gets zero rows. */
+int flint_attn_decode(const void* q, const void* k, const void* v, const float* q_norm_w,
+                      const float* k_norm_w, const float* sink, const int32_t* positions,
+                      const int32_t* cache_len, int32_t batch, void* k_cache, void* vt_cache,
+                      int32_t cache_cap, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t window, int32_t use_rope, float rope_theta,
+                      float eps, void* workspace, size_t workspace_bytes, void* out,
+                      void* stream);
 
 #ifdef __cplusplus
 }

@@ -12,4 +12,5 @@ from .gen import (  # noqa: F401
     Workload,
     make_workload,
     make_custom,
+    make_long_decode,
 )

@@ -228,3 +228,28 @@ def make_custom(seed: int, lengths: Sequence[int], *, layout: str = "thd", sequs
                     v=_bf16(v), q_norm_w=qw, k_norm_w=kw, sinks=sinks,
                     cu_seqlens=torch.from_numpy(cu.astype(np.int32)), seqused=su, positions=pos,
                     layers=list(layers), batch=B, seqlen=S)
+
+
+def make_long_decode(seed: int, n_cached: int, layers=(FULL,), sink_std: float = 1.0):
+    """One sequence of n_cached + 1 tokens for a decode check at long context.
+
+    Only the last token's query is drawn (the earlier queries never enter a
+    decode step); k and v cover every token. Draw order: q of the last token,
+    k, v, then weights and sinks. Returns a Workload whose q has a single row
+    (the last token) and cu_seqlens = [0, 1], plus k and v for all tokens in
+    ``meta["k_all"]`` / ``meta["v_all"]``.
+    """
+    rng = np.random.default_rng(seed)
+    T = n_cached + 1
+    q = _normal(rng, (1, NUM_Q_HEADS, HEAD_DIM))
+    k = _normal(rng, (T, NUM_KV_HEADS, HEAD_DIM))
+    v = _normal(rng, (T, NUM_KV_HEADS, HEAD_DIM))
+    qw, kw, sinks = _draw_params(rng, sink_std)
+    wl = Workload(name=f"longdecode{seed}", seed=seed, layout="thd", q=_bf16(q), k=_bf16(k[-1:]),
+                  v=_bf16(v[-1:]), q_norm_w=qw, k_norm_w=kw, sinks=sinks,
+                  cu_seqlens=torch.tensor([0, 1], dtype=torch.int32), seqused=None, positions=None,
+                  layers=list(layers), description=f"one sequence, {n_cached} cached tokens")
+    wl.meta["k_all"] = _bf16(k)
+    wl.meta["v_all"] = _bf16(v)
+    return wl
+
