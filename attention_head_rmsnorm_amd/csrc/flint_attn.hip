@@ -966,15 +966,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
 // Token t of a sequence sits in slot t (full layers) or t % cap (sliding
 // layers, cap >= window: a ring holding the window). cap is a multiple of
 // kDecBlock, so an aligned block of 32 tokens occupies 32 consecutive slots.
-constexpr int kDecBlock = 32;       // tokens per step of the decode attention
-constexpr int kDecSplitBlocks = 8;  // blocks per split (256 tokens)
+constexpr int kDecBlock = 32;         // tokens per step of the decode attention
+constexpr int kDecMinSplitBlocks = 2;  // smallest split (64 tokens), sizes the workspace
+constexpr int kDecMaxSplitBlocks = 8;  // largest split (256 tokens)
+constexpr int kDecMergeLanes = 32;     // splits merged in parallel per (sequence, head)
 
 struct DecWs {
   int* hdr;        // [0] device-data error bits
   uint16_t* q;     // [B][32][128] bf16 query rows, normalized, rotated, scaled to log2 units
   float* ml;       // [B][4][nsplit][8][2] running max and denominator of each split
   float* part;     // [B][4][nsplit][8][128] unnormalized output of each split
-  int nsplit;
+  int nsplit;      // split slots per (sequence, kv head) in ml / part
+  int bps;         // blocks per split of this call
 };
 
 struct DecLayout {
@@ -984,7 +987,7 @@ struct DecLayout {
 
 static DecLayout make_dec_layout(int64_t batch, int64_t cap) {
   DecLayout L;
-  L.nsplit = (int)((cap / kDecBlock + 1 + kDecSplitBlocks - 1) / kDecSplitBlocks);
+  L.nsplit = (int)((cap / kDecBlock + 1 + kDecMinSplitBlocks - 1) / kDecMinSplitBlocks);
   size_t o = 0;
   L.hdr = o;  o = align_up(o + 64 * sizeof(int), 256);
   L.q = o;    o = align_up(o + (size_t)batch * kH * kD * 2, 256);
@@ -1089,11 +1092,35 @@ __device__ __forceinline__ void dec_range(int len, int window, int* t_lo, int* t
 }
 
 // Split s of the decode attention of (sequence b, kv head g): one wave runs
-// kDecSplitBlocks blocks of 32 keys with v_mfma_f32_16x16x32_bf16, the 8
-// query heads as the columns 0-7 of S^T = K' Q'^T (columns 8-15 zero) and
+// ws.bps blocks of 32 keys with v_mfma_f32_16x16x32_bf16, the 8 query heads
+// as the columns 0-7 of S^T = K' Q'^T (columns 8-15 zero) and
 // O^T += V^T P^T, with a streaming softmax (running max per head; the sink
 // joins in the merge). Lane l holds column l % 16 and rows 4(l / 16) + [0, 4)
-// of each 16-row result block.
+// of each 16-row result block. The next block's K' and V^T fragments load
+// while the current one is computed.
+struct DecFrags {
+  bf16x8_t k[2][4];  // K' key 16kh + col, channels 32ds + 8qd .. +8
+  bf16x8_t v[8];     // V^T channel 16db + col, keys 4qd .. +4 and 16 + 4qd .. +4
+};
+
+__device__ __forceinline__ void dec_load(const uint16_t* kbase, const uint16_t* vbase, int slot0, int cap,
+                                         int col, int qd, DecFrags& f) {
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      f.k[kh][ds] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(kbase + (size_t)(slot0 + 16 * kh + col) * kD + 32 * ds + 8 * qd));
+  // V^T keys in the order in which this lane holds P: 4qd .. +4, then 16 + 4qd .. +4
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const uint16_t* vr = vbase + (size_t)(16 * db + col) * cap + slot0;
+    const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * qd);
+    const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * qd);
+    f.v[db] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  }
+}
+
 __global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__ cache_len, int cap,
                                                          int window,
                                                          const uint16_t* __restrict__ k_cache,
@@ -1105,9 +1132,9 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__
   if (len < 0 || (window == 0 && len >= cap)) return;
   int t_lo, t_hi, blk_lo, nblk;
   dec_range(len, window, &t_lo, &t_hi, &blk_lo, &nblk);
-  const int bs = s * kDecSplitBlocks;
+  const int bs = s * ws.bps;
   if (bs >= nblk) return;
-  const int be = min(bs + kDecSplitBlocks, nblk);
+  const int be = min(bs + ws.bps, nblk);
 
   bf16x8_t qf[4];
 #pragma unroll
@@ -1119,38 +1146,24 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__
   }
   const uint16_t* kbase = k_cache + ((size_t)b * kG + g) * cap * (size_t)kD;
   const uint16_t* vbase = vt_cache + ((size_t)b * kG + g) * kD * (size_t)cap;
+  auto slot_of = [&](int blk) { return window > 0 ? (blk * kDecBlock) % cap : blk * kDecBlock; };
 
   float m = -INFINITY, l = 0.f;
   f32x4 acc[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  DecFrags cur, nxt;
+  dec_load(kbase, vbase, slot_of(blk_lo + bs), cap, col, qd, cur);
   for (int blk = blk_lo + bs; blk < blk_lo + be; ++blk) {
-    const int slot0 = window > 0 ? (blk * kDecBlock) % cap : blk * kDecBlock;
-    // K' fragments: key 16kh + col, channels 32ds + 8qd .. +8
-    bf16x8_t kf[2][4];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
-        kf[kh][ds] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(kbase + (size_t)(slot0 + 16 * kh + col) * kD + 32 * ds + 8 * qd));
-    // V^T fragments: channel 16db + col, keys 4qd .. +4 and 16 + 4qd .. +4
-    // (the order in which this lane holds P)
-    bf16x8_t vf[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const uint16_t* vr = vbase + (size_t)(16 * db + col) * cap + slot0;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * qd);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * qd);
-      vf[db] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-    }
+    if (blk + 1 < blk_lo + be) dec_load(kbase, vbase, slot_of(blk + 1), cap, col, qd, nxt);
     f32x4 sc[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       sc[kh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) sc[kh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kh][ds], qf[ds], sc[kh], 0, 0, 0);
+      for (int ds = 0; ds < 4; ++ds)
+        sc[kh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[kh][ds], qf[ds], sc[kh], 0, 0, 0);
     }
     // mask keys outside [t_lo, t_hi]; key of sc[kh][i] is blk*32 + 16kh + 4qd + i
     float mx = -INFINITY;
@@ -1183,8 +1196,9 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       acc[db] *= alpha;
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf, acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.v[db], pf, acc[db], 0, 0, 0);
     }
+    cur = nxt;
   }
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
@@ -1199,35 +1213,71 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__
 }
 
 // out[b][h] = (sum_s acc_s 2^(m_s - m)) / (2^(sink - m) + sum_s l_s 2^(m_s - m)),
-// m = max(sink, max_s m_s): the sink joins the softmax once.
-__global__ __launch_bounds__(kD) void decode_merge_kernel(const int* __restrict__ cache_len, int cap,
-                                                          int window, const float* __restrict__ sink,
-                                                          DecWs ws, uint16_t* __restrict__ out) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+// m = max(sink, max_s m_s): the sink joins the softmax once. Thread (sl, dc)
+// of the 256 merges splits sl, sl + 32, ... for channels 16dc .. +16; the 32
+// partial merges then combine through LDS.
+__global__ __launch_bounds__(256) void decode_merge_kernel(const int* __restrict__ cache_len, int cap,
+                                                           int window, const float* __restrict__ sink,
+                                                           DecWs ws, uint16_t* __restrict__ out) {
+  __shared__ float s_m[kDecMergeLanes], s_l[kDecMergeLanes];
+  __shared__ float s_acc[kDecMergeLanes][kD];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int sl = tid & (kDecMergeLanes - 1), dc = tid / kDecMergeLanes;  // dc: 16-channel chunk
   const int g = h / kHpg, col = h % kHpg;
-  uint16_t* o = out + ((size_t)b * kH + h) * kD + d;
+  uint16_t* o = out + ((size_t)b * kH + h) * kD;
   const int len = cache_len[b];
   if (len < 0 || (window == 0 && len >= cap)) {
-    *o = 0;
+    if (tid < kD) o[tid] = 0;
     return;
   }
   int t_lo, t_hi, blk_lo, nblk;
   dec_range(len, window, &t_lo, &t_hi, &blk_lo, &nblk);
-  const int ns = (nblk + kDecSplitBlocks - 1) / kDecSplitBlocks;
+  const int ns = (nblk + ws.bps - 1) / ws.bps;
   const size_t base = ((size_t)b * kG + g) * ws.nsplit * kHpg + col;
-  const float sk = sink[h] * kLog2e;
-  float m = sk;
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, ws.ml[(base + (size_t)s * kHpg) * 2]);
-  float lsum = (m == -INFINITY || sk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sk - m);
-  float acc = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t e = base + (size_t)s * kHpg;
-    const float ms = ws.ml[e * 2];
-    const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - m);
-    lsum += ws.ml[e * 2 + 1] * w;
-    acc += ws.part[e * kD + d] * w;
+  float m = -INFINITY, l = 0.f, acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int sidx = sl; sidx < ns; sidx += kDecMergeLanes) {
+    const size_t e = base + (size_t)sidx * kHpg;
+    const float2 ml = *reinterpret_cast<const float2*>(ws.ml + e * 2);
+    const float mn = fmaxf(m, ml.x);
+    const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float a1 = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - mn);
+    const float4* pr = reinterpret_cast<const float4*>(ws.part + e * kD + 16 * dc);
+    l = l * a0 + ml.y * a1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = pr[i];
+      acc[4 * i] = acc[4 * i] * a0 + v.x * a1;
+      acc[4 * i + 1] = acc[4 * i + 1] * a0 + v.y * a1;
+      acc[4 * i + 2] = acc[4 * i + 2] * a0 + v.z * a1;
+      acc[4 * i + 3] = acc[4 * i + 3] * a0 + v.w * a1;
+    }
+    m = mn;
   }
-  *o = bf16_bits(lsum > 0.f ? acc / lsum : 0.f);
+  if (dc == 0) {
+    s_m[sl] = m;
+    s_l[sl] = l;
+  }
+  __syncthreads();
+  float mt = sink[h] * kLog2e;
+  const float sk = mt;
+#pragma unroll 4
+  for (int i = 0; i < kDecMergeLanes; ++i) mt = fmaxf(mt, s_m[i]);
+  const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mt);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s_acc[sl][16 * dc + i] = acc[i] * w;
+  __syncthreads();
+  if (tid < kD) {
+    float lsum = (mt == -INFINITY || sk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sk - mt);
+    float a = 0.f;
+    for (int i = 0; i < kDecMergeLanes; ++i) {
+      const float mi = s_m[i];
+      lsum += mi == -INFINITY ? 0.f : s_l[i] * __builtin_amdgcn_exp2f(mi - mt);
+      a += s_acc[i][tid];
+    }
+    o[tid] = bf16_bits(lsum > 0.f ? a / lsum : 0.f);
+  }
 }
 
 // Clears the device-data error bits at the start of a decode call (a kernel,
@@ -1437,6 +1487,7 @@ static DecWs dec_ws(void* workspace, const DecLayout& L) {
   ws.ml = reinterpret_cast<float*>(base + L.ml);
   ws.part = reinterpret_cast<float*>(base + L.part);
   ws.nsplit = L.nsplit;
+  ws.bps = kDecMaxSplitBlocks;
   return ws;
 }
 
@@ -1516,7 +1567,14 @@ extern "C" int flint_attn_decode(const void* q, const void* k, const void* v, co
       (positions && !aligned(positions, 4)))
     return FLINT_ERR_ALIGN;
   const DecLayout L = make_dec_layout(batch, cache_cap);
-  const DecWs ws = dec_ws(workspace, L);
+  DecWs ws = dec_ws(workspace, L);
+  // Split size: the largest that still gives about 4096 waves (4 per SIMD)
+  // over the cache's blocks, at least kDecMinSplitBlocks.
+  const int64_t blocks = (int64_t)batch * kG * (cache_cap / kDecBlock + 1);
+  int bps = kDecMaxSplitBlocks;
+  while (bps > kDecMinSplitBlocks && blocks / bps < 4096) bps /= 2;
+  ws.bps = bps;
+  const int nsplit = (int)((cache_cap / kDecBlock + 1 + bps - 1) / bps);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int rope = use_rope ? 1 : 0;
   const uint16_t* kc = static_cast<const uint16_t*>(k_cache);
@@ -1527,10 +1585,10 @@ extern "C" int flint_attn_decode(const void* q, const void* k, const void* v, co
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       q_norm_w, k_norm_w, rope ? positions : nullptr, cache_len, 1, cache_cap, window, rope,
       (double)rope_theta, eps, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(vt_cache), ws);
-  decode_attn_kernel<<<dim3((unsigned)L.nsplit, kG, (unsigned)batch), 64, 0, st>>>(cache_len, cache_cap,
-                                                                                   window, kc, vc, ws);
-  decode_merge_kernel<<<dim3(kH, (unsigned)batch), kD, 0, st>>>(cache_len, cache_cap, window, sink, ws,
-                                                                 static_cast<uint16_t*>(out));
+  decode_attn_kernel<<<dim3((unsigned)nsplit, kG, (unsigned)batch), 64, 0, st>>>(cache_len, cache_cap,
+                                                                                 window, kc, vc, ws);
+  decode_merge_kernel<<<dim3(kH, (unsigned)batch), 256, 0, st>>>(cache_len, cache_cap, window, sink,
+                                                                  ws, static_cast<uint16_t*>(out));
   if (hipGetLastError() != hipSuccess) return FLINT_ERR_HIP;
   if (debug_sync()) {
     int32_t flags = 0;

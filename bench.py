@@ -10,6 +10,9 @@ a seeded generator, resident in HBM before the timed region. One step = one
 flint_attn_fwd call (schedule, K/V prologue, attention kernel).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config tstar|c1|c2|c3|c4|c4full|c5]
+       python bench.py --decode [--decode-batch B] [--decode-len L] [--decode-window W]
+                                         (one decode step per sequence over an L-token
+                                          KV cache: HBM GB/s against 8 TB/s)
        python bench.py --copy-probe     (plain device copy of known size, for
                                           calibrating FETCH_SIZE / WRITE_SIZE)
 Prints one JSON line.
@@ -136,6 +139,85 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": 3}), flush=True)
 
 
+def decode_bench(args):
+    """Decode step: append the new token, attend over the cache, merge the splits.
+
+    The cache holds decode_len tokens per sequence (filled with kv_append from
+    seeded N(0,1) keys and values); every timed step decodes token decode_len
+    of every sequence (the same slot each time, so the length stays fixed).
+    Algorithmic HBM bytes per step: the cached K' and V^T the step reads, 2 KiB
+    per attended token per sequence (4 kv heads x 128 channels x 2 bytes x 2),
+    plus q, k, v and out of the new token.
+    """
+    import torch
+
+    import attention_head_rmsnorm_amd as fa
+    from workload.gen import _bf16, _draw_params
+
+    B, L, W = args.decode_batch, args.decode_len, args.decode_window
+    dev = torch.device("cuda", 0)
+    rng = np.random.default_rng(2001)
+    qw, kw, sinks = _draw_params(rng, 1.0)
+    use_rope = W > 0
+    cache = fa.KVCache(B, W, max_tokens=L + 1, use_rope=use_rope, device=dev)
+    qw, kw, sinks = qw.to(dev), kw.to(dev), sinks.to(dev)
+    chunk = cache.cap if W > 0 else L
+    for c0 in range(0, L, chunk):
+        n = min(chunk, L - c0)
+        k = _bf16(rng.standard_normal((B, n, 4, 128), dtype=np.float32)).to(dev)
+        v = _bf16(rng.standard_normal((B, n, 4, 128), dtype=np.float32)).to(dev)
+        cache.append(k, v, kw)
+    q = _bf16(rng.standard_normal((B, 32, 128), dtype=np.float32)).to(dev)
+    k1 = _bf16(rng.standard_normal((B, 4, 128), dtype=np.float32)).to(dev)
+    v1 = _bf16(rng.standard_normal((B, 4, 128), dtype=np.float32)).to(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    p = lambda t: int(t.data_ptr())  # noqa: E731
+    call = [p(q), p(k1), p(v1), p(qw), p(kw), p(sinks), 0, p(cache.length), B, p(cache.k),
+            p(cache.vt), cache.cap, 32, 4, 128, W, int(use_rope), 1.0e6, 1.0e-6,
+            p(cache.workspace), cache.workspace.numel(), p(out), int(stream.cuda_stream)]
+    for _ in range(args.warmup):
+        fa.flint_attn_decode(*call)
+    torch.cuda.synchronize()
+    st, flags = cache.device_status()
+    if st != 0:
+        raise RuntimeError(f"decode device error flags {flags}")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        st = fa.flint_attn_decode(*call)
+        if st != 0:
+            raise RuntimeError(fa.flint_attn_strerror(st))
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    attended = min(L + 1, W) if W > 0 else L + 1
+    alg = B * (attended * 2048.0 + (32 + 4 + 4 + 32) * 256.0)
+    gbs = alg / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "decode step HBM GB/s (one token per sequence, KV cache read once)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "tokens_per_s": round(B / (ms * 1e-3), 1),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 cache contents, q, k, v)",
+        "config": {"workload": f"decode, batch {B}, {L} cached tokens, "
+                               + (f"sliding window {W} (RoPE)" if W else "full attention (NoPE)"),
+                   "batch": B, "cached_tokens": L, "window": W, "attended_tokens": attended,
+                   "cache_cap": cache.cap},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": alg, "traffic": None},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +227,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--decode-batch", type=int, default=64)
+    ap.add_argument("--decode-len", type=int, default=8192)
+    ap.add_argument("--decode-window", type=int, default=0)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -156,6 +242,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.decode:
+        decode_bench(args)
         return
 
     import attention_head_rmsnorm_amd as fa
