@@ -1568,11 +1568,12 @@ extern "C" int flint_attn_decode(const void* q, const void* k, const void* v, co
     return FLINT_ERR_ALIGN;
   const DecLayout L = make_dec_layout(batch, cache_cap);
   DecWs ws = dec_ws(workspace, L);
-  // Split size: the largest that still gives about 4096 waves (4 per SIMD)
-  // over the cache's blocks, at least kDecMinSplitBlocks.
+  // Split size: the largest that still gives about 2048 waves (2 per SIMD,
+  // the occupancy of the attention kernel) over the cache's blocks, at least
+  // kDecMinSplitBlocks; larger splits leave less for the merge.
   const int64_t blocks = (int64_t)batch * kG * (cache_cap / kDecBlock + 1);
   int bps = kDecMaxSplitBlocks;
-  while (bps > kDecMinSplitBlocks && blocks / bps < 4096) bps /= 2;
+  while (bps > kDecMinSplitBlocks && blocks / bps < 2048) bps /= 2;
   ws.bps = bps;
   const int nsplit = (int)((cache_cap / kDecBlock + 1 + bps - 1) / bps);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
