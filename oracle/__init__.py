@@ -13,3 +13,4 @@ from .flint_oracle import (  # noqa: F401
     rope_neox,
     sink_softmax,
 )
+from .flint_oracle_bwd import flint_attention_backward  # noqa: F401,E402

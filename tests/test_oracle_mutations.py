@@ -122,3 +122,78 @@ def test_mutation_is_caught(name, monkeypatch):
             caught.append(pin.__name__)
             break
     assert caught, f"no pin caught the planted mistake '{name}'"
+
+
+# ---------------------------------------------------------------- backward oracle
+
+import oracle.flint_oracle_bwd as fb  # noqa: E402
+
+from . import oracle_bwd_pins  # noqa: E402
+
+_rope_adj = fb._rope_adjoint
+_rms_bwd = fb._rms_norm_backward
+_sm_bwd = fb._softmax_backward
+
+
+def _rope_adjoint_forward_turn(x, pos, theta):
+    return fo.rope_neox(x, pos, theta)
+
+
+def _rms_bwd_no_mean_term(x, w, eps, dy):
+    x = np.asarray(x, np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return r * dy * w, dy * x * r
+
+
+def _rms_bwd_weight_unnormalized(x, w, eps, dy):
+    dx, _ = _rms_bwd(x, w, eps, dy)
+    return dx, dy * np.asarray(x, np.float64)
+
+
+def _rms_bwd_weight_missing(x, w, eps, dy):
+    return _rms_bwd(x, np.ones_like(np.asarray(w, np.float64)), eps, dy)
+
+
+def _softmax_bwd_no_row_term(W, dW, Dr):
+    return W * dW
+
+
+def _softmax_bwd_row_term_unweighted(W, dW, Dr):
+    return W * dW - Dr[:, None]
+
+
+def _sink_adjoint_sign(p, Dr):
+    return float(np.sum(p * Dr))
+
+
+def _sink_adjoint_complement(p, Dr):
+    return -float(np.sum((1.0 - p) * Dr))
+
+
+BWD_MUTATIONS = {
+    "rope adjoint turns forward": ("_rope_adjoint", _rope_adjoint_forward_turn),
+    "rmsnorm backward without the mean term": ("_rms_norm_backward", _rms_bwd_no_mean_term),
+    "norm weight gradient unnormalized": ("_rms_norm_backward", _rms_bwd_weight_unnormalized),
+    "norm weight missing in backward": ("_rms_norm_backward", _rms_bwd_weight_missing),
+    "softmax backward without Dr": ("_softmax_backward", _softmax_bwd_no_row_term),
+    "softmax backward Dr not weighted": ("_softmax_backward", _softmax_bwd_row_term_unweighted),
+    "sink adjoint sign": ("_sink_adjoint", _sink_adjoint_sign),
+    "sink adjoint with 1 - p": ("_sink_adjoint", _sink_adjoint_complement),
+    "logit scale 1": ("_logit_scale", lambda d: 1.0),
+}
+
+_BWD_ORDER = list(oracle_bwd_pins.ALL_PINS)  # already cheapest first
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_backward_mutation_is_caught(name, monkeypatch):
+    attr, bad = BWD_MUTATIONS[name]
+    monkeypatch.setattr(fb, attr, bad)
+    caught = []
+    for pin in _BWD_ORDER:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no backward pin caught the planted mistake '{name}'"

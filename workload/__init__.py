@@ -13,4 +13,5 @@ from .gen import (  # noqa: F401
     make_workload,
     make_custom,
     make_long_decode,
+    draw_dout,
 )

@@ -253,3 +253,11 @@ def make_long_decode(seed: int, n_cached: int, layers=(FULL,), sink_std: float =
     wl.meta["v_all"] = _bf16(v)
     return wl
 
+
+
+def draw_dout(seed: int, T: int, std: float = 1.0) -> torch.Tensor:
+    """Upstream gradient dL/dO [T, 32, 128] for a backward check: float32
+    normals (stream seeded with seed + 7919, so it is not the q/k/v stream of
+    the same seed) rounded to bfloat16."""
+    rng = np.random.default_rng(seed + 7919)
+    return _bf16(_normal(rng, (T, NUM_Q_HEADS, HEAD_DIM), std))
