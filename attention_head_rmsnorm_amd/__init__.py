@@ -1,4 +1,4 @@
-"""Flint sink-aware attention forward (prefill and decode) for AMD Instinct MI355X.
+"""Flint sink-aware attention (prefill forward and backward, decode) for AMD Instinct MI355X.
 
 The compute path is the HIP library ``libflint_attn.so`` (C ABI in
 ``include/flint_attn.h``); this package only binds it.
@@ -23,6 +23,10 @@ from .binding import (  # noqa: F401
     FLINT_PHASE_SCHEDULE,
     FlintError,
     flint_attn,
+    flint_attn_backward,
+    flint_attn_bwd,
+    flint_attn_bwd_workspace_bytes,
+    flint_attn_fwd_lse,
     flint_attn_decode,
     flint_attn_decode_workspace_bytes,
     flint_attn_device_status,

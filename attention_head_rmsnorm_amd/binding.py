@@ -49,6 +49,9 @@ EXPORTED = (
     "flint_attn_decode_workspace_bytes",
     "flint_attn_kv_append",
     "flint_attn_decode",
+    "flint_attn_fwd_lse",
+    "flint_attn_bwd_workspace_bytes",
+    "flint_attn_bwd",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -95,6 +98,14 @@ def load_library() -> ctypes.CDLL:
     lib.flint_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32,
                                       i32, i32, i32, f32, f32, vp, sz, vp, vp]
     lib.flint_attn_decode.restype = ctypes.c_int
+    lib.flint_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                       i32, i32, i32, f32, f32, vp, sz, vp, vp, vp]
+    lib.flint_attn_fwd_lse.restype = ctypes.c_int
+    lib.flint_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.flint_attn_bwd_workspace_bytes.restype = sz
+    lib.flint_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                   i32, i32, f32, f32, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp]
+    lib.flint_attn_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -130,6 +141,38 @@ def flint_attn_fwd_phases(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqle
                                                     head_dim, window, use_rope, rope_theta, eps,
                                                     workspace, workspace_bytes, out, stream,
                                                     phases))
+
+
+def flint_attn_fwd_lse(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused, n_seqs,
+                       max_seqlen, total_tokens, num_q_heads, num_kv_heads, head_dim, window,
+                       use_rope, rope_theta, eps, workspace, workspace_bytes, out, lse,
+                       stream) -> int:
+    """flint_attn_fwd that also writes the per-row normalizer lse (float32 [T, 32])."""
+    return int(load_library().flint_attn_fwd_lse(q, k, v, q_norm_w, k_norm_w, sink, positions,
+                                                 cu_seqlens, seqused, n_seqs, max_seqlen,
+                                                 total_tokens, num_q_heads, num_kv_heads,
+                                                 head_dim, window, use_rope, rope_theta, eps,
+                                                 workspace, workspace_bytes, out, lse, stream))
+
+
+def flint_attn_bwd_workspace_bytes(total_tokens: int, n_seqs: int, max_seqlen: int,
+                                   num_kv_heads: int = NUM_KV_HEADS,
+                                   head_dim: int = HEAD_DIM) -> int:
+    return int(load_library().flint_attn_bwd_workspace_bytes(total_tokens, n_seqs, max_seqlen,
+                                                             num_kv_heads, head_dim))
+
+
+def flint_attn_bwd(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused, n_seqs,
+                   max_seqlen, total_tokens, num_q_heads, num_kv_heads, head_dim, window, use_rope,
+                   rope_theta, eps, out, lse, dout, workspace, workspace_bytes, dq, dk, dv,
+                   dq_norm_w, dk_norm_w, dsink, stream) -> int:
+    """The backward C entry point with pointer arguments as ints; returns the status."""
+    return int(load_library().flint_attn_bwd(q, k, v, q_norm_w, k_norm_w, sink, positions,
+                                             cu_seqlens, seqused, n_seqs, max_seqlen,
+                                             total_tokens, num_q_heads, num_kv_heads, head_dim,
+                                             window, use_rope, rope_theta, eps, out, lse, dout,
+                                             workspace, workspace_bytes, dq, dk, dv, dq_norm_w,
+                                             dk_norm_w, dsink, stream))
 
 
 def flint_attn_seqused_from_mask(mask, batch, seqlen, seqused, n_bad, stream) -> int:
@@ -210,19 +253,9 @@ def seqused_from_mask(attention_mask):
     return seqused
 
 
-def flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens=None,
-               attention_mask=None, seqused=None, max_seqlen: Optional[int] = None,
-               window: int = 513, use_rope: bool = True, rope_theta: float = 1.0e6,
-               eps: float = 1.0e-6, out=None, workspace=None):
-    """Sink-aware GQA attention forward on torch tensors.
-
-    q: bf16 [B, S, 32, 128] (BSHD) or [T, 32, 128] (THD); k, v: bf16 with 4
-    heads in the same layout. q_norm_w, k_norm_w: fp32 [128]; sinks: fp32 [32].
-    THD takes ``cu_seqlens`` (int32 [n+1], device) and, optionally,
-    ``max_seqlen``; BSHD takes ``attention_mask`` [B, S] (trailing padding) or
-    ``seqused`` [B]. ``positions`` is int32 [B, S] or [T] (default: index in
-    the sequence). Returns the output in q's layout.
-    """
+def _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, attention_mask,
+                seqused, max_seqlen):
+    """Checks the layer's tensors; returns (T, n, max_seqlen, cu, seqused, positions)."""
     import torch
 
     if not q.is_cuda:
@@ -276,19 +309,90 @@ def flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens
         if positions.dtype != torch.int32 or positions.device != dev or positions.numel() != T:
             raise TypeError("positions must be int32 with one entry per token, on the device")
         positions = positions.contiguous()
+    return T, n, mx, cu, seqused, positions
+
+
+def flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens=None,
+               attention_mask=None, seqused=None, max_seqlen: Optional[int] = None,
+               window: int = 513, use_rope: bool = True, rope_theta: float = 1.0e6,
+               eps: float = 1.0e-6, out=None, workspace=None, return_lse: bool = False):
+    """Sink-aware GQA attention forward on torch tensors.
+
+    q: bf16 [B, S, 32, 128] (BSHD) or [T, 32, 128] (THD); k, v: bf16 with 4
+    heads in the same layout. q_norm_w, k_norm_w: fp32 [128]; sinks: fp32 [32].
+    THD takes ``cu_seqlens`` (int32 [n+1], device) and, optionally,
+    ``max_seqlen``; BSHD takes ``attention_mask`` [B, S] (trailing padding) or
+    ``seqused`` [B]. ``positions`` is int32 [B, S] or [T] (default: index in
+    the sequence). Returns the output in q's layout; with ``return_lse`` also
+    the per-row normalizer, float32 [..., 32] in natural-log units (what the
+    backward takes).
+    """
+    import torch
+
+    T, n, mx, cu, seqused, positions = _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions,
+                                                   cu_seqlens, attention_mask, seqused, max_seqlen)
+    dev = q.device
     if out is None:
         out = torch.empty_like(q)
     nbytes = flint_attn_workspace_bytes(T, n, mx, k.shape[-2], k.shape[-1])
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    st = flint_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(sinks),
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(sinks),
+            _ptr(positions), _ptr(cu), _ptr(seqused), n, mx, T, q.shape[-2], k.shape[-2],
+            q.shape[-1], int(window), int(bool(use_rope)), float(rope_theta), float(eps),
+            _ptr(workspace), workspace.numel(), _ptr(out))
+    if not return_lse:
+        st = flint_attn_fwd(*args, _stream_handle(dev))
+        if st != FLINT_OK:
+            raise FlintError(st, "flint_attn_fwd")
+        return out
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    st = flint_attn_fwd_lse(*args, _ptr(lse), _stream_handle(dev))
+    if st != FLINT_OK:
+        raise FlintError(st, "flint_attn_fwd_lse")
+    return out, lse
+
+
+def flint_attn_backward(dout, q, k, v, q_norm_w, k_norm_w, sinks, out, lse, *, positions=None,
+                        cu_seqlens=None, attention_mask=None, seqused=None,
+                        max_seqlen: Optional[int] = None, window: int = 513,
+                        use_rope: bool = True, rope_theta: float = 1.0e6, eps: float = 1.0e-6,
+                        workspace=None):
+    """Gradients of the layer for upstream ``dout`` (bf16, the output's layout).
+
+    ``out`` and ``lse`` are what ``flint_attn(..., return_lse=True)`` returned
+    for the same inputs. Returns (dq, dk, dv, dq_norm_w, dk_norm_w, dsinks):
+    bf16 in the layouts of q, k, v and float32 for the parameters.
+    """
+    import torch
+
+    T, n, mx, cu, seqused, positions = _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions,
+                                                   cu_seqlens, attention_mask, seqused, max_seqlen)
+    dev = q.device
+    for name, t, dt in (("dout", dout, torch.bfloat16), ("out", out, torch.bfloat16),
+                        ("lse", lse, torch.float32)):
+        if t.dtype != dt or not t.is_contiguous() or t.device != dev:
+            raise TypeError(f"{name} must be a contiguous {dt} tensor on {dev}")
+    if dout.shape != q.shape or out.shape != q.shape or lse.shape != q.shape[:-1]:
+        raise ValueError("dout and out must have q's shape and lse q's shape without head_dim")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dqw = torch.empty_like(q_norm_w)
+    dkw = torch.empty_like(k_norm_w)
+    dsk = torch.empty_like(sinks)
+    nbytes = flint_attn_bwd_workspace_bytes(T, n, mx, k.shape[-2], k.shape[-1])
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = flint_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(sinks),
                         _ptr(positions), _ptr(cu), _ptr(seqused), n, mx, T, q.shape[-2],
                         k.shape[-2], q.shape[-1], int(window), int(bool(use_rope)),
-                        float(rope_theta), float(eps), _ptr(workspace), workspace.numel(),
-                        _ptr(out), _stream_handle(dev))
+                        float(rope_theta), float(eps), _ptr(out), _ptr(lse), _ptr(dout),
+                        _ptr(workspace), workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv),
+                        _ptr(dqw), _ptr(dkw), _ptr(dsk), _stream_handle(dev))
     if st != FLINT_OK:
-        raise FlintError(st, "flint_attn_fwd")
-    return out
+        raise FlintError(st, "flint_attn_bwd")
+    return dq, dk, dv, dqw, dkw, dsk
 
 
 class KVCache:

@@ -13,7 +13,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "flint_attn.hip")
+CSRC = os.path.join(PKG, "csrc")
+SRCS = [os.path.join(CSRC, "flint_attn.hip"), os.path.join(CSRC, "flint_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflint_attn.so")
 
@@ -39,7 +40,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False, extra_flags=()) -> str:
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

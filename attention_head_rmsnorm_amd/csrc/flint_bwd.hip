@@ -1,0 +1,1033 @@
+// Flint sink-aware attention backward for AMD Instinct MI355X (gfx950).
+//
+// Gradients of the layer of flint_attn.hip (NeMo AutoModel "flint" page,
+// "Model Architecture"; flint.layers API page, FlintAttention; Hugging Face
+// discussion #26 on RecursiveSI/flint, "What was unusually easy", and "Where
+// other stacks fail" for the sink in backward). With Z = Q'K'^T / sqrt(d),
+// W the sink softmax and O = W V, an upstream dO gives
+//   Dr = rowsum(dO * O),  dZ = W * (dO V^T - Dr),
+//   dV = W^T dO,  dQ' = dZ K' / sqrt(d),  dK' = dZ^T Q' / sqrt(d),
+//   d sink_h = -sum_t p_sink(t, h) Dr(t, h)   (the sink has value 0),
+// then the adjoint of the RoPE rotation (the opposite turn) and of the
+// weight-form RMSNorm, which also yields the two norm-weight gradients.
+// W is recomputed from the forward's per-row normalizer lse: W = exp(Z - lse).
+//
+// Kernels, in order on the caller's stream:
+//   schedule_kernel (forward)  sequence table, key tiles, query blocks.
+//   bwd_schedule_kernel   one workgroup: splits the query range seen by each
+//                         128-key block into chunks of about equal work and
+//                         orders the chunks by decreasing work.
+//   bwd_kv_prep_kernel    per (64-key tile, kv head): K' = RoPE(RMSNorm(k)) in
+//                         bf16 as a K' operand tile, V as a V operand tile, and
+//                         K'^T in the key-slot order of the dQ product; zero dq
+//                         rows of padded tokens.
+//   bwd_q_prep_kernel     per (32-query block, head): Q' (with the softmax
+//                         scale in log2 units, rounded as the forward rounds
+//                         it) and dO as operand tiles and transposed
+//                         (query-slot order), the row
+//                         terms lse (log2 units) and Dr, the block's share of
+//                         the sink adjoint.
+//   bwd_dq_kernel         query-major: per (query block, 4 heads of a kv head),
+//                         over the key tiles in the window: S^T = K'Q'^T,
+//                         dP^T = V dO^T, dS^T, dQ'^T += K'^T dS^T; then RoPE and
+//                         RMSNorm adjoints, dq, and the block's q-norm-weight
+//                         terms.
+//   bwd_dkdv_kernel       key-major: per (128 keys, kv head, query chunk), over
+//                         the chunk's query blocks x 8 heads: S = Q'K'^T,
+//                         dP = dO V^T, dS, dV^T += dO^T P, dK'^T += Q'^T dS, as
+//                         FP32 partial sums of the chunk.
+//   bwd_kv_reduce_kernel  per (64-key tile, kv head): sums the chunks in a fixed
+//                         order, RoPE and RMSNorm adjoints, dk, dv, and the
+//                         tile's k-norm-weight terms.
+//   bwd_finalize_kernel   sums the norm-weight terms and the sink shares in a
+//                         fixed order (the result does not depend on timing).
+// Every product runs on v_mfma_f32_32x32x16_bf16 with FP32 accumulation.
+
+#include <hip/hip_runtime.h>
+
+#include "flint_common.h"
+
+namespace flint {
+
+constexpr int kBwdThreads = 256;             // four waves
+constexpr int kKvbPart = kBN * kD * 2;       // 16 KiB: one 64-key operand part
+constexpr int kKvbBytes = 3 * kKvbPart;      // K' | V | K'^T (key-slot order)
+constexpr int kKvbVecPerWave = kKvbBytes / (16 * kBwdThreads);  // 12
+constexpr int kQtPart = kBM * kD * 2;        // 8 KiB: one 32-query operand part
+constexpr int kQtStats = 2 * kBM * 4;        // lse (log2 units) [32], Dr [32]
+constexpr int kQtBytes = 4 * kQtPart + kQtStats;  // Q' | dO | Q'^T | dO^T | stats
+constexpr int kQtVecPerWave = 4 * kQtPart / (16 * kBwdThreads);  // 8
+constexpr int kBwdStages = 3;
+constexpr int kKB = 2 * kBN;                 // keys per dK/dV item
+constexpr int kTargetChunks = 512;           // about this many key-major items per kv head
+constexpr int kMinChunkQB = 8;               // query blocks per chunk, at least
+constexpr int kHdrNC = 8;                    // header: key-major items
+constexpr int kHdrCH = 9;                    // header: query blocks per chunk
+constexpr float kInvSqrtD = 0.08838834764831845f;
+constexpr int kPartFloats = 2 * kKB * kD;    // dK' and dV of one chunk
+
+struct BwdWs {
+  Ws f;            // the forward schedule's regions
+  char* kvb;       // [kG][ntmax][kKvbBytes]
+  char* qt;        // [nqmax][kH][kQtBytes]
+  float* sinkpart; // [kH][nqmax]: sum over the block's rows of p_sink * Dr
+  float* wq;       // [kD][nqmax * 2 * kG]: q-norm-weight terms per dQ workgroup
+  float* wk;       // [kD][ntmax * kG]: k-norm-weight terms per (tile, kv head)
+  int* cb;         // [ntmax] first chunk slot of the key block starting at tile e
+  int* nc;         // [ntmax] its chunks
+  int2* kitems;    // [ncmax] {tile, chunk}, most work first
+  float* part;     // [ncmax][kG][kPartFloats]
+  int nqmax, ncmax, n;
+};
+
+struct BwdLayout {
+  Layout f;
+  size_t kvb, qt, sinkpart, wq, wk, cb, nc, kitems, part, total;
+  int64_t ncmax;
+};
+
+static BwdLayout make_bwd_layout(int64_t T, int64_t n) {
+  BwdLayout L;
+  L.f = make_layout(T, n, false);
+  L.ncmax = kTargetChunks + L.f.ntmax;
+  size_t o = L.f.total;
+  L.kvb = o;      o = align_up(o + (size_t)kG * L.f.ntmax * kKvbBytes, 256);
+  L.qt = o;       o = align_up(o + (size_t)L.f.nqmax * kH * kQtBytes, 256);
+  L.sinkpart = o; o = align_up(o + (size_t)kH * L.f.nqmax * 4, 256);
+  L.wq = o;       o = align_up(o + (size_t)kD * L.f.nqmax * 2 * kG * 4, 256);
+  L.wk = o;       o = align_up(o + (size_t)kD * L.f.ntmax * kG * 4, 256);
+  L.cb = o;       o = align_up(o + (size_t)L.f.ntmax * 4, 256);
+  L.nc = o;       o = align_up(o + (size_t)L.f.ntmax * 4, 256);
+  L.kitems = o;   o = align_up(o + (size_t)L.ncmax * 8, 256);
+  L.part = o;     o = align_up(o + (size_t)L.ncmax * kG * kPartFloats * 4, 256);
+  L.total = o;
+  return L;
+}
+
+// ----------------------------------------------------------------- helpers
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
+}
+
+// One 16-byte vector per lane from global memory straight into LDS: lane L's
+// vector lands at `lds` + 16 L.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld_frag(const uint4* p) { return __builtin_bit_cast(bf16x8, *p); }
+
+__device__ __forceinline__ bf16x8 pack_frag(const float* x) { return __builtin_bit_cast(bf16x8, pack8(x)); }
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Query blocks [*lo, *hi) that see some key of the 128-key block starting at
+// key k0 of a sequence with valid length u (none when k0 >= u).
+__device__ __forceinline__ void kb_queries(int k0, int u, int window, int* lo, int* hi) {
+  if (k0 >= u) {
+    *lo = *hi = 0;
+    return;
+  }
+  const int last_key = min(k0 + kKB, u) - 1;
+  const int q_end = window > 0 ? min(u, last_key + window) : u;
+  *lo = k0 / kBM;
+  *hi = (q_end + kBM - 1) / kBM;
+}
+
+// Work of the key block that starts at tile e (query blocks), 0 for odd tiles.
+__device__ __forceinline__ int kb_work(const BwdWs& ws, int e, int window, int* lo) {
+  const int2 te = ws.f.tiles[e];
+  if (te.y & 1) return 0;
+  const int u = ws.f.seq[te.x].z;
+  int hi;
+  kb_queries(te.y * kBN, u, window, lo, &hi);
+  return hi - *lo;
+}
+
+// ----------------------------------------------------------------- schedule
+
+__global__ __launch_bounds__(1024) void bwd_schedule_kernel(int window, BwdWs ws) {
+  __shared__ int tmp[1024];
+  __shared__ int hist[kBuckets];
+  const int tid = threadIdx.x;
+  const int NT = ws.f.hdr[1];
+  // total work, then the chunk size that gives about kTargetChunks chunks
+  int lo;
+  int local = 0;
+  for (int e = tid; e < NT; e += 1024) local += kb_work(ws, e, window, &lo);
+  int total;
+  (void)block_excl_scan(local, tmp, &total);
+  const int CH = max(kMinChunkQB, (total + kTargetChunks - 1) / kTargetChunks);
+
+  int carry = 0;
+  for (int base = 0; base < NT; base += 1024) {
+    const int e = base + tid;
+    const int w = e < NT ? kb_work(ws, e, window, &lo) : 0;
+    const int c = (w + CH - 1) / CH;
+    int tot;
+    const int ex = block_excl_scan(c, tmp, &tot);
+    if (e < NT) {
+      ws.cb[e] = carry + ex;
+      ws.nc[e] = c;
+    }
+    carry += tot;
+  }
+  for (int i = tid; i < kBuckets; i += 1024) hist[i] = 0;
+  __syncthreads();
+  for (int e = tid; e < NT; e += 1024) {
+    const int w = kb_work(ws, e, window, &lo);
+    for (int c = 0; c * CH < w; ++c) atomicAdd(&hist[min(min(CH, w - c * CH), kBuckets - 1)], 1);
+  }
+  __syncthreads();
+  int local4[4], sum = 0;
+  for (int j = 0; j < 4; ++j) {
+    local4[j] = hist[kBuckets - 1 - (4 * tid + j)];
+    sum += local4[j];
+  }
+  int tot;
+  int run = block_excl_scan(sum, tmp, &tot);
+  for (int j = 0; j < 4; ++j) {
+    hist[kBuckets - 1 - (4 * tid + j)] = run;
+    run += local4[j];
+  }
+  __syncthreads();
+  for (int e = tid; e < NT; e += 1024) {
+    const int w = kb_work(ws, e, window, &lo);
+    for (int c = 0; c * CH < w; ++c) {
+      const int pos = atomicAdd(&hist[min(min(CH, w - c * CH), kBuckets - 1)], 1);
+      ws.kitems[pos] = make_int2(e, c);
+    }
+  }
+  if (tid == 0) {
+    ws.f.hdr[kHdrNC] = carry;
+    ws.f.hdr[kHdrCH] = CH;
+  }
+}
+
+// ----------------------------------------------------------------- K/V prep
+
+__global__ __launch_bounds__(256) void bwd_kv_prep_kernel(const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          const float* __restrict__ k_norm_w,
+                                                          const int* __restrict__ positions,
+                                                          float eps, int use_rope, BwdWs ws,
+                                                          uint16_t* __restrict__ dq) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kD * kBN];
+  const int e = blockIdx.x, g = blockIdx.y;
+  if (e >= ws.f.hdr[1]) return;
+  const int2 te = ws.f.tiles[e];
+  const int4 meta = ws.f.seq[te.x];
+  const int start = meta.x, len = meta.y, u = meta.z;
+  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
+  const int ell = te.y * kBN + r;
+  const bool valid = ell < u;
+  const size_t t = (size_t)start + ell;
+  char* tile = ws.kvb + ((size_t)g * ws.f.ntmax + e) * kKvbBytes;
+  const int b = r >> 5, col = r & 31;
+
+  // K': channels [16p, 16p+16) and their RoPE partners +64.
+  float x[32];
+  if (valid) {
+    const uint4* src = reinterpret_cast<const uint4*>(k + (t * kG + g) * kD);
+    unpack8(src[2 * p], x);
+    unpack8(src[2 * p + 1], x + 8);
+    unpack8(src[8 + 2 * p], x + 16);
+    unpack8(src[9 + 2 * p], x + 24);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.f;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) ss += x[i] * x[i];
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[i] *= rstd * k_norm_w[16 * p + i];
+    x[16 + i] *= rstd * k_norm_w[64 + 16 * p + i];
+  }
+  if (use_rope && valid) {
+    const int pos = positions ? positions[t] : ell;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float c, s;
+      rope_cos_sin(pos, ws.f.rope_r[16 * p + i], &c, &s);
+      const float a = x[i], bb = x[16 + i];
+      x[i] = a * c - bb * s;
+      x[16 + i] = bb * c + a * s;
+    }
+  }
+  {
+    uint4* kfrag = reinterpret_cast<uint4*>(tile);
+    const uint4 w[4] = {pack8(x), pack8(x + 8), pack8(x + 16), pack8(x + 24)};
+    kfrag[frag_index(b, 8, p, 0, col)] = w[0];
+    kfrag[frag_index(b, 8, p, 1, col)] = w[1];
+    kfrag[frag_index(b, 8, 4 + p, 0, col)] = w[2];
+    kfrag[frag_index(b, 8, 4 + p, 1, col)] = w[3];
+    // K'^T in key-slot order, through LDS
+    const int slot = vt_slot(r);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint32_t w4[4] = {w[q4].x, w[q4].y, w[q4].z, w[q4].w};
+      const int d0 = (q4 < 2 ? 16 * p + 8 * q4 : 64 + 16 * p + 8 * (q4 - 2));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kt[(d0 + 2 * j) * kBN + slot] = (uint16_t)(w4[j] & 0xffff);
+        kt[(d0 + 2 * j + 1) * kBN + slot] = (uint16_t)(w4[j] >> 16);
+      }
+    }
+  }
+  // V operand tile: key rows, channels [32p, 32p+32)
+  {
+    uint4* vfrag = reinterpret_cast<uint4*>(tile + kKvbPart);
+    const uint4* src = reinterpret_cast<const uint4*>(v + (t * kG + g) * kD);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vfrag[frag_index(b, 8, 2 * p + (i >> 1), i & 1, col)] = valid ? src[4 * p + i] : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  {
+    uint4* ktile = reinterpret_cast<uint4*>(tile + 2 * kKvbPart);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qv = tid + 256 * i;
+      const int d = qv >> 3, c = qv & 7;
+      ktile[frag_index(d >> 5, 4, c >> 1, c & 1, d & 31)] =
+          *reinterpret_cast<const uint4*>(&kt[d * kBN + c * 8]);
+    }
+  }
+  // Padded query rows of this kv head's 8 query heads get zero gradients.
+  if (ell >= u && ell < len) {
+    uint4* dst = reinterpret_cast<uint4*>(dq + (t * kH + (size_t)g * kHpg) * kD);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) dst[p * 32 + i] = z;
+  }
+}
+
+// ----------------------------------------------------------------- Q / dO prep
+
+__global__ __launch_bounds__(256) void bwd_q_prep_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ o,
+                                                         const uint16_t* __restrict__ dout,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ q_norm_w,
+                                                         const float* __restrict__ sink,
+                                                         const int* __restrict__ positions,
+                                                         float eps, int use_rope, BwdWs ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t qts[kD * kBM];
+  __shared__ __attribute__((aligned(16))) uint16_t dts[kD * kBM];
+  __shared__ float red[4];
+  const int qg = blockIdx.x, h = blockIdx.y;
+  if (qg >= ws.f.hdr[2]) return;
+  const int s = find_seq(ws.f.qbase, ws.n, qg);
+  const int qb = qg - ws.f.qbase[s];
+  const int4 meta = ws.f.seq[s];
+  const int start = meta.x, u = meta.z;
+  const int tid = threadIdx.x, r = tid >> 3, p = tid & 7;
+  const int ell = qb * kBM + r;
+  const bool valid = ell < u;
+  const size_t t = (size_t)start + ell;
+  char* tile = ws.qt + ((size_t)qg * kH + h) * kQtBytes;
+
+  // this thread: channels [8p, 8p+8) and their RoPE partners +64
+  float x[16], dy[16], y[16];
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  const size_t row = (t * kH + h) * kD;
+  const uint4 qa = valid ? *reinterpret_cast<const uint4*>(q + row + 8 * p) : z4;
+  const uint4 qc = valid ? *reinterpret_cast<const uint4*>(q + row + 64 + 8 * p) : z4;
+  const uint4 da = valid ? *reinterpret_cast<const uint4*>(dout + row + 8 * p) : z4;
+  const uint4 dc = valid ? *reinterpret_cast<const uint4*>(dout + row + 64 + 8 * p) : z4;
+  const uint4 oa = valid ? *reinterpret_cast<const uint4*>(o + row + 8 * p) : z4;
+  const uint4 oc = valid ? *reinterpret_cast<const uint4*>(o + row + 64 + 8 * p) : z4;
+  unpack8(qa, x);
+  unpack8(qc, x + 8);
+  unpack8(da, dy);
+  unpack8(dc, dy + 8);
+  unpack8(oa, y);
+  unpack8(oc, y + 8);
+  float ss = 0.f, dr = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ss += x[i] * x[i];
+    dr += dy[i] * y[i];
+  }
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    ss += __shfl_xor(ss, off);
+    dr += __shfl_xor(dr, off);
+  }
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[i] *= rstd * q_norm_w[8 * p + i];
+    x[8 + i] *= rstd * q_norm_w[64 + 8 * p + i];
+  }
+  if (use_rope && valid) {
+    const int pos = positions ? positions[t] : ell;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float c, sn;
+      rope_cos_sin(pos, ws.f.rope_r[8 * p + i], &c, &sn);
+      const float a = x[i], bb = x[8 + i];
+      x[i] = a * c - bb * sn;
+      x[8 + i] = bb * c + a * sn;
+    }
+  }
+  // the softmax scale in log2 units, applied and rounded as in the forward, so
+  // the logits recomputed here are the forward's own
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] *= kLog2e * kInvSqrtD;
+  const uint4 w0 = pack8(x), w1 = pack8(x + 8);
+  uint4* qf = reinterpret_cast<uint4*>(tile);
+  uint4* df = reinterpret_cast<uint4*>(tile + kQtPart);
+  // channels 8p.. are k-step p>>1, half p&1; channels 64+8p.. are k-step 4+(p>>1)
+  qf[frag_index(0, 8, p >> 1, p & 1, r)] = w0;
+  qf[frag_index(0, 8, 4 + (p >> 1), p & 1, r)] = w1;
+  df[frag_index(0, 8, p >> 1, p & 1, r)] = da;
+  df[frag_index(0, 8, 4 + (p >> 1), p & 1, r)] = dc;
+  {
+    const int slot = vt_slot(r);
+    const uint32_t wq[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const uint32_t wd[8] = {da.x, da.y, da.z, da.w, dc.x, dc.y, dc.z, dc.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = (j < 4 ? 8 * p : 64 + 8 * p) + 2 * (j & 3);
+      qts[d * kBM + slot] = (uint16_t)(wq[j] & 0xffff);
+      qts[(d + 1) * kBM + slot] = (uint16_t)(wq[j] >> 16);
+      dts[d * kBM + slot] = (uint16_t)(wd[j] & 0xffff);
+      dts[(d + 1) * kBM + slot] = (uint16_t)(wd[j] >> 16);
+    }
+  }
+  // row terms and the block's share of the sink adjoint
+  float* stats = reinterpret_cast<float*>(tile + 4 * kQtPart);
+  const float l2 = valid ? lse[t * kH + h] * kLog2e : INFINITY;
+  float share = 0.f;
+  if (p == 0) {
+    stats[r] = l2;
+    stats[kBM + r] = valid ? dr : 0.f;
+    const float sk2 = sink[h] * kLog2e;
+    share = valid ? __builtin_amdgcn_exp2f(sk2 - l2) * dr : 0.f;
+  }
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) share += __shfl_xor(share, off);
+  if ((tid & 63) == 0) red[tid >> 6] = share;
+  __syncthreads();
+  if (tid == 0) ws.sinkpart[(size_t)h * ws.nqmax + qg] = (red[0] + red[1]) + (red[2] + red[3]);
+  {
+    uint4* qtt = reinterpret_cast<uint4*>(tile + 2 * kQtPart);
+    uint4* dtt = reinterpret_cast<uint4*>(tile + 3 * kQtPart);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int qv = tid + 256 * i;
+      const int d = qv >> 2, c = qv & 3;
+      const int fi = frag_index(d >> 5, 2, c >> 1, c & 1, d & 31);
+      qtt[fi] = *reinterpret_cast<const uint4*>(&qts[d * kBM + c * 8]);
+      dtt[fi] = *reinterpret_cast<const uint4*>(&dts[d * kBM + c * 8]);
+    }
+  }
+}
+
+// ----------------------------------------------------------------- dQ
+
+// P and dS of one 32-key block b of a 64-key tile, transposed (S^T rows are
+// keys): lane (col, half) holds query col and keys k0 + 32b + 8(i>>2) + 4half
+// + (i&3). Returns dS^T packed as the two bf16 B-operand fragments.
+__device__ __forceinline__ void dq_block_grad(const f32x16& s, const f32x16& dp, float l2, float dr,
+                                              bool mask, int k0b, int qrow, int u, int window,
+                                              int half, bf16x8* out) {
+  float g[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float pv = __builtin_amdgcn_exp2f(s[i] - l2);
+    if (mask) {
+      const int key = k0b + 8 * (i >> 2) + 4 * half + (i & 3);
+      const bool ok = key <= qrow && key < u && qrow < u &&
+                      (window == 0 || qrow - key <= window - 1);
+      pv = ok ? pv : 0.f;
+    }
+    g[i] = pv * (dp[i] - dr);
+  }
+  out[0] = pack_frag(g);
+  out[1] = pack_frag(g + 8);
+}
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const uint16_t* __restrict__ q,
+                                                             const float* __restrict__ q_norm_w,
+                                                             const int* __restrict__ positions,
+                                                             int window, int use_rope, float eps,
+                                                             BwdWs ws, uint16_t* __restrict__ dq) {
+  __shared__ uint4 smem[kBwdStages][kKvbBytes / 16];
+  const int bid = blockIdx.x;
+  const int i_item = bid >> 3, g = (bid >> 1) & (kG - 1), hh = bid & 1;
+  if (i_item >= ws.f.hdr[2]) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int h = g * kHpg + hh * 4 + wave;
+  const int2 itm = ws.f.items[i_item];
+  const int4 meta = ws.f.seq[itm.x];
+  const int start = __builtin_amdgcn_readfirstlane(meta.x);
+  const int u = __builtin_amdgcn_readfirstlane(meta.z);
+  const int t0 = itm.y * kBM;
+  int klo, khi;
+  block_keys(u, itm.y, window, &klo, &khi);
+  const int tile_lo = klo / kBN;
+  const int ntiles = (khi + kBN - 1) / kBN - tile_lo;
+  const int qg = ws.f.qbase[itm.x] + itm.y;
+  const int voff = lane * 16 + wave * 1024;
+
+  // Q' and dO of this head as B operands (query col, channels 16kk + 8half..),
+  // and the row terms of query col.
+  const char* qtile = ws.qt + ((size_t)qg * kH + h) * kQtBytes;
+  const uint4* qfp = reinterpret_cast<const uint4*>(qtile);
+  const uint4* dfp = reinterpret_cast<const uint4*>(qtile + kQtPart);
+  bf16x8 qf[8], df[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    qf[kk] = ld_frag(qfp + kk * 64 + lane);
+    df[kk] = ld_frag(dfp + kk * 64 + lane);
+  }
+  const float* stats = reinterpret_cast<const float*>(qtile + 4 * kQtPart);
+  const float l2 = stats[col];
+  const float dr = stats[kBM + col];
+
+  const char* tiles = ws.kvb + ((size_t)g * ws.f.ntmax + meta.w + tile_lo) * kKvbBytes;
+  const __amdgpu_buffer_rsrc_t trs = rsrc_of(tiles, ntiles * kKvbBytes);
+  auto load_tile = [&](int k, int stage) {
+#pragma unroll
+    for (int i = 0; i < kKvbVecPerWave; ++i)
+      dma16(trs, voff, k * kKvbBytes + i * 4096,
+            reinterpret_cast<char*>(smem[stage]) + i * 4096 + wave * 1024);
+  };
+  load_tile(0, 0);
+  if (ntiles > 1) load_tile(1, 1);
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  const int qrow = t0 + col;
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    if (kt + 1 < ntiles) ring_barrier_n<kKvbVecPerWave>();
+    else ring_barrier_n<0>();
+    if (kt + 2 < ntiles) load_tile(kt + 2, (kt + 2) % kBwdStages);
+    const uint4* st = smem[kt % kBwdStages];
+    const uint4* kp = st;                 // K' part
+    const uint4* vp = st + kKvbPart / 16;  // V part
+    const uint4* tp = st + 2 * kKvbPart / 16;  // K'^T part
+    const int k0 = (tile_lo + kt) * kBN;
+    const bool mask = (k0 + kBN - 1 > t0) || (k0 + kBN > u) ||
+                      (window > 0 && t0 + kBM - 1 - k0 > window - 1);
+    bf16x8 ds[4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        s = mfma(ld_frag(kp + frag_index(b, 8, kk, 0, 0) + lane), qf[kk], s);
+        dp = mfma(ld_frag(vp + frag_index(b, 8, kk, 0, 0) + lane), df[kk], dp);
+      }
+      dq_block_grad(s, dp, l2, dr, mask, k0 + 32 * b, qrow, u, window, half, ds + 2 * b);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc[db] = mfma(ld_frag(tp + frag_index(db, 4, kk, 0, 0) + lane), ds[kk], acc[db]);
+  }
+
+  // Epilogue. Lane (col, half) holds dQ'^T for query t0 + col, channels
+  // c = 32db + 8rg + 4half + j at acc[db][4rg + j]; c and c + 64 are db and
+  // db + 2 at the same index.
+  const int rows = min(u - t0, kBM);
+  const bool valid = col < rows;
+  float xq[4][16];
+  const __amdgpu_buffer_rsrc_t qr = rsrc_of(q + ((size_t)(start + t0) * kH + h) * kD, rows * (kH * kD * 2));
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const uint2 w = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(qr, col * (kH * kD * 2) + (32 * db + 8 * rg + 4 * half) * 2, 0, 0));
+      xq[db][4 * rg + 0] = bf16_lo(w.x);
+      xq[db][4 * rg + 1] = bf16_hi(w.x);
+      xq[db][4 * rg + 2] = bf16_lo(w.y);
+      xq[db][4 * rg + 3] = bf16_hi(w.y);
+    }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] *= kInvSqrtD;
+  if (use_rope) {  // adjoint of the rotation: the opposite turn
+    const int pos = positions ? (valid ? positions[(size_t)start + t0 + col] : 0) : t0 + col;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float cs, sn;
+        rope_cos_sin(pos, ws.f.rope_r[32 * db + 8 * (i >> 2) + 4 * half + (i & 3)], &cs, &sn);
+        const float a = acc[db][i], b = acc[db + 2][i];
+        acc[db][i] = a * cs + b * sn;
+        acc[db + 2][i] = b * cs - a * sn;
+      }
+  }
+  // RMSNorm adjoint: dq = rstd (dy w - xn mean(xn dy w)), xn = q rstd
+  float ss = 0.f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss += xq[db][i] * xq[db][i];
+  ss += __shfl_xor(ss, 32);
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+  float dot = 0.f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      xq[db][i] *= rstd;
+      dot += xq[db][i] * acc[db][i] * q_norm_w[32 * db + 8 * (i >> 2) + 4 * half + (i & 3)];
+    }
+  dot += __shfl_xor(dot, 32);
+  dot *= 1.0f / kD;
+  const __amdgpu_buffer_rsrc_t dqr = rsrc_of(dq + ((size_t)(start + t0) * kH + h) * kD, rows * (kH * kD * 2));
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      float y[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * rg + j;
+        const float w = q_norm_w[32 * db + 8 * rg + 4 * half + j];
+        y[j] = rstd * (acc[db][i] * w - xq[db][i] * dot);
+      }
+      const uint2 pk = make_uint2(pack2(y[0], y[1]), pack2(y[2], y[3]));
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, pk),
+                                            dqr, col * (kH * kD * 2) + (32 * db + 8 * rg + 4 * half) * 2, 0, 0);
+    }
+  // q-norm-weight terms dy * xn, summed over the workgroup's 32 rows x 4 heads
+  __syncthreads();  // every wave is done with the tile ring
+  float* red = reinterpret_cast<float*>(&smem[0][0]);  // [4 waves][32 cols][128]
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      *reinterpret_cast<float4*>(red + (wave * kBM + col) * kD + 32 * db + 8 * rg + 4 * half) =
+          make_float4(acc[db][4 * rg] * xq[db][4 * rg], acc[db][4 * rg + 1] * xq[db][4 * rg + 1],
+                      acc[db][4 * rg + 2] * xq[db][4 * rg + 2], acc[db][4 * rg + 3] * xq[db][4 * rg + 3]);
+  __syncthreads();
+  {
+    const int c = tid & (kD - 1), part = tid >> 7;
+    float sum = 0.f;
+    for (int w = 0; w < 4; ++w)
+      for (int cc = 16 * part; cc < 16 * part + 16; ++cc) sum += red[(w * kBM + cc) * kD + c];
+    float* sum2 = red + 4 * kBM * kD;
+    sum2[part * kD + c] = sum;
+    __syncthreads();
+    if (part == 0) ws.wq[(size_t)c * (ws.nqmax * 2 * kG) + bid] = sum2[c] + sum2[kD + c];
+  }
+}
+
+// ----------------------------------------------------------------- dK, dV
+
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(int window, BwdWs ws) {
+  __shared__ uint4 smem[kBwdStages][kQtBytes / 16];
+  const int bid = blockIdx.x;
+  const int ii = bid >> 2, g = bid & (kG - 1);
+  if (ii >= ws.f.hdr[kHdrNC]) return;
+  const int CH = ws.f.hdr[kHdrCH];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int2 kit = ws.kitems[ii];
+  const int e = kit.x, chunk = kit.y;
+  const int2 te = ws.f.tiles[e];
+  const int4 meta = ws.f.seq[te.x];
+  const int u = __builtin_amdgcn_readfirstlane(meta.z);
+  const int len = meta.y;
+  const int k0 = te.y * kBN;
+  int qlo, qhi;
+  kb_queries(k0, u, window, &qlo, &qhi);
+  const int qb0 = qlo + chunk * CH;
+  const int qb1 = min(qhi, qb0 + CH);
+  const int nsteps = (qb1 - qb0) * kHpg;
+  const int qgbase = ws.f.qbase[te.x];
+  const int voff = lane * 16 + wave * 1024;
+
+  // This wave's 32 keys: tile e + (wave >> 1), block wave & 1. K' and V as
+  // B operands (key col, channels 16kk + 8half ..); a tile past the
+  // sequence's last reads as zeros and its keys are masked.
+  const int kt = wave >> 1, bb = wave & 1;
+  const int kbase = k0 + kt * kBN + bb * 32;
+  const bool tile_exists = te.y + kt < (len + kBN - 1) / kBN;
+  const char* ktile = ws.kvb + ((size_t)g * ws.f.ntmax + e + kt) * kKvbBytes;
+  const __amdgpu_buffer_rsrc_t krs = rsrc_of(ktile, tile_exists ? 2 * kKvbPart : 0);
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    kf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            krs, frag_index(bb, 8, kk, half, col) * 16, 0, 0));
+    vf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            krs, kKvbPart + frag_index(bb, 8, kk, half, col) * 16, 0, 0));
+  }
+
+  // step j: query block qb0 + j / 8, head 8g + j % 8
+  auto load_step = [&](int j, int stage) {
+    const int qg = qgbase + qb0 + j / kHpg;
+    const char* src = ws.qt + ((size_t)qg * kH + g * kHpg + j % kHpg) * kQtBytes;
+    const __amdgpu_buffer_rsrc_t r = rsrc_of(src, kQtBytes);
+    char* dst = reinterpret_cast<char*>(smem[stage]);
+#pragma unroll
+    for (int i = 0; i < kQtVecPerWave; ++i) dma16(r, voff, i * 4096, dst + i * 4096 + wave * 1024);
+    dma4(r, lane * 4, 4 * kQtPart, dst + 4 * kQtPart);
+  };
+  constexpr int kStepOps = kQtVecPerWave + 1;
+  load_step(0, 0);
+  if (nsteps > 1) load_step(1, 1);
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk[db][i] = 0.f;
+      dv[db][i] = 0.f;
+    }
+
+  for (int j = 0; j < nsteps; ++j) {
+    if (j + 1 < nsteps) ring_barrier_n<kStepOps>();
+    else ring_barrier_n<0>();
+    if (j + 2 < nsteps) load_step(j + 2, (j + 2) % kBwdStages);
+    const int t0 = (qb0 + j / kHpg) * kBM;
+    // nothing to do when every query of the step is before every key, past the
+    // window of every key, or the keys are padding
+    const bool none = t0 + kBM - 1 < kbase || kbase >= u ||
+                      (window > 0 && t0 - (kbase + 31) > window - 1);
+    if (none) continue;
+    const bool mask = !(kbase + 31 < u && t0 + kBM - 1 < u && t0 >= kbase + 31 &&
+                        (window == 0 || t0 + kBM - 1 - kbase <= window - 1));
+    const uint4* st = smem[j % kBwdStages];
+    const uint4* qfp = st;
+    const uint4* dfp = st + kQtPart / 16;
+    const uint4* qtp = st + 2 * kQtPart / 16;
+    const uint4* dtp = st + 3 * kQtPart / 16;
+    const float* stats = reinterpret_cast<const float*>(st + 4 * kQtPart / 16);
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      s = mfma(ld_frag(qfp + kk * 64 + lane), kf[kk], s);
+      dp = mfma(ld_frag(dfp + kk * 64 + lane), vf[kk], dp);
+    }
+    // S and dP: lane (col, half) holds key kbase + col and queries
+    // t0 + 8rg + 4half + jj at index 4rg + jj
+    float pr[16], gr[16];
+    const int key = kbase + col;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const float4 L = *reinterpret_cast<const float4*>(stats + 8 * rg + 4 * half);
+      const float4 R = *reinterpret_cast<const float4*>(stats + kBM + 8 * rg + 4 * half);
+      const float Lv[4] = {L.x, L.y, L.z, L.w}, Rv[4] = {R.x, R.y, R.z, R.w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int i = 4 * rg + jj;
+        float pv = __builtin_amdgcn_exp2f(s[i] - Lv[jj]);
+        if (mask) {
+          const int qrow = t0 + 8 * rg + 4 * half + jj;
+          const bool ok = key <= qrow && key < u && qrow < u &&
+                          (window == 0 || qrow - key <= window - 1);
+          pv = ok ? pv : 0.f;
+        }
+        pr[i] = pv;
+        gr[i] = pv * (dp[i] - Rv[jj]);
+      }
+    }
+    const bf16x8 pb[2] = {pack_frag(pr), pack_frag(pr + 8)};
+    const bf16x8 gb[2] = {pack_frag(gr), pack_frag(gr + 8)};
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        dv[db] = mfma(ld_frag(dtp + frag_index(db, 2, kk, 0, 0) + lane), pb[kk], dv[db]);
+        dk[db] = mfma(ld_frag(qtp + frag_index(db, 2, kk, 0, 0) + lane), gb[kk], dk[db]);
+      }
+  }
+
+  // FP32 partial sums of this chunk: [dK' | dV][128 keys][128 channels];
+  // lane (col, half) holds key col of the wave's block, channels
+  // 32db + 8rg + 4half + [0, 4) at index 4rg + [0, 4). Q' carries the
+  // softmax scale log2(e)/sqrt(d), so dK' = dS^T Q' ln 2.
+  float* part = ws.part + ((size_t)(ws.cb[e] + chunk) * kG + g) * kPartFloats;
+  const int krow = kt * kBN + bb * 32 + col;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int c = 32 * db + 8 * rg + 4 * half;
+      *reinterpret_cast<float4*>(part + krow * kD + c) =
+          make_float4(dk[db][4 * rg] * kLn2, dk[db][4 * rg + 1] * kLn2,
+                      dk[db][4 * rg + 2] * kLn2, dk[db][4 * rg + 3] * kLn2);
+      *reinterpret_cast<float4*>(part + kKB * kD + krow * kD + c) =
+          make_float4(dv[db][4 * rg], dv[db][4 * rg + 1], dv[db][4 * rg + 2], dv[db][4 * rg + 3]);
+    }
+}
+
+// ----------------------------------------------------------------- K/V reduce
+
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const uint16_t* __restrict__ k,
+                                                            const float* __restrict__ k_norm_w,
+                                                            const int* __restrict__ positions,
+                                                            float eps, int use_rope, BwdWs ws,
+                                                            uint16_t* __restrict__ dk,
+                                                            uint16_t* __restrict__ dv) {
+  __shared__ float red[kBN * kD + 2 * kD];
+  const int e = blockIdx.x, g = blockIdx.y;
+  if (e >= ws.f.hdr[1]) return;
+  const int2 te = ws.f.tiles[e];
+  const int4 meta = ws.f.seq[te.x];
+  const int start = meta.x, len = meta.y, u = meta.z;
+  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
+  const int ell = te.y * kBN + r;
+  const bool valid = ell < u;
+  const size_t t = (size_t)start + ell;
+  const int eb = e - (te.y & 1);
+  const int row = (te.y & 1) * kBN + r;
+  // channels [16p, 16p+16) and [64+16p, 64+16p+16)
+  float gk[32], gv[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) gk[i] = gv[i] = 0.f;
+  const int nch = valid ? ws.nc[eb] : 0;
+  const float* part = ws.part + ((size_t)ws.cb[eb] * kG + g) * kPartFloats;
+  for (int ch = 0; ch < nch; ++ch) {
+    const float* pk = part + (size_t)ch * kG * kPartFloats + row * kD;
+    const float* pv = pk + kKB * kD;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 a = *reinterpret_cast<const float4*>(pk + 64 * h2 + 16 * p + 4 * i);
+        const float4 b = *reinterpret_cast<const float4*>(pv + 64 * h2 + 16 * p + 4 * i);
+        float* x = gk + 16 * h2 + 4 * i;
+        float* y = gv + 16 * h2 + 4 * i;
+        x[0] += a.x; x[1] += a.y; x[2] += a.z; x[3] += a.w;
+        y[0] += b.x; y[1] += b.y; y[2] += b.z; y[3] += b.w;
+      }
+  }
+  float xk[32];
+  if (valid) {
+    const uint4* src = reinterpret_cast<const uint4*>(k + (t * kG + g) * kD);
+    unpack8(src[2 * p], xk);
+    unpack8(src[2 * p + 1], xk + 8);
+    unpack8(src[8 + 2 * p], xk + 16);
+    unpack8(src[9 + 2 * p], xk + 24);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xk[i] = 0.f;
+  }
+  if (use_rope && valid) {  // adjoint of the rotation
+    const int pos = positions ? positions[t] : ell;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float cs, sn;
+      rope_cos_sin(pos, ws.f.rope_r[16 * p + i], &cs, &sn);
+      const float a = gk[i], b = gk[16 + i];
+      gk[i] = a * cs + b * sn;
+      gk[16 + i] = b * cs - a * sn;
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) ss += xk[i] * xk[i];
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    xk[i] *= rstd;
+    dot += xk[i] * gk[i] * k_norm_w[(i < 16 ? 16 * p : 64 + 16 * p) + (i & 15)];
+  }
+  dot += __shfl_xor(dot, 1);
+  dot += __shfl_xor(dot, 2);
+  dot *= 1.0f / kD;
+  if (ell < len) {
+    float y[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float w = k_norm_w[(i < 16 ? 16 * p : 64 + 16 * p) + (i & 15)];
+      y[i] = rstd * (gk[i] * w - xk[i] * dot);
+    }
+    uint4* dkr = reinterpret_cast<uint4*>(dk + (t * kG + g) * kD);
+    uint4* dvr = reinterpret_cast<uint4*>(dv + (t * kG + g) * kD);
+    dkr[2 * p] = pack8(y);
+    dkr[2 * p + 1] = pack8(y + 8);
+    dkr[8 + 2 * p] = pack8(y + 16);
+    dkr[9 + 2 * p] = pack8(y + 24);
+    dvr[2 * p] = pack8(gv);
+    dvr[2 * p + 1] = pack8(gv + 8);
+    dvr[8 + 2 * p] = pack8(gv + 16);
+    dvr[9 + 2 * p] = pack8(gv + 24);
+  }
+  // k-norm-weight terms dy * xn of the tile's 64 keys, summed in key order
+#pragma unroll
+  for (int i = 0; i < 32; ++i) red[r * kD + (i < 16 ? 16 * p : 64 + 16 * p) + (i & 15)] = gk[i] * xk[i];
+  __syncthreads();
+  {
+    const int c = tid & (kD - 1), half2 = tid >> 7;
+    float sum = 0.f;
+    for (int rr = 32 * half2; rr < 32 * half2 + 32; ++rr) sum += red[rr * kD + c];
+    red[kBN * kD + half2 * kD + c] = sum;
+    __syncthreads();
+    if (half2 == 0)
+      ws.wk[(size_t)c * (ws.f.ntmax * kG) + (size_t)e * kG + g] = red[kBN * kD + c] + red[kBN * kD + kD + c];
+  }
+}
+
+// ----------------------------------------------------------------- finalize
+
+// Block sum of 256 values in a fixed order.
+__device__ float block_sum256(float v, float* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) sh[tid] += sh[tid + off];
+    __syncthreads();
+  }
+  return sh[0];
+}
+
+// With `empty` (no tokens) nothing was scheduled and the sums are zero.
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdWs ws, int empty,
+                                                           float* __restrict__ dq_norm_w,
+                                                           float* __restrict__ dk_norm_w,
+                                                           float* __restrict__ dsink) {
+  __shared__ float sh[256];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int NQ = empty ? 0 : ws.f.hdr[2], NT = empty ? 0 : ws.f.hdr[1];
+  float v = 0.f;
+  if (b < kD) {
+    const float* src = ws.wq + (size_t)b * (ws.nqmax * 2 * kG);
+    for (int j = tid; j < NQ * 2 * kG; j += 256) v += src[j];
+    v = block_sum256(v, sh);
+    if (tid == 0) dq_norm_w[b] = v;
+  } else if (b < 2 * kD) {
+    const float* src = ws.wk + (size_t)(b - kD) * (ws.f.ntmax * kG);
+    for (int j = tid; j < NT * kG; j += 256) v += src[j];
+    v = block_sum256(v, sh);
+    if (tid == 0) dk_norm_w[b - kD] = v;
+  } else {
+    const int h = b - 2 * kD;
+    const float* src = ws.sinkpart + (size_t)h * ws.nqmax;
+    for (int j = tid; j < NQ; j += 256) v += src[j];
+    v = block_sum256(v, sh);
+    if (tid == 0) dsink[h] = -v;
+  }
+}
+
+}  // namespace flint
+
+// ===================================================================== C ABI
+
+using namespace flint;
+
+extern "C" size_t flint_attn_bwd_workspace_bytes(int32_t total_tokens, int32_t n_seqs,
+                                                 int32_t max_seqlen, int32_t num_kv_heads,
+                                                 int32_t head_dim) {
+  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return 0;
+  if (num_kv_heads != kG || head_dim != kD) return 0;
+  return make_bwd_layout(total_tokens, n_seqs).total;
+}
+
+extern "C" int flint_attn_bwd(const void* q, const void* k, const void* v, const float* q_norm_w,
+                              const float* k_norm_w, const float* sink, const int32_t* positions,
+                              const int32_t* cu_seqlens, const int32_t* seqused, int32_t n_seqs,
+                              int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                              int32_t use_rope, float rope_theta, float eps, const void* out,
+                              const float* lse, const void* dout, void* workspace,
+                              size_t workspace_bytes, void* dq, void* dk, void* dv,
+                              float* dq_norm_w, float* dk_norm_w, float* dsink, void* stream) {
+  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return FLINT_ERR_SHAPE;
+  if (num_q_heads != kH || num_kv_heads != kG || head_dim != kD) return FLINT_ERR_UNSUPPORTED;
+  if (window < 0 || !(eps > 0.f) || !isfinite(eps)) return FLINT_ERR_VALUE;
+  if (use_rope && (!(rope_theta > 0.f) || !isfinite(rope_theta))) return FLINT_ERR_VALUE;
+  if (!dq_norm_w || !dk_norm_w || !dsink) return FLINT_ERR_NULL;
+  if (total_tokens > 0 && n_seqs < 1) return FLINT_ERR_SHAPE;
+  if (total_tokens > 0 && (!q || !k || !v || !q_norm_w || !k_norm_w || !sink || !cu_seqlens ||
+                           !out || !lse || !dout || !dq || !dk || !dv))
+    return FLINT_ERR_NULL;
+  if (!workspace) return FLINT_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 16) || !aligned(workspace, 256) || !aligned(q_norm_w, 4) ||
+      !aligned(k_norm_w, 4) || !aligned(sink, 4) || !aligned(cu_seqlens, 4) ||
+      !aligned(dq_norm_w, 4) || !aligned(dk_norm_w, 4) || !aligned(dsink, 4) ||
+      (positions && !aligned(positions, 4)) || (seqused && !aligned(seqused, 4)))
+    return FLINT_ERR_ALIGN;
+  const BwdLayout L = make_bwd_layout(total_tokens, n_seqs);
+  if (workspace_bytes < L.total) return FLINT_ERR_WORKSPACE;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  BwdWs ws;
+  ws.f = ws_at(workspace, L.f);
+  char* base = static_cast<char*>(workspace);
+  ws.kvb = base + L.kvb;
+  ws.qt = base + L.qt;
+  ws.sinkpart = reinterpret_cast<float*>(base + L.sinkpart);
+  ws.wq = reinterpret_cast<float*>(base + L.wq);
+  ws.wk = reinterpret_cast<float*>(base + L.wk);
+  ws.cb = reinterpret_cast<int*>(base + L.cb);
+  ws.nc = reinterpret_cast<int*>(base + L.nc);
+  ws.kitems = reinterpret_cast<int2*>(base + L.kitems);
+  ws.part = reinterpret_cast<float*>(base + L.part);
+  ws.nqmax = (int)L.f.nqmax;
+  ws.ncmax = (int)L.ncmax;
+  ws.n = n_seqs;
+
+  const uint16_t* qh = static_cast<const uint16_t*>(q);
+  const uint16_t* kh = static_cast<const uint16_t*>(k);
+  const uint16_t* vh = static_cast<const uint16_t*>(v);
+  const int rope = use_rope ? 1 : 0;
+  const int* pos = rope ? positions : nullptr;
+
+  (void)hipGetLastError();
+  if (total_tokens == 0) {
+    // no rows: the parameter gradients are zero
+    bwd_finalize_kernel<<<2 * kD + kH, 256, 0, st>>>(ws, 1, dq_norm_w, dk_norm_w, dsink);
+  } else {
+    launch_schedule(cu_seqlens, seqused, n_seqs, total_tokens, max_seqlen, window,
+                    (double)rope_theta, ws.f, st);
+    bwd_schedule_kernel<<<1, 1024, 0, st>>>(window, ws);
+    bwd_kv_prep_kernel<<<dim3((unsigned)L.f.ntmax, kG), 256, 0, st>>>(
+        kh, vh, k_norm_w, pos, eps, rope, ws, static_cast<uint16_t*>(dq));
+    bwd_q_prep_kernel<<<dim3((unsigned)L.f.nqmax, kH), 256, 0, st>>>(
+        qh, static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, q_norm_w,
+        sink, pos, eps, rope, ws);
+    bwd_dq_kernel<<<(unsigned)(L.f.nqmax * 2 * kG), kBwdThreads, 0, st>>>(
+        qh, q_norm_w, pos, window, rope, eps, ws, static_cast<uint16_t*>(dq));
+    bwd_dkdv_kernel<<<(unsigned)(L.ncmax * kG), kBwdThreads, 0, st>>>(window, ws);
+    bwd_kv_reduce_kernel<<<dim3((unsigned)L.f.ntmax, kG), 256, 0, st>>>(
+        kh, k_norm_w, pos, eps, rope, ws, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
+    bwd_finalize_kernel<<<2 * kD + kH, 256, 0, st>>>(ws, 0, dq_norm_w, dk_norm_w, dsink);
+  }
+  if (hipGetLastError() != hipSuccess) return FLINT_ERR_HIP;
+  if (debug_sync()) {
+    int32_t flags = 0;
+    return flint_attn_device_status(workspace, stream, &flags);
+  }
+  return FLINT_OK;
+}

@@ -1,6 +1,7 @@
 /*
- * flint_attn.h - C ABI of the Flint sink-aware attention forward (prefill)
- * on AMD Instinct MI355X (gfx950).
+ * flint_attn.h - C ABI of the Flint sink-aware attention on AMD Instinct
+ * MI355X (gfx950): the prefill forward, its backward, and decode with a KV
+ * cache.
  *
  * What one call computes, for every valid token t of sequence s, query head
  * h (0..31) and its key/value head g = h / 8 (grouped-query attention,
@@ -237,6 +238,66 @@ int flint_attn_decode(const void* q, const void* k, const void* v, const float* 
                       int32_t head_dim, int32_t window, int32_t use_rope, float rope_theta,
                       float eps, void* workspace, size_t workspace_bytes, void* out,
                       void* stream);
+
+/* ------------------------------------------------------------------------
+ * Training: forward with the row normalizer, and the backward.
+ *
+ * The backward is what the pages' training recipes need (Hugging Face
+ * discussion #26 on RecursiveSI/flint, "Where other stacks fail": sinks in
+ * backward and the sink gradient). With z the scaled logits, W the sink
+ * softmax weights and p_sink the sink's weight of a row, for an upstream
+ * gradient dO of out:
+ *   Dr[t,h]   = dO[t,h,:] . out[t,h,:]
+ *   dZ        = W * (dO V^T - Dr)            (per row, over its allowed keys)
+ *   dv[t',g]  = sum over t and the 8 heads h of g of W[t,h,t'] dO[t,h,:]
+ *   dq'[t,h]  = sum_t' dZ[t,h,t'] khat(t') / sqrt(128)
+ *   dk'[t',g] = sum over t, h of g of dZ[t,h,t'] qhat(t) / sqrt(128)
+ *   dsink[h]  = - sum_t p_sink[t,h] Dr[t,h]  (the sink has value 0)
+ * then the adjoint of the rotation (the opposite turn) and of the weight-form
+ * RMSNorm: for y = x r w with r = 1/sqrt(mean(x^2) + eps),
+ *   dx = r (dy w - x r mean(x r dy w)),  dw += dy x r over tokens and heads.
+ * The softmax weights are recomputed from the forward's lse (W = exp(z - lse)).
+ * ------------------------------------------------------------------------ */
+
+/* flint_attn_fwd that also writes lse [total_tokens][32] float32 (16-byte
+ * aligned): the natural-log normalizer of each row,
+ * log(exp(sink[h]) + sum_t' exp(z(t'))), -INF on padded rows. Same errors as
+ * flint_attn_fwd; lse NULL with total_tokens > 0 is FLINT_ERR_NULL. */
+int flint_attn_fwd_lse(const void* q, const void* k, const void* v, const float* q_norm_w,
+                       const float* k_norm_w, const float* sink, const int32_t* positions,
+                       const int32_t* cu_seqlens, const int32_t* seqused, int32_t n_seqs,
+                       int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                       int32_t use_rope, float rope_theta, float eps, void* workspace,
+                       size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/* Workspace size in bytes for flint_attn_bwd (0 for invalid sizes or an
+ * unsupported head layout). It holds the normalized operands, per-chunk FP32
+ * partial sums of dk and dv, and the per-block terms of the parameter
+ * gradients. */
+size_t flint_attn_bwd_workspace_bytes(int32_t total_tokens, int32_t n_seqs, int32_t max_seqlen,
+                                      int32_t num_kv_heads, int32_t head_dim);
+
+/* Gradients of the layer. Inputs are the forward's arguments (same layout,
+ * flags and sequence description) plus out and lse of flint_attn_fwd_lse on
+ * those inputs and dout = dL/dout [total_tokens][32][128] bf16. Outputs
+ * (caller-owned, written, not accumulated): dq [T][32][128], dk [T][4][128],
+ * dv [T][4][128] bf16, zero on padded tokens; dq_norm_w, dk_norm_w [128] and
+ * dsink [32] float32, sums over every valid token and head formed in a fixed
+ * order, so repeated calls give identical bits. All device pointers; tensors
+ * 16-byte aligned, float arrays 4-byte aligned. Errors as for flint_attn_fwd
+ * (FLINT_ERR_NULL also for a missing out, lse, dout or output). Device-data
+ * errors (cu_seqlens, seqused) leave dq, dk and dv unwritten, set the three
+ * parameter gradients to zero and are read with flint_attn_device_status.
+ * Asynchronous on `stream`. */
+int flint_attn_bwd(const void* q, const void* k, const void* v, const float* q_norm_w,
+                   const float* k_norm_w, const float* sink, const int32_t* positions,
+                   const int32_t* cu_seqlens, const int32_t* seqused, int32_t n_seqs,
+                   int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t window, int32_t use_rope,
+                   float rope_theta, float eps, const void* out, const float* lse,
+                   const void* dout, void* workspace, size_t workspace_bytes, void* dq, void* dk,
+                   void* dv, float* dq_norm_w, float* dk_norm_w, float* dsink, void* stream);
 
 #ifdef __cplusplus
 }
