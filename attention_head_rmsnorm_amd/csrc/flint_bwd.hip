@@ -27,7 +27,7 @@
 //                         (query-slot order), the row
 //                         terms lse (log2 units) and Dr, the block's share of
 //                         the sink adjoint.
-//   bwd_dq_kernel         query-major: per (query block, 4 heads of a kv head),
+//   bwd_dq_kernel         query-major: per (query block, the 8 heads of a kv head),
 //                         over the key tiles in the window: S^T = K'Q'^T,
 //                         dP^T = V dO^T, dS^T, dQ'^T += K'^T dS^T; then RoPE and
 //                         RMSNorm adjoints, dq, and the block's q-norm-weight
@@ -52,7 +52,6 @@ namespace flint {
 constexpr int kBwdThreads = 256;             // four waves
 constexpr int kKvbPart = kBN * kD * 2;       // 16 KiB: one 64-key operand part
 constexpr int kKvbBytes = 3 * kKvbPart;      // K' | V | K'^T (key-slot order)
-constexpr int kKvbVecPerWave = kKvbBytes / (16 * kBwdThreads);  // 12
 constexpr int kQtPart = kBM * kD * 2;        // 8 KiB: one 32-query operand part
 constexpr int kQtStats = 2 * kBM * 4;        // lse (log2 units) [32], Dr [32]
 constexpr int kQtBytes = 4 * kQtPart + kQtStats;  // Q' | dO | Q'^T | dO^T | stats
@@ -71,7 +70,7 @@ struct BwdWs {
   char* kvb;       // [kG][ntmax][kKvbBytes]
   char* qt;        // [nqmax][kH][kQtBytes]
   float* sinkpart; // [kH][nqmax]: sum over the block's rows of p_sink * Dr
-  float* wq;       // [kD][nqmax * 2 * kG]: q-norm-weight terms per dQ workgroup
+  float* wq;       // [kD][nqmax * kG]: q-norm-weight terms per dQ workgroup
   float* wk;       // [kD][ntmax * kG]: k-norm-weight terms per (tile, kv head)
   int* cb;         // [ntmax] first chunk slot of the key block starting at tile e
   int* nc;         // [ntmax] its chunks
@@ -94,7 +93,7 @@ static BwdLayout make_bwd_layout(int64_t T, int64_t n) {
   L.kvb = o;      o = align_up(o + (size_t)kG * L.f.ntmax * kKvbBytes, 256);
   L.qt = o;       o = align_up(o + (size_t)L.f.nqmax * kH * kQtBytes, 256);
   L.sinkpart = o; o = align_up(o + (size_t)kH * L.f.nqmax * 4, 256);
-  L.wq = o;       o = align_up(o + (size_t)kD * L.f.nqmax * 2 * kG * 4, 256);
+  L.wq = o;       o = align_up(o + (size_t)kD * L.f.nqmax * kG * 4, 256);
   L.wk = o;       o = align_up(o + (size_t)kD * L.f.ntmax * kG * 4, 256);
   L.cb = o;       o = align_up(o + (size_t)L.f.ntmax * 4, 256);
   L.nc = o;       o = align_up(o + (size_t)L.f.ntmax * 4, 256);
@@ -441,41 +440,90 @@ __global__ __launch_bounds__(256) void bwd_q_prep_kernel(const uint16_t* __restr
 
 // ----------------------------------------------------------------- dQ
 
-// P and dS of one 32-key block b of a 64-key tile, transposed (S^T rows are
-// keys): lane (col, half) holds query col and keys k0 + 32b + 8(i>>2) + 4half
-// + (i&3). Returns dS^T packed as the two bf16 B-operand fragments.
-__device__ __forceinline__ void dq_block_grad(const f32x16& s, const f32x16& dp, float l2, float dr,
-                                              bool mask, int k0b, int qrow, int u, int window,
-                                              int half, bf16x8* out) {
-  float g[16];
+constexpr int kDqAhead = 4;  // operand fragments read ahead of their product
+
+constexpr int kDqThreads = 64 * kHpg;   // one wave per query head of a kv head
+constexpr int kDqVecPerWave = kKvbBytes / (16 * kDqThreads);  // 6
+
+// One 64-key tile of the query-major kernel for the wave's head, as one
+// straight block, a 32-key block b at a time: S^T = K'Q'^T and dP^T = V dO^T
+// (A operands from LDS, read kDqAhead products ahead; lane (col, half) gets
+// query col and keys k0 + 32b + 8(i>>2) + 4half + (i&3)), then
+// dS^T = P^T (dP^T - Dr) with P^T = exp2(S^T - lse), then the block's share
+// of dQ'^T += K'^T dS^T (key steps 2b, 2b + 1). The lane's query sees keys
+// klo .. klo + krange (causal, window and length limits), applied on every
+// tile. One block at a time keeps the wave within 256 registers, so two waves
+// share each SIMD.
+__device__ __forceinline__ void dq_tile(const uint4* st, int lane, int half, const bf16x8* qf,
+                                       const bf16x8* df, float l2, float dr, int klo,
+                                       unsigned krange, int k0, f32x16* acc) {
+  const int d0 = k0 + 4 * half - klo;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float pv = __builtin_amdgcn_exp2f(s[i] - l2);
-    if (mask) {
-      const int key = k0b + 8 * (i >> 2) + 4 * half + (i & 3);
-      const bool ok = key <= qrow && key < u && qrow < u &&
-                      (window == 0 || qrow - key <= window - 1);
-      pv = ok ? pv : 0.f;
+  for (int b = 0; b < 2; ++b) {
+    f32x16 sc = {}, dp = {};
+    {
+      // fragment i: channel step i >> 1, K' (even) or V (odd)
+      auto frag = [&](int i) {
+        return ld_frag(st + (i & 1) * (kKvbPart / 16) + frag_index(b, 8, i >> 1, 0, 0) + lane);
+      };
+      bf16x8 f[16];
+#pragma unroll
+      for (int i = 0; i < kDqAhead; ++i) f[i] = frag(i);
+      __builtin_amdgcn_sched_group_barrier(0x100, kDqAhead, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + kDqAhead < 16) f[i + kDqAhead] = frag(i + kDqAhead);
+        if (i & 1) dp = mfma(f[i], df[i >> 1], dp);
+        else sc = mfma(f[i], qf[i >> 1], sc);
+        if (i + kDqAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
     }
-    g[i] = pv * (dp[i] - dr);
+    bf16x8 ds[2];
+    {
+      float g[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = __builtin_amdgcn_exp2f(sc[i] - l2);
+        pv = (unsigned)(d0 + 32 * b + 8 * (i >> 2) + (i & 3)) <= krange ? pv : 0.f;
+        g[i] = pv * (dp[i] - dr);
+      }
+      ds[0] = pack_frag(g);
+      ds[1] = pack_frag(g + 8);
+    }
+    {
+      // fragment i: K'^T channel block i >> 1, key step 2b + (i & 1)
+      auto frag = [&](int i) {
+        return ld_frag(st + 2 * (kKvbPart / 16) + frag_index(i >> 1, 4, 2 * b + (i & 1), 0, 0) + lane);
+      };
+      bf16x8 f[8];
+#pragma unroll
+      for (int i = 0; i < kDqAhead; ++i) f[i] = frag(i);
+      __builtin_amdgcn_sched_group_barrier(0x100, kDqAhead, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i + kDqAhead < 8) f[i + kDqAhead] = frag(i + kDqAhead);
+        acc[i >> 1] = mfma(f[i], ds[i & 1], acc[i >> 1]);
+        if (i + kDqAhead < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
   }
-  out[0] = pack_frag(g);
-  out[1] = pack_frag(g + 8);
 }
 
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const uint16_t* __restrict__ q,
-                                                             const float* __restrict__ q_norm_w,
-                                                             const int* __restrict__ positions,
-                                                             int window, int use_rope, float eps,
-                                                             BwdWs ws, uint16_t* __restrict__ dq) {
+__global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __restrict__ q,
+                                                            const float* __restrict__ q_norm_w,
+                                                            const int* __restrict__ positions,
+                                                            int window, int use_rope, float eps,
+                                                            BwdWs ws, uint16_t* __restrict__ dq) {
   __shared__ uint4 smem[kBwdStages][kKvbBytes / 16];
   const int bid = blockIdx.x;
-  const int i_item = bid >> 3, g = (bid >> 1) & (kG - 1), hh = bid & 1;
+  const int i_item = bid >> 2, g = bid & (kG - 1);
   if (i_item >= ws.f.hdr[2]) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int h = g * kHpg + hh * 4 + wave;
+  const int h = g * kHpg + wave;
   const int2 itm = ws.f.items[i_item];
   const int4 meta = ws.f.seq[itm.x];
   const int start = __builtin_amdgcn_readfirstlane(meta.x);
@@ -507,9 +555,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const uint16_t* __r
   const __amdgpu_buffer_rsrc_t trs = rsrc_of(tiles, ntiles * kKvbBytes);
   auto load_tile = [&](int k, int stage) {
 #pragma unroll
-    for (int i = 0; i < kKvbVecPerWave; ++i)
-      dma16(trs, voff, k * kKvbBytes + i * 4096,
-            reinterpret_cast<char*>(smem[stage]) + i * 4096 + wave * 1024);
+    for (int i = 0; i < kDqVecPerWave; ++i)
+      dma16(trs, voff, k * kKvbBytes + i * 8192,
+            reinterpret_cast<char*>(smem[stage]) + i * 8192 + wave * 1024);
   };
   load_tile(0, 0);
   if (ntiles > 1) load_tile(1, 1);
@@ -519,35 +567,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const uint16_t* __r
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  // keys this lane's query sees: max(0, q - window + 1) .. min(q, u - 1);
+  // none for a padded row (an empty range: krange wraps past 2^31)
   const int qrow = t0 + col;
+  const int kfirst = window > 0 ? max(0, qrow - (window - 1)) : 0;
+  const unsigned krange = qrow < u ? (unsigned)(qrow - kfirst) : 0xffffffffu;
 
   for (int kt = 0; kt < ntiles; ++kt) {
-    if (kt + 1 < ntiles) ring_barrier_n<kKvbVecPerWave>();
+    if (kt + 1 < ntiles) ring_barrier_n<kDqVecPerWave>();
     else ring_barrier_n<0>();
     if (kt + 2 < ntiles) load_tile(kt + 2, (kt + 2) % kBwdStages);
-    const uint4* st = smem[kt % kBwdStages];
-    const uint4* kp = st;                 // K' part
-    const uint4* vp = st + kKvbPart / 16;  // V part
-    const uint4* tp = st + 2 * kKvbPart / 16;  // K'^T part
-    const int k0 = (tile_lo + kt) * kBN;
-    const bool mask = (k0 + kBN - 1 > t0) || (k0 + kBN > u) ||
-                      (window > 0 && t0 + kBM - 1 - k0 > window - 1);
-    bf16x8 ds[4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        s = mfma(ld_frag(kp + frag_index(b, 8, kk, 0, 0) + lane), qf[kk], s);
-        dp = mfma(ld_frag(vp + frag_index(b, 8, kk, 0, 0) + lane), df[kk], dp);
-      }
-      dq_block_grad(s, dp, l2, dr, mask, k0 + 32 * b, qrow, u, window, half, ds + 2 * b);
-    }
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        acc[db] = mfma(ld_frag(tp + frag_index(db, 4, kk, 0, 0) + lane), ds[kk], acc[db]);
+    dq_tile(smem[kt % kBwdStages], lane, half, qf, df, l2, dr, kfirst, krange,
+            (tile_lo + kt) * kBN, acc);
   }
 
   // Epilogue. Lane (col, half) holds dQ'^T for query t0 + col, channels
@@ -619,9 +650,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const uint16_t* __r
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, pk),
                                             dqr, col * (kH * kD * 2) + (32 * db + 8 * rg + 4 * half) * 2, 0, 0);
     }
-  // q-norm-weight terms dy * xn, summed over the workgroup's 32 rows x 4 heads
+  // q-norm-weight terms dy * xn, summed over the workgroup's 32 rows x 8 heads
   __syncthreads();  // every wave is done with the tile ring
-  float* red = reinterpret_cast<float*>(&smem[0][0]);  // [4 waves][32 cols][128]
+  float* red = reinterpret_cast<float*>(&smem[0][0]);  // [8 waves][32 cols][128]
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -631,21 +662,126 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const uint16_t* __r
                       acc[db][4 * rg + 2] * xq[db][4 * rg + 2], acc[db][4 * rg + 3] * xq[db][4 * rg + 3]);
   __syncthreads();
   {
-    const int c = tid & (kD - 1), part = tid >> 7;
+    const int c = tid & (kD - 1), part = tid >> 7;  // 4 parts of 8 columns
     float sum = 0.f;
-    for (int w = 0; w < 4; ++w)
-      for (int cc = 16 * part; cc < 16 * part + 16; ++cc) sum += red[(w * kBM + cc) * kD + c];
-    float* sum2 = red + 4 * kBM * kD;
-    sum2[part * kD + c] = sum;
+    for (int w = 0; w < kHpg; ++w)
+      for (int cc = 8 * part; cc < 8 * part + 8; ++cc) sum += red[(w * kBM + cc) * kD + c];
+    float* sum4 = red + kHpg * kBM * kD;
+    sum4[part * kD + c] = sum;
     __syncthreads();
-    if (part == 0) ws.wq[(size_t)c * (ws.nqmax * 2 * kG) + bid] = sum2[c] + sum2[kD + c];
+    if (part == 0)
+      ws.wq[(size_t)c * (ws.nqmax * kG) + bid] = (sum4[c] + sum4[kD + c]) + (sum4[2 * kD + c] + sum4[3 * kD + c]);
   }
 }
 
 // ----------------------------------------------------------------- dK, dV
 
+// Row terms of a step for the lanes of `half`: lse (log2 units) and Dr of
+// queries 8rg + 4half + [0, 4), rg = 0..3, as lv / rv[4rg + j]. The step's
+// terms arrive in LDS by a direct global->LDS load, which the compiler's wait
+// insertion cannot tell from the loads still in flight for later steps (it
+// would wait for all of them), so the read is written out with its own wait.
+__device__ __forceinline__ void read_stats(const float* stats, int half, float* lv, float* rv) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  f32x4_t a0, a1, a2, a3, b0, b1, b2, b3;
+  const unsigned base =
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) float*)stats + 16u * half;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:32\n\t"
+      "ds_read_b128 %2, %8 offset:64\n\t"
+      "ds_read_b128 %3, %8 offset:96\n\t"
+      "ds_read_b128 %4, %8 offset:128\n\t"
+      "ds_read_b128 %5, %8 offset:160\n\t"
+      "ds_read_b128 %6, %8 offset:192\n\t"
+      "ds_read_b128 %7, %8 offset:224\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      // early clobber: a read's destination must not be the address register
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+      : "v"(base)
+      : "memory");
+  const f32x4_t a[4] = {a0, a1, a2, a3}, b[4] = {b0, b1, b2, b3};
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lv[4 * rg + j] = a[rg][j];
+      rv[4 * rg + j] = b[rg][j];
+    }
+}
+
+constexpr int kDkdvStages = 3;  // the step in use and two loads ahead
+constexpr int kDkdvAhead = 4;   // operand fragments read ahead of their product
+
+// One step of the key-major kernel for the wave's 32 keys, as one straight
+// block: S = Q'K'^T and dP = dO V^T (A operands from LDS, read kDkdvAhead
+// products ahead), P = exp2(S - lse) and dS = P (dP - Dr), then
+// dV^T += dO^T P and dK'^T += Q'^T dS. The lane's key is seen by queries
+// qlo .. qlo + qrange (causal, window and length limits); the mask is applied
+// on every step, so the loop body has no branch.
+__device__ __forceinline__ void dkdv_step(const uint4* st, int lane, int half, const bf16x8* kf,
+                                          const bf16x8* vf, f32x16* dk, f32x16* dv, int qlo,
+                                          unsigned qrange, int t0) {
+  f32x16 s = {}, dp = {};
+  {
+    // fragment i: Q' (even) or dO (odd) at channel step i >> 1
+    auto frag = [&](int i) { return ld_frag(st + (i & 1) * (kQtPart / 16) + (i >> 1) * 64 + lane); };
+    bf16x8 f[16];
+#pragma unroll
+    for (int i = 0; i < kDkdvAhead; ++i) f[i] = frag(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, kDkdvAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + kDkdvAhead < 16) f[i + kDkdvAhead] = frag(i + kDkdvAhead);
+      if (i & 1) dp = mfma(f[i], vf[i >> 1], dp);
+      else s = mfma(f[i], kf[i >> 1], s);
+      if (i + kDkdvAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  }
+  bf16x8 pb[2], gb[2];
+  {
+    float lv[16], rv[16];
+    read_stats(reinterpret_cast<const float*>(st + 4 * kQtPart / 16), half, lv, rv);
+    float pr[16], gr[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pr[e] = __builtin_amdgcn_exp2f(s[e] - lv[e]);
+    // S rows are queries t0 + 8(e>>2) + 4half + (e&3); this lane's key
+    // allows rows qlo .. qlo + qrange
+    const int d0 = t0 + 4 * half - qlo;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      pr[e] = (unsigned)(d0 + 8 * (e >> 2) + (e & 3)) <= qrange ? pr[e] : 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) gr[e] = pr[e] * (dp[e] - rv[e]);
+    pb[0] = pack_frag(pr);
+    pb[1] = pack_frag(pr + 8);
+    gb[0] = pack_frag(gr);
+    gb[1] = pack_frag(gr + 8);
+  }
+  {
+    // fragment i: dO^T (even) or Q'^T (odd) of channel block i >> 2, query step (i >> 1) & 1
+    auto frag = [&](int i) {
+      return ld_frag(st + ((i & 1) ? 2 : 3) * (kQtPart / 16) + frag_index(i >> 2, 2, (i >> 1) & 1, 0, 0) + lane);
+    };
+    bf16x8 f[16];
+#pragma unroll
+    for (int i = 0; i < kDkdvAhead; ++i) f[i] = frag(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, kDkdvAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + kDkdvAhead < 16) f[i + kDkdvAhead] = frag(i + kDkdvAhead);
+      const int db = i >> 2, kk = (i >> 1) & 1;
+      if (i & 1) dk[db] = mfma(f[i], gb[kk], dk[db]);
+      else dv[db] = mfma(f[i], pb[kk], dv[db]);
+      if (i + kDkdvAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(int window, BwdWs ws) {
-  __shared__ uint4 smem[kBwdStages][kQtBytes / 16];
+  __shared__ uint4 smem[kDkdvStages][kQtBytes / 16];
   const int bid = blockIdx.x;
   const int ii = bid >> 2, g = bid & (kG - 1);
   if (ii >= ws.f.hdr[kHdrNC]) return;
@@ -707,63 +843,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(int window, BwdWs
       dk[db][i] = 0.f;
       dv[db][i] = 0.f;
     }
-
+  // queries that see this lane's key: key .. min(key + window - 1, u - 1);
+  // none for a padding key (an empty range: qrange wraps past 2^31)
+  const int key = kbase + col;
+  const int qlast = window > 0 ? min(key + window - 1, u - 1) : u - 1;
+  const unsigned qrange = key < u ? (unsigned)(qlast - key) : 0xffffffffu;
+  const int qfirst = key < u ? key : 0x40000000;
+  // every step of the wave's keys is computed; one whose queries see none of
+  // them (before the keys, past their window) has an all-zero P
   for (int j = 0; j < nsteps; ++j) {
+    // step j's operands are in LDS once at most the next step's loads remain
     if (j + 1 < nsteps) ring_barrier_n<kStepOps>();
     else ring_barrier_n<0>();
-    if (j + 2 < nsteps) load_step(j + 2, (j + 2) % kBwdStages);
+    if (j + 2 < nsteps) load_step(j + 2, (j + 2) % kDkdvStages);
     const int t0 = (qb0 + j / kHpg) * kBM;
-    // nothing to do when every query of the step is before every key, past the
-    // window of every key, or the keys are padding
-    const bool none = t0 + kBM - 1 < kbase || kbase >= u ||
-                      (window > 0 && t0 - (kbase + 31) > window - 1);
-    if (none) continue;
-    const bool mask = !(kbase + 31 < u && t0 + kBM - 1 < u && t0 >= kbase + 31 &&
-                        (window == 0 || t0 + kBM - 1 - kbase <= window - 1));
-    const uint4* st = smem[j % kBwdStages];
-    const uint4* qfp = st;
-    const uint4* dfp = st + kQtPart / 16;
-    const uint4* qtp = st + 2 * kQtPart / 16;
-    const uint4* dtp = st + 3 * kQtPart / 16;
-    const float* stats = reinterpret_cast<const float*>(st + 4 * kQtPart / 16);
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      s = mfma(ld_frag(qfp + kk * 64 + lane), kf[kk], s);
-      dp = mfma(ld_frag(dfp + kk * 64 + lane), vf[kk], dp);
-    }
-    // S and dP: lane (col, half) holds key kbase + col and queries
-    // t0 + 8rg + 4half + jj at index 4rg + jj
-    float pr[16], gr[16];
-    const int key = kbase + col;
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const float4 L = *reinterpret_cast<const float4*>(stats + 8 * rg + 4 * half);
-      const float4 R = *reinterpret_cast<const float4*>(stats + kBM + 8 * rg + 4 * half);
-      const float Lv[4] = {L.x, L.y, L.z, L.w}, Rv[4] = {R.x, R.y, R.z, R.w};
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int i = 4 * rg + jj;
-        float pv = __builtin_amdgcn_exp2f(s[i] - Lv[jj]);
-        if (mask) {
-          const int qrow = t0 + 8 * rg + 4 * half + jj;
-          const bool ok = key <= qrow && key < u && qrow < u &&
-                          (window == 0 || qrow - key <= window - 1);
-          pv = ok ? pv : 0.f;
-        }
-        pr[i] = pv;
-        gr[i] = pv * (dp[i] - Rv[jj]);
-      }
-    }
-    const bf16x8 pb[2] = {pack_frag(pr), pack_frag(pr + 8)};
-    const bf16x8 gb[2] = {pack_frag(gr), pack_frag(gr + 8)};
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        dv[db] = mfma(ld_frag(dtp + frag_index(db, 2, kk, 0, 0) + lane), pb[kk], dv[db]);
-        dk[db] = mfma(ld_frag(qtp + frag_index(db, 2, kk, 0, 0) + lane), gb[kk], dk[db]);
-      }
+    dkdv_step(smem[j % kDkdvStages], lane, half, kf, vf, dk, dv, qfirst, qrange, t0);
   }
 
   // FP32 partial sums of this chunk: [dK' | dV][128 keys][128 channels];
@@ -920,8 +1014,8 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdWs ws, int empty,
   const int NQ = empty ? 0 : ws.f.hdr[2], NT = empty ? 0 : ws.f.hdr[1];
   float v = 0.f;
   if (b < kD) {
-    const float* src = ws.wq + (size_t)b * (ws.nqmax * 2 * kG);
-    for (int j = tid; j < NQ * 2 * kG; j += 256) v += src[j];
+    const float* src = ws.wq + (size_t)b * (ws.nqmax * kG);
+    for (int j = tid; j < NQ * kG; j += 256) v += src[j];
     v = block_sum256(v, sh);
     if (tid == 0) dq_norm_w[b] = v;
   } else if (b < 2 * kD) {
@@ -1017,7 +1111,7 @@ extern "C" int flint_attn_bwd(const void* q, const void* k, const void* v, const
     bwd_q_prep_kernel<<<dim3((unsigned)L.f.nqmax, kH), 256, 0, st>>>(
         qh, static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, q_norm_w,
         sink, pos, eps, rope, ws);
-    bwd_dq_kernel<<<(unsigned)(L.f.nqmax * 2 * kG), kBwdThreads, 0, st>>>(
+    bwd_dq_kernel<<<(unsigned)(L.f.nqmax * kG), kDqThreads, 0, st>>>(
         qh, q_norm_w, pos, window, rope, eps, ws, static_cast<uint16_t*>(dq));
     bwd_dkdv_kernel<<<(unsigned)(L.ncmax * kG), kBwdThreads, 0, st>>>(window, ws);
     bwd_kv_reduce_kernel<<<dim3((unsigned)L.f.ntmax, kG), 256, 0, st>>>(

@@ -218,6 +218,92 @@ def decode_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def backward_bench(args):
+    """Backward of one layer: dq, dk, dv, the norm-weight and sink gradients.
+
+    The forward (with its row normalizer) runs once, untimed; every timed step
+    is one flint_attn_bwd call over the whole workload. Algorithmic FLOPs are
+    the usual 2.5x the forward's (five 2*128-FLOP products per unmasked
+    (query, key, head) pair: the logit recompute, dP, dV, dK and dQ); the
+    kernels execute 3.5x (the query-major dQ pass recomputes the logits and dP).
+    """
+    import torch
+
+    import attention_head_rmsnorm_amd as fa
+    from workload import make_workload
+    from workload.gen import draw_dout
+
+    cfg = args.config
+    li = 0
+    if cfg == "c4full":
+        cfg, li = "c4", 1
+    wl = make_workload(cfg)
+    layer = wl.layers[li]
+    dev = torch.device("cuda", 0)
+    fa.load_library()
+    q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
+    qw, kw, sk = wl.q_norm_w.to(dev), wl.k_norm_w.to(dev), wl.sinks.to(dev)
+    cu = wl.cu_seqlens.to(dev)
+    su = None if wl.seqused is None else wl.seqused.to(dev)
+    pos = None if wl.positions is None else wl.positions.to(dev)
+    T, n, mx = wl.total_tokens, wl.n_seqs, wl.max_seqlen
+    kw_args = dict(positions=pos, cu_seqlens=cu, seqused=su, max_seqlen=mx, window=layer.window,
+                   use_rope=layer.use_rope, rope_theta=layer.theta, eps=layer.eps)
+    out, lse = fa.flint_attn(q, k, v, qw, kw, sk, return_lse=True, **kw_args)
+    dout = draw_dout(wl.seed, T).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dqw, dkw, dsk = torch.empty_like(qw), torch.empty_like(kw), torch.empty_like(sk)
+    nbytes = fa.flint_attn_bwd_workspace_bytes(T, n, mx)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    p = lambda t: 0 if t is None else int(t.data_ptr())  # noqa: E731
+    call = [p(q), p(k), p(v), p(qw), p(kw), p(sk), p(pos), p(cu), p(su), n, mx, T, 32, 4, 128,
+            layer.window, int(layer.use_rope), layer.theta, layer.eps, p(out), p(lse), p(dout),
+            p(ws), nbytes, p(dq), p(dk), p(dv), p(dqw), p(dkw), p(dsk), int(stream.cuda_stream)]
+    for _ in range(args.warmup):
+        st = fa.flint_attn_bwd(*call)
+        if st != 0:
+            raise RuntimeError(fa.flint_attn_strerror(st))
+    torch.cuda.synchronize()
+    st, flags = fa.flint_attn_device_status(p(ws), int(stream.cuda_stream))
+    if st != 0:
+        raise RuntimeError(f"device data error flags {flags}")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        fa.flint_attn_bwd(*call)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+    pairs = unmasked_pairs(wl.cu_seqlens.numpy(), None if wl.seqused is None else wl.seqused.numpy(),
+                           layer.window)
+    flops = 2.5 * 16384.0 * pairs
+    value = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "sink-attention backward TFLOP/s (2.5x the forward's unmasked FLOPs), 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v and dO, N(1,0.1) norm weights, N(0,1) sinks)",
+        "config": {"workload": wl.description, "name": wl.name, "layer": layer.name,
+                   "total_tokens": T, "n_seqs": n, "window": layer.window,
+                   "use_rope": layer.use_rope},
+        "pct_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
+        "algorithmic_flops": flops,
+        "executed_mfma_tflops": round(3.5 * 16384.0 * pairs / (ms * 1e-3) / 1e12, 3),
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +314,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--backward", action="store_true")
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--decode-len", type=int, default=8192)
     ap.add_argument("--decode-window", type=int, default=0)
@@ -245,6 +332,9 @@ def main():
         return
     if args.decode:
         decode_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
 
     import attention_head_rmsnorm_amd as fa
