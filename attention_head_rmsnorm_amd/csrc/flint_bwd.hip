@@ -14,9 +14,10 @@
 //
 // Kernels, in order on the caller's stream:
 //   schedule_kernel (forward)  sequence table, key tiles, query blocks.
-//   bwd_schedule_kernel   one workgroup: splits the query range seen by each
-//                         128-key block into chunks of about equal work and
-//                         orders the chunks by decreasing work.
+//   bwd_schedule_kernel   one workgroup: cuts the query range seen by each
+//                         128-key block at fixed chunk boundaries and orders
+//                         the chunks by query position, so the workgroups on
+//                         one L2 share the query tiles they stream.
 //   bwd_kv_prep_kernel    per (64-key tile, kv head): K' = RoPE(RMSNorm(k)) in
 //                         bf16 as a K' operand tile, V as a V operand tile, and
 //                         K'^T in the key-slot order of the dQ product; zero dq
@@ -32,7 +33,7 @@
 //                         dP^T = V dO^T, dS^T, dQ'^T += K'^T dS^T; then RoPE and
 //                         RMSNorm adjoints, dq, and the block's q-norm-weight
 //                         terms.
-//   bwd_dkdv_kernel       key-major: per (128 keys, kv head, query chunk), over
+//   bwd_dkdv_kernel       key-major: per (256 keys, kv head, query chunk), over
 //                         the chunk's query blocks x 8 heads: S = Q'K'^T,
 //                         dP = dO V^T, dS, dV^T += dO^T P, dK'^T += Q'^T dS, as
 //                         FP32 partial sums of the chunk.
@@ -49,17 +50,17 @@
 
 namespace flint {
 
-constexpr int kBwdThreads = 256;             // four waves
 constexpr int kKvbPart = kBN * kD * 2;       // 16 KiB: one 64-key operand part
 constexpr int kKvbBytes = 3 * kKvbPart;      // K' | V | K'^T (key-slot order)
 constexpr int kQtPart = kBM * kD * 2;        // 8 KiB: one 32-query operand part
 constexpr int kQtStats = 2 * kBM * 4;        // lse (log2 units) [32], Dr [32]
 constexpr int kQtBytes = 4 * kQtPart + kQtStats;  // Q' | dO | Q'^T | dO^T | stats
-constexpr int kQtVecPerWave = 4 * kQtPart / (16 * kBwdThreads);  // 8
 constexpr int kBwdStages = 3;
-constexpr int kKB = 2 * kBN;                 // keys per dK/dV item
-constexpr int kTargetChunks = 512;           // about this many key-major items per kv head
+constexpr int kKBTiles = 4;                  // key tiles per dK/dV item
+constexpr int kKB = kKBTiles * kBN;          // keys per dK/dV item (one wave per 32)
+constexpr int kTargetChunks = 1024;          // about this many key-major items per kv head
 constexpr int kMinChunkQB = 8;               // query blocks per chunk, at least
+constexpr int kXcds = 8;                     // L2 domains; workgroups reach them round robin
 constexpr int kHdrNC = 8;                    // header: key-major items
 constexpr int kHdrCH = 9;                    // header: query blocks per chunk
 constexpr float kInvSqrtD = 0.08838834764831845f;
@@ -74,7 +75,7 @@ struct BwdWs {
   float* wk;       // [kD][ntmax * kG]: k-norm-weight terms per (tile, kv head)
   int* cb;         // [ntmax] first chunk slot of the key block starting at tile e
   int* nc;         // [ntmax] its chunks
-  int2* kitems;    // [ncmax] {tile, chunk}, most work first
+  int2* kitems;    // [ncmax] {tile, chunk}, by the chunk's global query position
   float* part;     // [ncmax][kG][kPartFloats]
   int nqmax, ncmax, n;
 };
@@ -88,7 +89,8 @@ struct BwdLayout {
 static BwdLayout make_bwd_layout(int64_t T, int64_t n) {
   BwdLayout L;
   L.f = make_layout(T, n, false);
-  L.ncmax = kTargetChunks + L.f.ntmax;
+  // chunks of a key block: at most work / CH + 2; key blocks: at most (ntmax + 3n) / 4
+  L.ncmax = kTargetChunks + L.f.ntmax + n;
   size_t o = L.f.total;
   L.kvb = o;      o = align_up(o + (size_t)kG * L.f.ntmax * kKvbBytes, 256);
   L.qt = o;       o = align_up(o + (size_t)L.f.nqmax * kH * kQtBytes, 256);
@@ -129,7 +131,7 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Query blocks [*lo, *hi) that see some key of the 128-key block starting at
+// Query blocks [*lo, *hi) that see some key of the 256-key block starting at
 // key k0 of a sequence with valid length u (none when k0 >= u).
 __device__ __forceinline__ void kb_queries(int k0, int u, int window, int* lo, int* hi) {
   if (k0 >= u) {
@@ -142,27 +144,39 @@ __device__ __forceinline__ void kb_queries(int k0, int u, int window, int* lo, i
   *hi = (q_end + kBM - 1) / kBM;
 }
 
-// Work of the key block that starts at tile e (query blocks), 0 for odd tiles.
-__device__ __forceinline__ int kb_work(const BwdWs& ws, int e, int window, int* lo) {
+// Query blocks [*lo, *hi) seen by the key block that starts at tile e; empty
+// for tiles inside a key block (one is kKBTiles tiles) and for key blocks of
+// padding.
+// Returns the tile's sequence.
+__device__ __forceinline__ int kb_range(const BwdWs& ws, int e, int window, int* lo, int* hi) {
   const int2 te = ws.f.tiles[e];
-  if (te.y & 1) return 0;
-  const int u = ws.f.seq[te.x].z;
-  int hi;
-  kb_queries(te.y * kBN, u, window, lo, &hi);
-  return hi - *lo;
+  *lo = *hi = 0;
+  if (te.y % kKBTiles) return te.x;
+  kb_queries(te.y * kBN, ws.f.seq[te.x].z, window, lo, hi);
+  return te.x;
 }
 
 // ----------------------------------------------------------------- schedule
 
+// Key-major work items. The query range seen by a 256-key block is cut at
+// fixed query-block positions, multiples of CH: chunk c of a sequence covers
+// its query blocks [c CH, (c + 1) CH). Every key block overlapping chunk c
+// reads the same Q'/dO tiles, so the item list is sorted by the chunk's
+// global position, and each of the kXcds L2 domains takes one contiguous
+// stretch of it (per kv head): the workgroups running together on one L2
+// stream the same tiles at about the same time. CH grows with the total work
+// so there are about kTargetChunks chunks per kv head.
 __global__ __launch_bounds__(1024) void bwd_schedule_kernel(int window, BwdWs ws) {
   __shared__ int tmp[1024];
   __shared__ int hist[kBuckets];
   const int tid = threadIdx.x;
   const int NT = ws.f.hdr[1];
-  // total work, then the chunk size that gives about kTargetChunks chunks
-  int lo;
+  int lo, hi;
   int local = 0;
-  for (int e = tid; e < NT; e += 1024) local += kb_work(ws, e, window, &lo);
+  for (int e = tid; e < NT; e += 1024) {
+    kb_range(ws, e, window, &lo, &hi);
+    local += hi - lo;
+  }
   int total;
   (void)block_excl_scan(local, tmp, &total);
   const int CH = max(kMinChunkQB, (total + kTargetChunks - 1) / kTargetChunks);
@@ -170,8 +184,11 @@ __global__ __launch_bounds__(1024) void bwd_schedule_kernel(int window, BwdWs ws
   int carry = 0;
   for (int base = 0; base < NT; base += 1024) {
     const int e = base + tid;
-    const int w = e < NT ? kb_work(ws, e, window, &lo) : 0;
-    const int c = (w + CH - 1) / CH;
+    int c = 0;
+    if (e < NT) {
+      kb_range(ws, e, window, &lo, &hi);
+      c = hi > lo ? (hi + CH - 1) / CH - lo / CH : 0;
+    }
     int tot;
     const int ex = block_excl_scan(c, tmp, &tot);
     if (e < NT) {
@@ -180,29 +197,32 @@ __global__ __launch_bounds__(1024) void bwd_schedule_kernel(int window, BwdWs ws
     }
     carry += tot;
   }
+  // counting sort by the chunk's global query position (qbase + c CH) / CH
   for (int i = tid; i < kBuckets; i += 1024) hist[i] = 0;
   __syncthreads();
   for (int e = tid; e < NT; e += 1024) {
-    const int w = kb_work(ws, e, window, &lo);
-    for (int c = 0; c * CH < w; ++c) atomicAdd(&hist[min(min(CH, w - c * CH), kBuckets - 1)], 1);
+    const int sq = kb_range(ws, e, window, &lo, &hi);
+    const int qb = ws.f.qbase[sq];
+    for (int c = lo / CH; c * CH < hi; ++c) atomicAdd(&hist[min((qb + c * CH) / CH, kBuckets - 1)], 1);
   }
   __syncthreads();
   int local4[4], sum = 0;
   for (int j = 0; j < 4; ++j) {
-    local4[j] = hist[kBuckets - 1 - (4 * tid + j)];
+    local4[j] = hist[4 * tid + j];
     sum += local4[j];
   }
   int tot;
   int run = block_excl_scan(sum, tmp, &tot);
   for (int j = 0; j < 4; ++j) {
-    hist[kBuckets - 1 - (4 * tid + j)] = run;
+    hist[4 * tid + j] = run;
     run += local4[j];
   }
   __syncthreads();
   for (int e = tid; e < NT; e += 1024) {
-    const int w = kb_work(ws, e, window, &lo);
-    for (int c = 0; c * CH < w; ++c) {
-      const int pos = atomicAdd(&hist[min(min(CH, w - c * CH), kBuckets - 1)], 1);
+    const int sq = kb_range(ws, e, window, &lo, &hi);
+    const int qb = ws.f.qbase[sq];
+    for (int c = lo / CH; c * CH < hi; ++c) {
+      const int pos = atomicAdd(&hist[min((qb + c * CH) / CH, kBuckets - 1)], 1);
       ws.kitems[pos] = make_int2(e, c);
     }
   }
@@ -676,84 +696,88 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __re
 
 // ----------------------------------------------------------------- dK, dV
 
-// Row terms of a step for the lanes of `half`: lse (log2 units) and Dr of
-// queries 8rg + 4half + [0, 4), rg = 0..3, as lv / rv[4rg + j]. The step's
-// terms arrive in LDS by a direct global->LDS load, which the compiler's wait
-// insertion cannot tell from the loads still in flight for later steps (it
-// would wait for all of them), so the read is written out with its own wait.
-__device__ __forceinline__ void read_stats(const float* stats, int half, float* lv, float* rv) {
+constexpr int kDkdvThreads = 512;  // eight waves, one per 32 keys
+constexpr int kDkdvStages = 2;     // the step in use and the next one loading
+constexpr int kDkdvAhead = 3;      // operand fragments read ahead of their product
+constexpr int kStepVecPerWave = 4 * kQtPart / (16 * kDkdvThreads);  // 4
+
+// Row terms lse (log2 units) and Dr of queries 8rg + 4half + [0, 4) for the
+// lanes of `half`. The step's terms arrive in LDS by a direct global->LDS
+// load, which the compiler's wait insertion cannot tell from the loads still
+// in flight for the next step (it would wait for them too), so the read is
+// written out with its own wait.
+__device__ __forceinline__ void read_stats4(const float* stats, int half, int rg, float* lv, float* rv) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  f32x4_t a0, a1, a2, a3, b0, b1, b2, b3;
+  f32x4_t a, b;
   const unsigned base =
-      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) float*)stats + 16u * half;
+      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) float*)stats + 16u * half + 32u * rg;
+  // early clobber: a read's destination must not be the address register
   asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:32\n\t"
-      "ds_read_b128 %2, %8 offset:64\n\t"
-      "ds_read_b128 %3, %8 offset:96\n\t"
-      "ds_read_b128 %4, %8 offset:128\n\t"
-      "ds_read_b128 %5, %8 offset:160\n\t"
-      "ds_read_b128 %6, %8 offset:192\n\t"
-      "ds_read_b128 %7, %8 offset:224\n\t"
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %2 offset:128\n\t"
       "s_waitcnt lgkmcnt(0)"
-      // early clobber: a read's destination must not be the address register
-      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+      : "=&v"(a), "=&v"(b)
       : "v"(base)
       : "memory");
-  const f32x4_t a[4] = {a0, a1, a2, a3}, b[4] = {b0, b1, b2, b3};
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lv[4 * rg + j] = a[rg][j];
-      rv[4 * rg + j] = b[rg][j];
-    }
+  for (int j = 0; j < 4; ++j) {
+    lv[j] = a[j];
+    rv[j] = b[j];
+  }
 }
 
-constexpr int kDkdvStages = 3;  // the step in use and two loads ahead
-constexpr int kDkdvAhead = 4;   // operand fragments read ahead of their product
-
 // One step of the key-major kernel for the wave's 32 keys, as one straight
-// block: S = Q'K'^T and dP = dO V^T (A operands from LDS, read kDkdvAhead
-// products ahead), P = exp2(S - lse) and dS = P (dP - Dr), then
+// block: S = Q'K'^T and dP = dO V^T (A operands from the step's stage, V's B
+// operand from the item's V tiles in LDS, K' in registers; fragments read
+// kDkdvAhead products ahead), P = exp2(S - lse) and dS = P (dP - Dr), then
 // dV^T += dO^T P and dK'^T += Q'^T dS. The lane's key is seen by queries
 // qlo .. qlo + qrange (causal, window and length limits); the mask is applied
 // on every step, so the loop body has no branch.
-__device__ __forceinline__ void dkdv_step(const uint4* st, int lane, int half, const bf16x8* kf,
-                                          const bf16x8* vf, f32x16* dk, f32x16* dv, int qlo,
+__device__ __forceinline__ void dkdv_step(const uint4* st, const uint4* vt, int lane, int half,
+                                          const bf16x8* kf, f32x16* dk, f32x16* dv, int qlo,
                                           unsigned qrange, int t0) {
   f32x16 s = {}, dp = {};
   {
-    // fragment i: Q' (even) or dO (odd) at channel step i >> 1
+    // fragment i: Q' (i even, A of S at channel step i >> 1) or, for odd i,
+    // dO (A of dP) and V (its B), at channel step i >> 1
+    bf16x8 f[16], fv[8];
     auto frag = [&](int i) { return ld_frag(st + (i & 1) * (kQtPart / 16) + (i >> 1) * 64 + lane); };
-    bf16x8 f[16];
 #pragma unroll
-    for (int i = 0; i < kDkdvAhead; ++i) f[i] = frag(i);
-    __builtin_amdgcn_sched_group_barrier(0x100, kDkdvAhead, 0);
+    for (int i = 0; i < kDkdvAhead; ++i) {
+      f[i] = frag(i);
+      if (i & 1) fv[i >> 1] = ld_frag(vt + (i >> 1) * 64 + lane);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i + kDkdvAhead < 16) f[i + kDkdvAhead] = frag(i + kDkdvAhead);
-      if (i & 1) dp = mfma(f[i], vf[i >> 1], dp);
+      if (i + kDkdvAhead < 16) {
+        const int n = i + kDkdvAhead;
+        f[n] = frag(n);
+        if (n & 1) fv[n >> 1] = ld_frag(vt + (n >> 1) * 64 + lane);
+      }
+      if (i & 1) dp = mfma(f[i], fv[i >> 1], dp);
       else s = mfma(f[i], kf[i >> 1], s);
-      if (i + kDkdvAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   }
   bf16x8 pb[2], gb[2];
   {
-    float lv[16], rv[16];
-    read_stats(reinterpret_cast<const float*>(st + 4 * kQtPart / 16), half, lv, rv);
+    const float* stats = reinterpret_cast<const float*>(st + 4 * kQtPart / 16);
+    // S rows are queries t0 + 8rg + 4half + j; this lane's key allows rows
+    // qlo .. qlo + qrange
+    const int d0 = t0 + 4 * half - qlo;
     float pr[16], gr[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) pr[e] = __builtin_amdgcn_exp2f(s[e] - lv[e]);
-    // S rows are queries t0 + 8(e>>2) + 4half + (e&3); this lane's key
-    // allows rows qlo .. qlo + qrange
-    const int d0 = t0 + 4 * half - qlo;
+    for (int rg = 0; rg < 4; ++rg) {
+      float lv[4], rv[4];
+      read_stats4(stats, half, rg, lv, rv);
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      pr[e] = (unsigned)(d0 + 8 * (e >> 2) + (e & 3)) <= qrange ? pr[e] : 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) gr[e] = pr[e] * (dp[e] - rv[e]);
+      for (int j = 0; j < 4; ++j) {
+        const int e = 4 * rg + j;
+        float pv = __builtin_amdgcn_exp2f(s[e] - lv[j]);
+        pv = (unsigned)(d0 + 8 * rg + j) <= qrange ? pv : 0.f;
+        pr[e] = pv;
+        gr[e] = pv * (dp[e] - rv[j]);
+      }
+    }
     pb[0] = pack_frag(pr);
     pb[1] = pack_frag(pr + 8);
     gb[0] = pack_frag(gr);
@@ -767,24 +791,26 @@ __device__ __forceinline__ void dkdv_step(const uint4* st, int lane, int half, c
     bf16x8 f[16];
 #pragma unroll
     for (int i = 0; i < kDkdvAhead; ++i) f[i] = frag(i);
-    __builtin_amdgcn_sched_group_barrier(0x100, kDkdvAhead, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + kDkdvAhead < 16) f[i + kDkdvAhead] = frag(i + kDkdvAhead);
       const int db = i >> 2, kk = (i >> 1) & 1;
       if (i & 1) dk[db] = mfma(f[i], gb[kk], dk[db]);
       else dv[db] = mfma(f[i], pb[kk], dv[db]);
-      if (i + kDkdvAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   }
 }
 
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(int window, BwdWs ws) {
+__global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(int window, BwdWs ws) {
   __shared__ uint4 smem[kDkdvStages][kQtBytes / 16];
-  const int bid = blockIdx.x;
-  const int ii = bid >> 2, g = bid & (kG - 1);
-  if (ii >= ws.f.hdr[kHdrNC]) return;
+  __shared__ uint4 vlds[kKBTiles][kKvbPart / 16];  // the item's V operand tiles
+  // Workgroup b runs on L2 domain b % kXcds; domain x takes ranks
+  // [x per, (x + 1) per) of the kv-head-major item list.
+  const int NC = ws.f.hdr[kHdrNC];
+  const int per = (NC * kG + kXcds - 1) / kXcds;
+  const int rank = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if ((int)(blockIdx.x / kXcds) >= per || rank >= NC * kG) return;
+  const int g = rank / NC, ii = rank - g * NC;
   const int CH = ws.f.hdr[kHdrCH];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -798,28 +824,32 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(int window, BwdWs
   const int k0 = te.y * kBN;
   int qlo, qhi;
   kb_queries(k0, u, window, &qlo, &qhi);
-  const int qb0 = qlo + chunk * CH;
-  const int qb1 = min(qhi, qb0 + CH);
+  const int qb0 = max(qlo, chunk * CH);
+  const int qb1 = min(qhi, (chunk + 1) * CH);
   const int nsteps = (qb1 - qb0) * kHpg;
   const int qgbase = ws.f.qbase[te.x];
   const int voff = lane * 16 + wave * 1024;
 
-  // This wave's 32 keys: tile e + (wave >> 1), block wave & 1. K' and V as
-  // B operands (key col, channels 16kk + 8half ..); a tile past the
-  // sequence's last reads as zeros and its keys are masked.
+  // The item's key tiles e .. e + 3 (those inside the sequence; reads past
+  // them return zeros and their keys are masked). Wave w owns keys
+  // 32 (w & 1) .. + 32 of tile w >> 1: K' as B operands in registers, V's
+  // operand tiles in LDS.
   const int kt = wave >> 1, bb = wave & 1;
   const int kbase = k0 + kt * kBN + bb * 32;
-  const bool tile_exists = te.y + kt < (len + kBN - 1) / kBN;
-  const char* ktile = ws.kvb + ((size_t)g * ws.f.ntmax + e + kt) * kKvbBytes;
-  const __amdgpu_buffer_rsrc_t krs = rsrc_of(ktile, tile_exists ? 2 * kKvbPart : 0);
-  bf16x8 kf[8], vf[8];
+  const int ntiles = min(kKBTiles, (len + kBN - 1) / kBN - te.y);
+  const char* tiles = ws.kvb + ((size_t)g * ws.f.ntmax + e) * kKvbBytes;
+  const __amdgpu_buffer_rsrc_t krs = rsrc_of(tiles, ntiles * kKvbBytes);
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    kf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                            krs, frag_index(bb, 8, kk, half, col) * 16, 0, 0));
-    vf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                            krs, kKvbPart + frag_index(bb, 8, kk, half, col) * 16, 0, 0));
+  for (int i = 0; i < 8; ++i) {
+    const int ci = i * 8 + wave;  // 1 KiB chunk ci of the 64 KiB of V tiles
+    dma16(krs, lane * 16, (ci >> 4) * kKvbBytes + kKvbPart + (ci & 15) * 1024,
+          reinterpret_cast<char*>(vlds[ci >> 4]) + (ci & 15) * 1024);
   }
+  bf16x8 kf[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    kf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            krs, kt * kKvbBytes + frag_index(bb, 8, kk, half, col) * 16, 0, 0));
 
   // step j: query block qb0 + j / 8, head 8g + j % 8
   auto load_step = [&](int j, int stage) {
@@ -828,12 +858,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(int window, BwdWs
     const __amdgpu_buffer_rsrc_t r = rsrc_of(src, kQtBytes);
     char* dst = reinterpret_cast<char*>(smem[stage]);
 #pragma unroll
-    for (int i = 0; i < kQtVecPerWave; ++i) dma16(r, voff, i * 4096, dst + i * 4096 + wave * 1024);
-    dma4(r, lane * 4, 4 * kQtPart, dst + 4 * kQtPart);
+    for (int i = 0; i < kStepVecPerWave; ++i) dma16(r, voff, i * 8192, dst + i * 8192 + wave * 1024);
+    dma4(r, lane * 4, 4 * kQtPart, dst + 4 * kQtPart);  // the row terms (every wave loads the same)
   };
-  constexpr int kStepOps = kQtVecPerWave + 1;
   load_step(0, 0);
-  if (nsteps > 1) load_step(1, 1);
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -849,22 +877,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(int window, BwdWs
   const int qlast = window > 0 ? min(key + window - 1, u - 1) : u - 1;
   const unsigned qrange = key < u ? (unsigned)(qlast - key) : 0xffffffffu;
   const int qfirst = key < u ? key : 0x40000000;
+  const uint4* vt = vlds[kt] + frag_index(bb, 8, 0, 0, 0);
   // every step of the wave's keys is computed; one whose queries see none of
   // them (before the keys, past their window) has an all-zero P
   for (int j = 0; j < nsteps; ++j) {
-    // step j's operands are in LDS once at most the next step's loads remain
-    if (j + 1 < nsteps) ring_barrier_n<kStepOps>();
-    else ring_barrier_n<0>();
-    if (j + 2 < nsteps) load_step(j + 2, (j + 2) % kDkdvStages);
+    // step j's operands (and, at j = 0, the V tiles) are in LDS once this
+    // wave's loads are done; after the barrier every wave has finished step
+    // j - 1, so its stage takes step j + 1
+    ring_barrier_n<0>();
+    if (j + 1 < nsteps) load_step(j + 1, (j + 1) % kDkdvStages);
     const int t0 = (qb0 + j / kHpg) * kBM;
-    dkdv_step(smem[j % kDkdvStages], lane, half, kf, vf, dk, dv, qfirst, qrange, t0);
+    dkdv_step(smem[j % kDkdvStages], vt, lane, half, kf, dk, dv, qfirst, qrange, t0);
   }
 
-  // FP32 partial sums of this chunk: [dK' | dV][128 keys][128 channels];
+  // FP32 partial sums of this chunk: [dK' | dV][256 keys][128 channels];
   // lane (col, half) holds key col of the wave's block, channels
   // 32db + 8rg + 4half + [0, 4) at index 4rg + [0, 4). Q' carries the
   // softmax scale log2(e)/sqrt(d), so dK' = dS^T Q' ln 2.
-  float* part = ws.part + ((size_t)(ws.cb[e] + chunk) * kG + g) * kPartFloats;
+  float* part = ws.part + ((size_t)(ws.cb[e] + chunk - qlo / CH) * kG + g) * kPartFloats;
   const int krow = kt * kBN + bb * 32 + col;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -897,8 +927,8 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const uint16_t* __re
   const int ell = te.y * kBN + r;
   const bool valid = ell < u;
   const size_t t = (size_t)start + ell;
-  const int eb = e - (te.y & 1);
-  const int row = (te.y & 1) * kBN + r;
+  const int eb = e - te.y % kKBTiles;
+  const int row = te.y % kKBTiles * kBN + r;
   // channels [16p, 16p+16) and [64+16p, 64+16p+16)
   float gk[32], gv[32];
 #pragma unroll
@@ -1113,7 +1143,7 @@ extern "C" int flint_attn_bwd(const void* q, const void* k, const void* v, const
         sink, pos, eps, rope, ws);
     bwd_dq_kernel<<<(unsigned)(L.f.nqmax * kG), kDqThreads, 0, st>>>(
         qh, q_norm_w, pos, window, rope, eps, ws, static_cast<uint16_t*>(dq));
-    bwd_dkdv_kernel<<<(unsigned)(L.ncmax * kG), kBwdThreads, 0, st>>>(window, ws);
+    bwd_dkdv_kernel<<<(unsigned)((L.ncmax * kG + kXcds - 1) / kXcds * kXcds), kDkdvThreads, 0, st>>>(window, ws);
     bwd_kv_reduce_kernel<<<dim3((unsigned)L.f.ntmax, kG), 256, 0, st>>>(
         kh, k_norm_w, pos, eps, rope, ws, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
     bwd_finalize_kernel<<<2 * kD + kH, 256, 0, st>>>(ws, 0, dq_norm_w, dk_norm_w, dsink);
