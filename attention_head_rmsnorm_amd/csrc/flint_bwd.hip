@@ -54,7 +54,7 @@ constexpr int kKvbPart = kBN * kD * 2;       // 16 KiB: one 64-key operand part
 constexpr int kKvbBytes = 3 * kKvbPart;      // K' | V | K'^T (key-slot order)
 constexpr int kQtPart = kBM * kD * 2;        // 8 KiB: one 32-query operand part
 constexpr int kQtStats = 2 * kBM * 4;        // lse (log2 units) [32], Dr [32]
-constexpr int kQtBytes = 4 * kQtPart + kQtStats;  // Q' | dO | Q'^T | dO^T | stats
+constexpr int kQtBytes = kQtPart + kQtStats;  // Q' in swizzled operand order | stats
 constexpr int kBwdStages = 3;
 constexpr int kKBTiles = 4;                  // key tiles per dK/dV item
 constexpr int kKB = kKBTiles * kBN;          // keys per dK/dV item (one wave per 32)
@@ -124,6 +124,13 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, int voff, int sof
 }
 
 __device__ __forceinline__ bf16x8 ld_frag(const uint4* p) { return __builtin_bit_cast(bf16x8, *p); }
+
+// Swizzled operand order of the 32-query tiles (Q' and dO): row r's channels
+// 16kk + 8half .. + 8 sit at 16-byte unit 64kk + 32half + (r ^ 8half). A
+// 16-byte operand read of k-step kk is a permutation of one 1 KiB unit run,
+// conflict free; lane `lane` reads unit 64kk + swz(lane).
+__device__ __forceinline__ int swz(int lane) { return lane ^ ((lane >> 5) << 3); }
+
 
 __device__ __forceinline__ bf16x8 pack_frag(const float* x) { return __builtin_bit_cast(bf16x8, pack8(x)); }
 
@@ -345,8 +352,6 @@ __global__ __launch_bounds__(256) void bwd_q_prep_kernel(const uint16_t* __restr
                                                          const float* __restrict__ sink,
                                                          const int* __restrict__ positions,
                                                          float eps, int use_rope, BwdWs ws) {
-  __shared__ __attribute__((aligned(16))) uint16_t qts[kD * kBM];
-  __shared__ __attribute__((aligned(16))) uint16_t dts[kD * kBM];
   __shared__ float red[4];
   const int qg = blockIdx.x, h = blockIdx.y;
   if (qg >= ws.f.hdr[2]) return;
@@ -410,27 +415,13 @@ __global__ __launch_bounds__(256) void bwd_q_prep_kernel(const uint16_t* __restr
   for (int i = 0; i < 16; ++i) x[i] *= kLog2e * kInvSqrtD;
   const uint4 w0 = pack8(x), w1 = pack8(x + 8);
   uint4* qf = reinterpret_cast<uint4*>(tile);
-  uint4* df = reinterpret_cast<uint4*>(tile + kQtPart);
-  // channels 8p.. are k-step p>>1, half p&1; channels 64+8p.. are k-step 4+(p>>1)
-  qf[frag_index(0, 8, p >> 1, p & 1, r)] = w0;
-  qf[frag_index(0, 8, 4 + (p >> 1), p & 1, r)] = w1;
-  df[frag_index(0, 8, p >> 1, p & 1, r)] = da;
-  df[frag_index(0, 8, 4 + (p >> 1), p & 1, r)] = dc;
-  {
-    const int slot = vt_slot(r);
-    const uint32_t wq[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    const uint32_t wd[8] = {da.x, da.y, da.z, da.w, dc.x, dc.y, dc.z, dc.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = (j < 4 ? 8 * p : 64 + 8 * p) + 2 * (j & 3);
-      qts[d * kBM + slot] = (uint16_t)(wq[j] & 0xffff);
-      qts[(d + 1) * kBM + slot] = (uint16_t)(wq[j] >> 16);
-      dts[d * kBM + slot] = (uint16_t)(wd[j] & 0xffff);
-      dts[(d + 1) * kBM + slot] = (uint16_t)(wd[j] >> 16);
-    }
-  }
+  // channels 8p.. are k-step p>>1, half p&1; channels 64+8p.. are k-step
+  // 4+(p>>1); swizzled operand order (unit 64kk + 32half + (r ^ 8half))
+  const int su = 32 * (p & 1) + (r ^ (8 * (p & 1)));
+  qf[64 * (p >> 1) + su] = w0;
+  qf[64 * (4 + (p >> 1)) + su] = w1;
   // row terms and the block's share of the sink adjoint
-  float* stats = reinterpret_cast<float*>(tile + 4 * kQtPart);
+  float* stats = reinterpret_cast<float*>(tile + kQtPart);
   const float l2 = valid ? lse[t * kH + h] * kLog2e : INFINITY;
   float share = 0.f;
   if (p == 0) {
@@ -444,18 +435,6 @@ __global__ __launch_bounds__(256) void bwd_q_prep_kernel(const uint16_t* __restr
   if ((tid & 63) == 0) red[tid >> 6] = share;
   __syncthreads();
   if (tid == 0) ws.sinkpart[(size_t)h * ws.nqmax + qg] = (red[0] + red[1]) + (red[2] + red[3]);
-  {
-    uint4* qtt = reinterpret_cast<uint4*>(tile + 2 * kQtPart);
-    uint4* dtt = reinterpret_cast<uint4*>(tile + 3 * kQtPart);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int qv = tid + 256 * i;
-      const int d = qv >> 2, c = qv & 3;
-      const int fi = frag_index(d >> 5, 2, c >> 1, c & 1, d & 31);
-      qtt[fi] = *reinterpret_cast<const uint4*>(&qts[d * kBM + c * 8]);
-      dtt[fi] = *reinterpret_cast<const uint4*>(&dts[d * kBM + c * 8]);
-    }
-  }
 }
 
 // ----------------------------------------------------------------- dQ
@@ -532,6 +511,7 @@ __device__ __forceinline__ void dq_tile(const uint4* st, int lane, int half, con
 }
 
 __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ dout,
                                                             const float* __restrict__ q_norm_w,
                                                             const int* __restrict__ positions,
                                                             int window, int use_rope, float eps,
@@ -557,17 +537,20 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __re
   const int voff = lane * 16 + wave * 1024;
 
   // Q' and dO of this head as B operands (query col, channels 16kk + 8half..),
-  // and the row terms of query col.
+  // Q' from its prepared tile, dO straight from the caller's tensor (rows past
+  // the valid length read as zeros), and the row terms of query col.
   const char* qtile = ws.qt + ((size_t)qg * kH + h) * kQtBytes;
   const uint4* qfp = reinterpret_cast<const uint4*>(qtile);
-  const uint4* dfp = reinterpret_cast<const uint4*>(qtile + kQtPart);
+  const int rows = min(u - t0, kBM);
+  const __amdgpu_buffer_rsrc_t dor = rsrc_of(dout + ((size_t)(start + t0) * kH + h) * kD, rows * (kH * kD * 2));
   bf16x8 qf[8], df[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    qf[kk] = ld_frag(qfp + kk * 64 + lane);
-    df[kk] = ld_frag(dfp + kk * 64 + lane);
+    qf[kk] = ld_frag(qfp + kk * 64 + swz(lane));
+    df[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            dor, col * (kH * kD * 2) + (16 * kk + 8 * half) * 2, 0, 0));
   }
-  const float* stats = reinterpret_cast<const float*>(qtile + 4 * kQtPart);
+  const float* stats = reinterpret_cast<const float*>(qtile + kQtPart);
   const float l2 = stats[col];
   const float dr = stats[kBM + col];
 
@@ -604,7 +587,6 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __re
   // Epilogue. Lane (col, half) holds dQ'^T for query t0 + col, channels
   // c = 32db + 8rg + 4half + j at acc[db][4rg + j]; c and c + 64 are db and
   // db + 2 at the same index.
-  const int rows = min(u - t0, kBM);
   const bool valid = col < rows;
   float xq[4][16];
   const __amdgpu_buffer_rsrc_t qr = rsrc_of(q + ((size_t)(start + t0) * kH + h) * kD, rows * (kH * kD * 2));
@@ -699,7 +681,33 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __re
 constexpr int kDkdvThreads = 512;  // eight waves, one per 32 keys
 constexpr int kDkdvStages = 2;     // the step in use and the next one loading
 constexpr int kDkdvAhead = 3;      // operand fragments read ahead of their product
-constexpr int kStepVecPerWave = 4 * kQtPart / (16 * kDkdvThreads);  // 4
+constexpr int kStepBytes = 2 * kQtPart + kQtStats;  // a step in LDS: Q' | dO | stats
+
+// A operand of the 32x32x16 MFMA holding X^T, from X (32 rows x 128
+// channels, bf16, swizzled operand order) in LDS: A[c][j] = X[row(j)][c] for
+// channel c = 32db + (lane & 31), rows 16kk + 8s + 4(lane >> 5) + m for k
+// index 8(lane >> 5) + 4s + m. Two transposing LDS reads (ds_read_b64_tr_b16)
+// give the two halves: within each group of 16 lanes, lane i's m-th value is
+// value i & 3 of the 8 bytes that lane 4m + (i >> 2) addresses, so lane
+// 16G + 4m + q addresses row 16kk + 8s + 4(G >> 1) + m, channels
+// 32db + 16(G & 1) + 4q .. + 4. tr_lane_offset(lane, s) is that byte address
+// for db = kk = 0; the swizzle makes the 16 units of each read fall on
+// distinct banks.
+__device__ __forceinline__ unsigned tr_lane_offset(int lane, int s) {
+  const int G = lane >> 4, m = (lane >> 2) & 3, q = lane & 3, hf = q >> 1;
+  const int row = 8 * s + 4 * (G >> 1) + m;
+  return (unsigned)(((G & 1) * 64 + hf * 32 + (row ^ (8 * hf))) * 16 + (q & 1) * 8);
+}
+
+__device__ __forceinline__ bf16x8 ld_frag_tr(const uint4* x, unsigned off0, unsigned off1, int db, int kk) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  __attribute__((address_space(3))) char* b = (__attribute__((address_space(3))) char*)x + db * 2048 + kk * 256;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(b + off0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(b + off1));
+  const v8i16 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, r);
+}
 
 // Row terms lse (log2 units) and Dr of queries 8rg + 4half + [0, 4) for the
 // lanes of `half`. The step's terms arrive in LDS by a direct global->LDS
@@ -730,18 +738,22 @@ __device__ __forceinline__ void read_stats4(const float* stats, int half, int rg
 // block: S = Q'K'^T and dP = dO V^T (A operands from the step's stage, V's B
 // operand from the item's V tiles in LDS, K' in registers; fragments read
 // kDkdvAhead products ahead), P = exp2(S - lse) and dS = P (dP - Dr), then
-// dV^T += dO^T P and dK'^T += Q'^T dS. The lane's key is seen by queries
+// dV^T += dO^T P and dK'^T += Q'^T dS with dO^T and Q'^T read transposed from
+// the same stage. P and dS sit in the B operand with their query rows in the
+// order the transposed reads deliver (k index 8half + 4s + m is query
+// 16kk + 8s + 4half + m, the S accumulator's own row order). The lane's key is seen by queries
 // qlo .. qlo + qrange (causal, window and length limits); the mask is applied
 // on every step, so the loop body has no branch.
 __device__ __forceinline__ void dkdv_step(const uint4* st, const uint4* vt, int lane, int half,
-                                          const bf16x8* kf, f32x16* dk, f32x16* dv, int qlo,
-                                          unsigned qrange, int t0) {
+                                          unsigned tr0, unsigned tr1, const bf16x8* kf,
+                                          f32x16* dk, f32x16* dv, int qlo, unsigned qrange, int t0) {
   f32x16 s = {}, dp = {};
   {
     // fragment i: Q' (i even, A of S at channel step i >> 1) or, for odd i,
     // dO (A of dP) and V (its B), at channel step i >> 1
     bf16x8 f[16], fv[8];
-    auto frag = [&](int i) { return ld_frag(st + (i & 1) * (kQtPart / 16) + (i >> 1) * 64 + lane); };
+    const int sl = swz(lane);
+    auto frag = [&](int i) { return ld_frag(st + (i & 1) * (kQtPart / 16) + (i >> 1) * 64 + sl); };
 #pragma unroll
     for (int i = 0; i < kDkdvAhead; ++i) {
       f[i] = frag(i);
@@ -760,7 +772,7 @@ __device__ __forceinline__ void dkdv_step(const uint4* st, const uint4* vt, int 
   }
   bf16x8 pb[2], gb[2];
   {
-    const float* stats = reinterpret_cast<const float*>(st + 4 * kQtPart / 16);
+    const float* stats = reinterpret_cast<const float*>(st + 2 * kQtPart / 16);
     // S rows are queries t0 + 8rg + 4half + j; this lane's key allows rows
     // qlo .. qlo + qrange
     const int d0 = t0 + 4 * half - qlo;
@@ -786,7 +798,7 @@ __device__ __forceinline__ void dkdv_step(const uint4* st, const uint4* vt, int 
   {
     // fragment i: dO^T (even) or Q'^T (odd) of channel block i >> 2, query step (i >> 1) & 1
     auto frag = [&](int i) {
-      return ld_frag(st + ((i & 1) ? 2 : 3) * (kQtPart / 16) + frag_index(i >> 2, 2, (i >> 1) & 1, 0, 0) + lane);
+      return ld_frag_tr(st + ((i & 1) ? 0 : kQtPart / 16), tr0, tr1, i >> 2, (i >> 1) & 1);
     };
     bf16x8 f[16];
 #pragma unroll
@@ -801,8 +813,9 @@ __device__ __forceinline__ void dkdv_step(const uint4* st, const uint4* vt, int 
   }
 }
 
-__global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(int window, BwdWs ws) {
-  __shared__ uint4 smem[kDkdvStages][kQtBytes / 16];
+__global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const uint16_t* __restrict__ dout,
+                                                                int window, BwdWs ws) {
+  __shared__ uint4 smem[kDkdvStages][kStepBytes / 16];
   __shared__ uint4 vlds[kKBTiles][kKvbPart / 16];  // the item's V operand tiles
   // Workgroup b runs on L2 domain b % kXcds; domain x takes ranks
   // [x per, (x + 1) per) of the kv-head-major item list.
@@ -820,6 +833,7 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(int window, BwdW
   const int2 te = ws.f.tiles[e];
   const int4 meta = ws.f.seq[te.x];
   const int u = __builtin_amdgcn_readfirstlane(meta.z);
+  const int start = __builtin_amdgcn_readfirstlane(meta.x);
   const int len = meta.y;
   const int k0 = te.y * kBN;
   int qlo, qhi;
@@ -851,15 +865,21 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(int window, BwdW
     kf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                             krs, kt * kKvbBytes + frag_index(bb, 8, kk, half, col) * 16, 0, 0));
 
-  // step j: query block qb0 + j / 8, head 8g + j % 8
+  // step j: query block qb0 + j / 8, head 8g + j % 8. Each wave moves one
+  // 1 KiB operand unit of Q' (from its prepared tile) and one of dO, gathered
+  // from the caller's tensor (rows past the valid length read as zeros), and
+  // the step's row terms (every wave loads the same 256 bytes).
   auto load_step = [&](int j, int stage) {
-    const int qg = qgbase + qb0 + j / kHpg;
-    const char* src = ws.qt + ((size_t)qg * kH + g * kHpg + j % kHpg) * kQtBytes;
+    const int qb = qb0 + j / kHpg, hh = g * kHpg + j % kHpg;
+    const char* src = ws.qt + ((size_t)(qgbase + qb) * kH + hh) * kQtBytes;
     const __amdgpu_buffer_rsrc_t r = rsrc_of(src, kQtBytes);
+    const __amdgpu_buffer_rsrc_t dr = rsrc_of(dout + ((size_t)(start + qb * kBM) * kH + hh) * kD,
+                                              min(u - qb * kBM, kBM) * (kH * kD * 2));
     char* dst = reinterpret_cast<char*>(smem[stage]);
-#pragma unroll
-    for (int i = 0; i < kStepVecPerWave; ++i) dma16(r, voff, i * 8192, dst + i * 8192 + wave * 1024);
-    dma4(r, lane * 4, 4 * kQtPart, dst + 4 * kQtPart);  // the row terms (every wave loads the same)
+    dma16(r, voff, 0, dst + wave * 1024);
+    // the lane at unit position `lane` carries row (col ^ 8half): the swizzle
+    dma16(dr, (col ^ (8 * half)) * (kH * kD * 2) + (16 * wave + 8 * half) * 2, 0, dst + kQtPart + wave * 1024);
+    dma4(r, lane * 4, kQtPart, dst + 2 * kQtPart);
   };
   load_step(0, 0);
 
@@ -878,8 +898,11 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(int window, BwdW
   const unsigned qrange = key < u ? (unsigned)(qlast - key) : 0xffffffffu;
   const int qfirst = key < u ? key : 0x40000000;
   const uint4* vt = vlds[kt] + frag_index(bb, 8, 0, 0, 0);
-  // every step of the wave's keys is computed; one whose queries see none of
-  // them (before the keys, past their window) has an all-zero P
+  const unsigned tr0 = tr_lane_offset(lane, 0), tr1 = tr_lane_offset(lane, 1);
+  // Queries that see some key of the wave: kbase .. min(kbase + 31 + window
+  // - 1, u - 1). A step whose 32 queries miss that range is skipped (its P is
+  // zero); with two waves per SIMD the other wave takes the matrix cores.
+  const int wq_lo = kbase, wq_hi = window > 0 ? min(kbase + 31 + window - 1, u - 1) : u - 1;
   for (int j = 0; j < nsteps; ++j) {
     // step j's operands (and, at j = 0, the V tiles) are in LDS once this
     // wave's loads are done; after the barrier every wave has finished step
@@ -887,7 +910,8 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(int window, BwdW
     ring_barrier_n<0>();
     if (j + 1 < nsteps) load_step(j + 1, (j + 1) % kDkdvStages);
     const int t0 = (qb0 + j / kHpg) * kBM;
-    dkdv_step(smem[j % kDkdvStages], vt, lane, half, kf, dk, dv, qfirst, qrange, t0);
+    if (t0 + kBM - 1 < wq_lo || t0 > wq_hi) continue;
+    dkdv_step(smem[j % kDkdvStages], vt, lane, half, tr0, tr1, kf, dk, dv, qfirst, qrange, t0);
   }
 
   // FP32 partial sums of this chunk: [dK' | dV][256 keys][128 channels];
@@ -1142,8 +1166,9 @@ extern "C" int flint_attn_bwd(const void* q, const void* k, const void* v, const
         qh, static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, q_norm_w,
         sink, pos, eps, rope, ws);
     bwd_dq_kernel<<<(unsigned)(L.f.nqmax * kG), kDqThreads, 0, st>>>(
-        qh, q_norm_w, pos, window, rope, eps, ws, static_cast<uint16_t*>(dq));
-    bwd_dkdv_kernel<<<(unsigned)((L.ncmax * kG + kXcds - 1) / kXcds * kXcds), kDkdvThreads, 0, st>>>(window, ws);
+        qh, static_cast<const uint16_t*>(dout), q_norm_w, pos, window, rope, eps, ws, static_cast<uint16_t*>(dq));
+    bwd_dkdv_kernel<<<(unsigned)((L.ncmax * kG + kXcds - 1) / kXcds * kXcds), kDkdvThreads, 0, st>>>(
+        static_cast<const uint16_t*>(dout), window, ws);
     bwd_kv_reduce_kernel<<<dim3((unsigned)L.f.ntmax, kG), 256, 0, st>>>(
         kh, k_norm_w, pos, eps, rope, ws, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
     bwd_finalize_kernel<<<2 * kD + kH, 256, 0, st>>>(ws, 0, dq_norm_w, dk_norm_w, dsink);
