@@ -37,7 +37,9 @@ if ROOT not in sys.path:
 METRIC = "sink-attention prefill TFLOP/s (unmasked FLOPs) & % bf16 MFMA peak, 1 GPU"
 BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "attention_head_rmsnorm_amd", "csrc", "flint_attn.hip")
+# the forward attention kernel's sources (its counters go stale when either changes)
+KERNEL_SRCS = [os.path.join(ROOT, "attention_head_rmsnorm_amd", "csrc", f)
+               for f in ("flint_attn.hip", "flint_common.h")]
 TRAFFIC_PROFILES = {
     "tstar": os.path.join(ROOT, "profiles", "attn_kernel_s8192_full_nope_traffic.md"),
     "c3": os.path.join(ROOT, "profiles", "attn_kernel_b8_s8192_sw513_rope_traffic.md"),
@@ -69,8 +71,11 @@ def pairs_of_rows(cu, seqused, window, rows):
 
 
 def source_sha256():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_from_profile(cfg):
