@@ -52,6 +52,8 @@ EXPORTED = (
     "flint_attn_fwd_lse",
     "flint_attn_bwd_workspace_bytes",
     "flint_attn_bwd",
+    "flint_attn_f16_workspace_bytes",
+    "flint_attn_fwd_f16",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -106,6 +108,10 @@ def load_library() -> ctypes.CDLL:
     lib.flint_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                    i32, i32, f32, f32, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp]
     lib.flint_attn_bwd.restype = ctypes.c_int
+    lib.flint_attn_f16_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.flint_attn_f16_workspace_bytes.restype = sz
+    lib.flint_attn_fwd_f16.argtypes = lib.flint_attn_fwd.argtypes
+    lib.flint_attn_fwd_f16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -153,6 +159,24 @@ def flint_attn_fwd_lse(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens,
                                                  total_tokens, num_q_heads, num_kv_heads,
                                                  head_dim, window, use_rope, rope_theta, eps,
                                                  workspace, workspace_bytes, out, lse, stream))
+
+
+def flint_attn_f16_workspace_bytes(total_tokens: int, n_seqs: int, max_seqlen: int,
+                                   num_kv_heads: int = NUM_KV_HEADS,
+                                   head_dim: int = HEAD_DIM) -> int:
+    return int(load_library().flint_attn_f16_workspace_bytes(total_tokens, n_seqs, max_seqlen,
+                                                             num_kv_heads, head_dim))
+
+
+def flint_attn_fwd_f16(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused, n_seqs,
+                       max_seqlen, total_tokens, num_q_heads, num_kv_heads, head_dim, window,
+                       use_rope, rope_theta, eps, workspace, workspace_bytes, out, stream) -> int:
+    """The FP16 attention-compute variant (FP32 q, k, v and out); returns the status."""
+    return int(load_library().flint_attn_fwd_f16(q, k, v, q_norm_w, k_norm_w, sink, positions,
+                                                 cu_seqlens, seqused, n_seqs, max_seqlen,
+                                                 total_tokens, num_q_heads, num_kv_heads,
+                                                 head_dim, window, use_rope, rope_theta, eps,
+                                                 workspace, workspace_bytes, out, stream))
 
 
 def flint_attn_bwd_workspace_bytes(total_tokens: int, n_seqs: int, max_seqlen: int,
@@ -254,16 +278,17 @@ def seqused_from_mask(attention_mask):
 
 
 def _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, attention_mask,
-                seqused, max_seqlen):
+                seqused, max_seqlen, dtype=None):
     """Checks the layer's tensors; returns (T, n, max_seqlen, cu, seqused, positions)."""
     import torch
 
     if not q.is_cuda:
         raise ValueError("flint_attn runs on a HIP device; q is on the CPU")
     dev = q.device
+    dtype = torch.bfloat16 if dtype is None else dtype
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be bfloat16")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         if t.device != dev:
@@ -351,6 +376,34 @@ def flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens
     if st != FLINT_OK:
         raise FlintError(st, "flint_attn_fwd_lse")
     return out, lse
+
+
+def flint_attn_f16(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens=None,
+                   attention_mask=None, seqused=None, max_seqlen: Optional[int] = None,
+                   window: int = 513, use_rope: bool = True, rope_theta: float = 1.0e6,
+                   eps: float = 1.0e-6, out=None, workspace=None):
+    """The FP16 attention-compute variant on torch tensors: q, k, v float32 (the
+    projections) in the layouts of ``flint_attn``; returns float32 output holding
+    the fp16-rounded attention result."""
+    import torch
+
+    T, n, mx, cu, seqused, positions = _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions,
+                                                   cu_seqlens, attention_mask, seqused, max_seqlen,
+                                                   dtype=torch.float32)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = flint_attn_f16_workspace_bytes(T, n, mx, k.shape[-2], k.shape[-1])
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = flint_attn_fwd_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(sinks),
+                            _ptr(positions), _ptr(cu), _ptr(seqused), n, mx, T, q.shape[-2],
+                            k.shape[-2], q.shape[-1], int(window), int(bool(use_rope)),
+                            float(rope_theta), float(eps), _ptr(workspace), workspace.numel(),
+                            _ptr(out), _stream_handle(dev))
+    if st != FLINT_OK:
+        raise FlintError(st, "flint_attn_fwd_f16")
+    return out
 
 
 def flint_attn_backward(dout, q, k, v, q_norm_w, k_norm_w, sinks, out, lse, *, positions=None,

@@ -51,6 +51,73 @@
 
 namespace flint {
 
+// ----------------------------------------------------------------- operand type
+
+// The attention products take bf16 operands, or fp16 ones in the FP16
+// attention-compute variant ([flint page] Numerical comparison: normalized,
+// rotated Q/K/V cast to FP16 at the attention boundary). Operands travel as
+// 16-bit containers either way; F16 picks the element type.
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef _Float16 f16x2_t __attribute__((__vector_size__(2 * sizeof(_Float16))));
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2t(float a, float b) {
+  if constexpr (F16) {
+    f16x2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  } else {
+    return pack2(a, b);
+  }
+}
+
+template <bool F16>
+__device__ __forceinline__ uint4 pack8t(const float* x) {
+  return make_uint4(pack2t<F16>(x[0], x[1]), pack2t<F16>(x[2], x[3]), pack2t<F16>(x[4], x[5]),
+                    pack2t<F16>(x[6], x[7]));
+}
+
+// acc + sum of the eight packed values in c
+template <bool F16>
+__device__ __forceinline__ float dot2_sumt(const uint4& c, float acc) {
+  if constexpr (F16) {
+    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, c.x), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, c.y), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, c.z), ones, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, c.w), ones, acc, false);
+    return acc;
+  } else {
+    return dot2_sum(c, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc);
+  }
+}
+
+// Sum of squares of eight packed values.
+template <bool F16>
+__device__ __forceinline__ float sumsq8t(const uint4& c) {
+  if constexpr (F16) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2_t h = __builtin_bit_cast(f16x2_t, w[i]);
+      const float a = (float)h[0], b = (float)h[1];
+      s += a * a + b * b;
+    }
+    return s;
+  } else {
+    return sumsq8(c);
+  }
+}
+
 // ----------------------------------------------------------------- schedule
 
 __global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ cu,
@@ -165,13 +232,18 @@ void launch_schedule(const int* cu, const int* seqused, int n, int T, int max_se
 
 // ----------------------------------------------------------------- K/V prologue
 
-__global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v,
+// F16: k, v and out are FP32, the tiles fp16 (the FP16 attention-compute
+// variant); otherwise all three are bf16.
+template <bool F16>
+__global__ __launch_bounds__(256) void kv_prologue_kernel(const void* __restrict__ kp,
+                                                          const void* __restrict__ vp,
                                                           const float* __restrict__ k_norm_w,
                                                           const int* __restrict__ positions,
                                                           float eps, int use_rope, Ws ws,
-                                                          uint16_t* __restrict__ out,
+                                                          void* __restrict__ outp,
                                                           float* __restrict__ lse) {
+  const uint16_t* k = static_cast<const uint16_t*>(kp);
+  const uint16_t* v = static_cast<const uint16_t*>(vp);
   __shared__ __attribute__((aligned(16))) uint16_t vt[kD * kBN];
   __shared__ float red[4];
   const int e = blockIdx.x, g = blockIdx.y;
@@ -187,7 +259,15 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
 
   // K: this thread owns channels [16p, 16p+16) and their RoPE partners +64.
   float x[32];
-  if (valid) {
+  if (valid && F16) {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(kp) + (t * kG + g) * kD);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 a = src[4 * p + i], b = src[16 + 4 * p + i];
+      x[4 * i] = a.x; x[4 * i + 1] = a.y; x[4 * i + 2] = a.z; x[4 * i + 3] = a.w;
+      x[16 + 4 * i] = b.x; x[16 + 4 * i + 1] = b.y; x[16 + 4 * i + 2] = b.z; x[16 + 4 * i + 3] = b.w;
+    }
+  } else if (valid) {
     const uint4* src = reinterpret_cast<const uint4*>(k + (t * kG + g) * kD);
     unpack8(src[2 * p], x);
     unpack8(src[2 * p + 1], x + 8);
@@ -222,13 +302,14 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
   {
     uint4* kfrag = reinterpret_cast<uint4*>(tile);
     const int b = r >> 5, col = r & 31;
-    const uint4 w0 = pack8(x), w1 = pack8(x + 8), w2 = pack8(x + 16), w3 = pack8(x + 24);
+    const uint4 w0 = pack8t<F16>(x), w1 = pack8t<F16>(x + 8), w2 = pack8t<F16>(x + 16),
+                w3 = pack8t<F16>(x + 24);
     kfrag[frag_index(b, 8, p, 0, col)] = w0;      // channels 16p .. 16p+7
     kfrag[frag_index(b, 8, p, 1, col)] = w1;      // 16p+8 .. 16p+15
     kfrag[frag_index(b, 8, 4 + p, 0, col)] = w2;  // 64+16p .. 64+16p+7
     kfrag[frag_index(b, 8, 4 + p, 1, col)] = w3;  // 64+16p+8 .. 64+16p+15
     // |k'| of the rounded key, for the logit bound of the attention kernel
-    float n2 = sumsq8(w0) + sumsq8(w1) + sumsq8(w2) + sumsq8(w3);
+    float n2 = sumsq8t<F16>(w0) + sumsq8t<F16>(w1) + sumsq8t<F16>(w2) + sumsq8t<F16>(w3);
     n2 += __shfl_xor(n2, 1);
     n2 += __shfl_xor(n2, 2);
     // tile max of |k'|: wave max, then across the four waves
@@ -241,7 +322,15 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
   // V: transpose through LDS; this thread owns channels [32p, 32p+32) of key r.
   {
     uint4 c4[4];
-    if (valid) {
+    if (valid && F16) {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(vp) + (t * kG + g) * kD);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 a = src[8 * p + 2 * i], b = src[8 * p + 2 * i + 1];
+        const float y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        c4[i] = pack8t<true>(y);
+      }
+    } else if (valid) {
       const uint4* src = reinterpret_cast<const uint4*>(v + (t * kG + g) * kD);
 #pragma unroll
       for (int i = 0; i < 4; ++i) c4[i] = src[4 * p + i];
@@ -278,13 +367,81 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const uint16_t* __rest
 
   // Padded query rows of this kv head's 8 query heads are exact zeros.
   if (ell >= u && ell < len) {
-    uint4* dst = reinterpret_cast<uint4*>(out + (t * kH + (size_t)g * kHpg) * kD);
+    constexpr int kVecPerThread = F16 ? 64 : 32;  // a token's 8 rows: 4 KiB FP32 or 2 KiB bf16
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(outp) + (t * kH + (size_t)g * kHpg) * kD * (F16 ? 4 : 2));
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll 4
-    for (int i = 0; i < 32; ++i) dst[p * 32 + i] = z;
+    for (int i = 0; i < kVecPerThread; ++i) dst[p * kVecPerThread + i] = z;
     if (lse && p < 2)  // an empty softmax: log 0
       *reinterpret_cast<float4*>(lse + t * kH + g * kHpg + 4 * p) =
           make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  }
+}
+
+// ----------------------------------------------------------------- FP16 query prep
+
+// The FP16 attention-compute variant's query rows: RMSNorm, RoPE and the
+// softmax scale in log2 units on the FP32 projection, one fp16 rounding, into
+// q16 [T][32][128] (the layout the attention kernel reads raw bf16 rows from).
+// Per (64-token tile, kv head): thread (token r, quarter p) forms channels
+// [16p, 16p+16) and their RoPE partners +64 of the kv head's 8 query heads.
+// Padded rows are not written; the attention kernel never reads them.
+__global__ __launch_bounds__(256) void q16_prep_kernel(const float* __restrict__ q,
+                                                       const float* __restrict__ q_norm_w,
+                                                       const int* __restrict__ positions,
+                                                       float eps, int use_rope, Ws ws,
+                                                       uint16_t* __restrict__ q16) {
+  const int e = blockIdx.x, g = blockIdx.y;
+  if (e >= ws.hdr[1]) return;
+  const int2 te = ws.tiles[e];
+  const int4 meta = ws.seq[te.x];
+  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
+  const int ell = te.y * kBN + r;
+  if (ell >= meta.z) return;  // padding; the shuffles below stay within valid quads
+  const size_t t = (size_t)meta.x + ell;
+  float cs[16], sn[16];
+  if (use_rope) {
+    const int pos = positions ? positions[t] : ell;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rope_cos_sin(pos, ws.rope_r[16 * p + i], &cs[i], &sn[i]);
+  }
+  const float scale = kLog2e * 0.08838834764831845f;
+  for (int hl = 0; hl < kHpg; ++hl) {
+    const size_t row = (t * kH + g * kHpg + hl) * kD;
+    const float4* src = reinterpret_cast<const float4*>(q + row);
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 a = src[4 * p + i], b = src[16 + 4 * p + i];
+      x[4 * i] = a.x; x[4 * i + 1] = a.y; x[4 * i + 2] = a.z; x[4 * i + 3] = a.w;
+      x[16 + 4 * i] = b.x; x[16 + 4 * i + 1] = b.y; x[16 + 4 * i + 2] = b.z; x[16 + 4 * i + 3] = b.w;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ss += x[i] * x[i];
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[i] *= rstd * q_norm_w[16 * p + i];
+      x[16 + i] *= rstd * q_norm_w[64 + 16 * p + i];
+    }
+    if (use_rope) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float a = x[i], b = x[16 + i];
+        x[i] = a * cs[i] - b * sn[i];
+        x[16 + i] = b * cs[i] + a * sn[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] *= scale;
+    uint4* dst = reinterpret_cast<uint4*>(q16 + row);
+    dst[2 * p] = pack8t<true>(x);
+    dst[2 * p + 1] = pack8t<true>(x + 8);
+    dst[8 + 2 * p] = pack8t<true>(x + 16);
+    dst[9 + 2 * p] = pack8t<true>(x + 24);
   }
 }
 
@@ -315,15 +472,26 @@ __device__ __forceinline__ void load_tile_async(__amdgpu_buffer_rsrc_t rsrc, int
 // the item's query rows; loads complete in issue order, so waiting for those
 // rows (n = the operations issued since: output stores, 8, the normalizer
 // store when it is written, 1, and the third slot's loads, 4) waits for the
-// slots as well.
+// slots as well. The FP32 output of the FP16 variant takes 16 stores (and
+// writes no normalizer).
+template <bool F16>
 __device__ __forceinline__ void ring_barrier(int n) {
-  switch (n) {
-    case 4: ring_barrier_n<4>(); break;
-    case 8: ring_barrier_n<8>(); break;
-    case 9: ring_barrier_n<9>(); break;
-    case 12: ring_barrier_n<12>(); break;
-    case 13: ring_barrier_n<13>(); break;
-    default: ring_barrier_n<0>(); break;
+  if constexpr (F16) {
+    switch (n) {
+      case 4: ring_barrier_n<4>(); break;
+      case 16: ring_barrier_n<16>(); break;
+      case 20: ring_barrier_n<20>(); break;
+      default: ring_barrier_n<0>(); break;
+    }
+  } else {
+    switch (n) {
+      case 4: ring_barrier_n<4>(); break;
+      case 8: ring_barrier_n<8>(); break;
+      case 9: ring_barrier_n<9>(); break;
+      case 12: ring_barrier_n<12>(); break;
+      case 13: ring_barrier_n<13>(); break;
+      default: ring_barrier_n<0>(); break;
+    }
   }
 }
 
@@ -339,6 +507,7 @@ struct RowState {
 // `load` is set, this wave's four direct-to-LDS loads of a later tile (byte
 // offset `loff`, into `lstage`) are spread over the MFMAs, one after every
 // fourth, so the loads of all waves do not reach the texture unit in one burst.
+template <bool F16>
 __device__ __forceinline__ void tile_logits(const uint4* kt, int lane, const bf16x8* qf,
                                             f32x16& s0, f32x16& s1, bool load,
                                             __amdgpu_buffer_rsrc_t rsrc, int voff, int loff,
@@ -356,11 +525,9 @@ __device__ __forceinline__ void tile_logits(const uint4* kt, int lane, const bf1
     }
     const int kk = i >> 1;
     if (i & 1) {
-      s1 = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[kk], f32x16{}, 0, 0, 0)
-                   : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[kk], s1, 0, 0, 0);
+      s1 = kk == 0 ? mma<F16>(f[i], qf[kk], f32x16{}) : mma<F16>(f[i], qf[kk], s1);
     } else {
-      s0 = kk == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[kk], f32x16{}, 0, 0, 0)
-                   : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[kk], s0, 0, 0, 0);
+      s0 = kk == 0 ? mma<F16>(f[i], qf[kk], f32x16{}) : mma<F16>(f[i], qf[kk], s0);
     }
     if (i + kFragAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // this MFMA
@@ -370,6 +537,7 @@ __device__ __forceinline__ void tile_logits(const uint4* kt, int lane, const bf1
 
 // Mask, (streaming path) running max, and P = exp2(S - m) as the bf16 B
 // operand of the PV product; the denominators sum the same rounded values.
+template <bool F16>
 __device__ __forceinline__ void tile_softmax(f32x16& s0, f32x16& s1, RowState& st, bf16x8* pk,
                                              int k0, int t0, int qrow, int u, int window, int half) {
   const bool need_mask =
@@ -417,26 +585,26 @@ __device__ __forceinline__ void tile_softmax(f32x16& s0, f32x16& s1, RowState& s
       for (int i = 0; i < 16; ++i) { s0[i] -= delta; s1[i] -= delta; }
     }
   }
-  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
   float p[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(s0[i]);
-  const uint4 w0 = pack8(p), w1 = pack8(p + 8);
+  const uint4 w0 = pack8t<F16>(p), w1 = pack8t<F16>(p + 8);
 #pragma unroll
   for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(s1[i]);
-  const uint4 w2 = pack8(p), w3 = pack8(p + 8);
+  const uint4 w2 = pack8t<F16>(p), w3 = pack8t<F16>(p + 8);
   pk[0] = __builtin_bit_cast(bf16x8, w0);
   pk[1] = __builtin_bit_cast(bf16x8, w1);
   pk[2] = __builtin_bit_cast(bf16x8, w2);
   pk[3] = __builtin_bit_cast(bf16x8, w3);
-  st.l0 = dot2_sum(w0, ones, st.l0);
-  st.l1 = dot2_sum(w1, ones, st.l1);
-  st.l0 = dot2_sum(w2, ones, st.l0);
-  st.l1 = dot2_sum(w3, ones, st.l1);
+  st.l0 = dot2_sumt<F16>(w0, st.l0);
+  st.l1 = dot2_sumt<F16>(w1, st.l1);
+  st.l0 = dot2_sumt<F16>(w2, st.l0);
+  st.l1 = dot2_sumt<F16>(w3, st.l1);
 }
 
 // O^T[d, query] += V^T[d, keys] P^T[keys, query]; fragments read
 // kFragAhead MFMAs ahead.
+template <bool F16>
 __device__ __forceinline__ void tile_pv(const uint4* vt, int lane, const bf16x8* pk, RowState& st) {
   bf16x8 f[16];
 #pragma unroll
@@ -447,7 +615,7 @@ __device__ __forceinline__ void tile_pv(const uint4* vt, int lane, const bf16x8*
     if (i + kFragAhead < 16)
       f[i + kFragAhead] = __builtin_bit_cast(bf16x8, vt[(i + kFragAhead) * 64 + lane]);
     const int db = i >> 2, kk = i & 3;
-    st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], pk[kk], st.acc[db], 0, 0, 0);
+    st.acc[db] = mma<F16>(f[i], pk[kk], st.acc[db]);
     if (i + kFragAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
@@ -521,10 +689,26 @@ __device__ __forceinline__ void load_q(const uint16_t* q, const int* positions, 
 
 // Query prologue: RMSNorm, RoPE, softmax scale in log2 units and one bf16
 // rounding, in the MFMA B-operand layout of Q^T; qmax = max |q'| over the
-// wave's 32 queries.
+// wave's 32 queries. With F16 the rows arrive prepared (q16_prep_kernel) and
+// only qmax is formed.
+template <bool F16>
 __device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw,
                                            const unsigned long long* s_rope, bool rope, float eps,
                                            int half, bf16x8* qf, float& qmax) {
+  if constexpr (F16) {
+    float n2 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qf[kk] = __builtin_bit_cast(bf16x8, qraw.x[kk]);
+      n2 += sumsq8t<true>(qraw.x[kk]);
+    }
+    n2 += __shfl_xor(n2, 32);
+    qmax = sqrtf(n2);
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+    qmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qmax)));
+    return;
+  }
   // The weight and frequency tables are re-read from LDS for every item; the
   // empty asm hides that the offset is zero, so the reads are not hoisted and
   // held in registers across the tile loop.
@@ -585,13 +769,21 @@ __device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw,
 // flow through a 4-stage LDS ring that does not stop at item boundaries: the
 // tile two slots ahead streams in meanwhile, and the next item's query rows
 // are fetched while the current item runs.
+//
+// F16 (the FP16 attention-compute variant): q holds the prepared fp16 rows,
+// the tiles are fp16, the products v_mfma_f32_32x32x16_f16, and `out` is FP32
+// holding the fp16-rounded output (the kernel-output boundary restored to
+// FP32). The unshifted path then needs every weight below fp16's largest
+// finite value, so its bound is 15 (log2 units) instead of kStaticBound.
+template <bool F16>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __restrict__ q,
                                                             const float* __restrict__ q_norm_w,
                                                             const float* __restrict__ sink,
                                                             const int* __restrict__ positions,
                                                             int window, int use_rope, float eps,
-                                                            Ws ws, uint16_t* __restrict__ out,
+                                                            Ws ws, void* __restrict__ outp,
                                                             float* __restrict__ lse) {
+  constexpr float kBound = F16 ? 15.0f : kStaticBound;
   __shared__ uint4 smem[kStages][kTileVec];
   __shared__ float s_qw[kD];                    // q_norm weights
   __shared__ unsigned long long s_rope[kD / 2];  // RoPE frequencies, 0.64 fixed point
@@ -676,13 +868,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   int endq = ops;  // `ops` after the current item's query loads
   bf16x8 qf[8];
   float qmax;
-  q_prologue(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
+  q_prologue<F16>(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
 
   for (int j = 0; j < nj; ++j) {
     // Softmax shift: none when the logit bound |q'| max|k'| and the sink stay
     // within kStaticBound; otherwise the streaming path.
     RowState st;
-    st.online = !(sk <= kStaticBound) || !(qmax * kmax * 1.0001f <= kStaticBound);
+    st.online = !(sk <= kBound) || !(qmax * kmax * 1.0001f <= kBound);
     st.m = st.online ? sk : 0.f;
     st.l0 = (half == 0 && sk != -INFINITY) ? __builtin_amdgcn_exp2f(sk - st.m) : 0.f;
     st.l1 = 0.f;
@@ -698,18 +890,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     f32x16 s0, s1;
     bf16x8 pk[4];
     for (int k = 0; k < it.ntiles; ++k, ++slot) {
-      if (group_b) ring_barrier(k < 2 ? ops - endq : ops - end0);
+      if (group_b) ring_barrier<F16>(k < 2 ? ops - endq : ops - end0);
       if (k > 0) {
-        tile_softmax(s0, s1, st, pk, (it.tile_lo + k - 1) * kBN, it.t0, qrow, it.u, window, half);
-        tile_pv(smem[(slot - 1) % kStages] + kTileVec / 2, lane, pk, st);
+        tile_softmax<F16>(s0, s1, st, pk, (it.tile_lo + k - 1) * kBN, it.t0, qrow, it.u, window, half);
+        tile_pv<F16>(smem[(slot - 1) % kStages] + kTileVec / 2, lane, pk, st);
       }
-      if (!group_b) ring_barrier(k < 2 ? ops - endq : ops - end0);  // slot is in LDS; stage (slot+2)%4 is free
+      if (!group_b) ring_barrier<F16>(k < 2 ? ops - endq : ops - end0);  // slot is in LDS; stage (slot+2)%4 is free
       bool ld;
       __amdgpu_buffer_rsrc_t r;
       int lo = 0;
       FLINT_NEXT_SLOT(ld, r, lo);
-      tile_logits(smem[slot % kStages], lane, qf, s0, s1, ld, r, voff, lo, smem[(slot + 2) % kStages],
-                  wave);
+      tile_logits<F16>(smem[slot % kStages], lane, qf, s0, s1, ld, r, voff, lo, smem[(slot + 2) % kStages],
+                       wave);
       end0 = end1;
       end1 = ops;
     }
@@ -723,8 +915,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
       ops += q_ops;
       endq = ops;
     }
-    tile_softmax(s0, s1, st, pk, (it.tile_lo + it.ntiles - 1) * kBN, it.t0, qrow, it.u, window, half);
-    tile_pv(smem[(slot - 1) % kStages] + kTileVec / 2, lane, pk, st);
+    tile_softmax<F16>(s0, s1, st, pk, (it.tile_lo + it.ntiles - 1) * kBN, it.t0, qrow, it.u, window, half);
+    tile_pv<F16>(smem[(slot - 1) % kStages] + kTileVec / 2, lane, pk, st);
     // Epilogue: O = acc / l in bf16. Lane (col, half) holds channels
     // 32db + 8rg + 4half + [0, 4) of query t0 + col; one swap with the
     // partner lane (col, 1 - half) gives it channels 32db + 16r2 + 8half +
@@ -739,8 +931,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
       for (int r2 = 0; r2 < 2; ++r2) {
         const f32x16& c = st.acc[db];
         const int o = 8 * r2;
-        const unsigned a0 = pack2(c[o] * inv, c[o + 1] * inv), a1 = pack2(c[o + 2] * inv, c[o + 3] * inv);
-        const unsigned b0 = pack2(c[o + 4] * inv, c[o + 5] * inv), b1 = pack2(c[o + 6] * inv, c[o + 7] * inv);
+        const unsigned a0 = pack2t<F16>(c[o] * inv, c[o + 1] * inv), a1 = pack2t<F16>(c[o + 2] * inv, c[o + 3] * inv);
+        const unsigned b0 = pack2t<F16>(c[o + 4] * inv, c[o + 5] * inv), b1 = pack2t<F16>(c[o + 6] * inv, c[o + 7] * inv);
         // lanes 32-63 of the first operand trade places with lanes 0-31 of the second
         const auto x0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
         const auto x1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
@@ -748,17 +940,37 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
       }
     // The next item's query prologue runs before this item's output stores,
     // so its query loads are the newest vector-memory operations it waits on.
-    if (more) q_prologue(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
+    if (more) q_prologue<F16>(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
     // Rows past the valid length fall outside the store range and are dropped.
+    constexpr int kOutElem = F16 ? 4 : 2;  // FP32 restored from fp16, or bf16
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-        out + ((size_t)(it.start + it.t0) * kH + h) * kD, 0, min(it.u - it.t0, kBM) * (kH * kD * 2),
-        kBufferWord3);
+        static_cast<char*>(outp) + ((size_t)(it.start + it.t0) * kH + h) * kD * kOutElem, 0,
+        min(it.u - it.t0, kBM) * (kH * kD * kOutElem), kBufferWord3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_buffer_store_b128(
-          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, ow[i]), orsrc,
-          col * (kH * kD * 2) + (32 * (i >> 1) + 16 * (i & 1) + 8 * half) * 2, 0, 0);
-    ops += 8;
+    for (int i = 0; i < 8; ++i) {
+      const int ob = col * (kH * kD * kOutElem) + (32 * (i >> 1) + 16 * (i & 1) + 8 * half) * kOutElem;
+      if constexpr (F16) {
+        const uint32_t w[4] = {ow[i].x, ow[i].y, ow[i].z, ow[i].w};
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f16x2_t hv = __builtin_bit_cast(f16x2_t, w[e]);
+          y[2 * e] = (float)hv[0];
+          y[2 * e + 1] = (float)hv[1];
+        }
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, f32x4_t{y[0], y[1], y[2], y[3]}), orsrc,
+            ob, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, f32x4_t{y[4], y[5], y[6], y[7]}), orsrc,
+            ob + 16, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, ow[i]), orsrc, ob, 0, 0);
+      }
+    }
+    ops += F16 ? 16 : 8;
     if (lse) {
       // natural-log normalizer of the row: (m + log2 l) ln 2 with m = 0 on the unshifted path
       const float m = st.online ? st.m : 0.f;
@@ -1201,7 +1413,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const float* q_
                     int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t window, int32_t use_rope,
                     float rope_theta, float eps, void* workspace, size_t workspace_bytes, void* out,
-                    float* lse, void* stream, int32_t phases) {
+                    float* lse, void* stream, int32_t phases, bool f16 = false) {
   if (phases <= 0 || (phases & ~FLINT_PHASE_ALL)) return FLINT_ERR_VALUE;
   if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return FLINT_ERR_SHAPE;
   if (num_q_heads != kH || num_kv_heads != kG || head_dim != kD) return FLINT_ERR_UNSUPPORTED;
@@ -1217,7 +1429,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const float* q_
       !aligned(sink, 4) || !aligned(cu_seqlens, 4) || (positions && !aligned(positions, 4)) ||
       (seqused && !aligned(seqused, 4)) || (lse && !aligned(lse, 16)))
     return FLINT_ERR_ALIGN;
-  const Layout L = make_layout(total_tokens, n_seqs);
+  const Layout L = make_layout(total_tokens, n_seqs, true, f16);
   if (workspace_bytes < L.total) return FLINT_ERR_WORKSPACE;
 
   const Ws ws = ws_at(workspace, L);
@@ -1234,12 +1446,26 @@ static int fwd_impl(const void* q, const void* k, const void* v, const float* q_
   if (phases & FLINT_PHASE_SCHEDULE)
     launch_schedule(cu_seqlens, seqused, n_seqs, total_tokens, max_seqlen, window,
                     (double)rope_theta, ws, st);
-  if (phases & FLINT_PHASE_KV)
-    kv_prologue_kernel<<<dim3((unsigned)L.ntmax, kG), 256, 0, st>>>(kh, vh, k_norm_w, pos, eps,
-                                                                    rope, ws, oh, lse);
-  if (phases & FLINT_PHASE_ATTEND)
-    attn_kernel<<<(unsigned)(attn_groups(L.nqmax) * kG), kAttnThreads, 0, st>>>(
-        qh, q_norm_w, sink, pos, window, rope, eps, ws, oh, lse);
+  uint16_t* q16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.q16);
+  const dim3 kv_grid((unsigned)L.ntmax, kG);
+  if (phases & FLINT_PHASE_KV) {
+    if (f16) {
+      kv_prologue_kernel<true><<<kv_grid, 256, 0, st>>>(k, v, k_norm_w, pos, eps, rope, ws, out, lse);
+      q16_prep_kernel<<<kv_grid, 256, 0, st>>>(static_cast<const float*>(q), q_norm_w, pos, eps,
+                                               rope, ws, q16);
+    } else {
+      kv_prologue_kernel<false><<<kv_grid, 256, 0, st>>>(kh, vh, k_norm_w, pos, eps, rope, ws, oh, lse);
+    }
+  }
+  if (phases & FLINT_PHASE_ATTEND) {
+    const unsigned grid = (unsigned)(attn_groups(L.nqmax) * kG);
+    if (f16)
+      attn_kernel<true><<<grid, kAttnThreads, 0, st>>>(q16, q_norm_w, sink, pos, window, rope, eps,
+                                                       ws, out, nullptr);
+    else
+      attn_kernel<false><<<grid, kAttnThreads, 0, st>>>(qh, q_norm_w, sink, pos, window, rope, eps,
+                                                        ws, oh, lse);
+  }
   if (hipGetLastError() != hipSuccess) return FLINT_ERR_HIP;
   if (debug_sync()) {
     int32_t flags = 0;
@@ -1274,6 +1500,28 @@ extern "C" int flint_attn_fwd_lse(const void* q, const void* k, const void* v,
   return fwd_impl(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused, n_seqs,
                   max_seqlen, total_tokens, num_q_heads, num_kv_heads, head_dim, window, use_rope,
                   rope_theta, eps, workspace, workspace_bytes, out, lse, stream, FLINT_PHASE_ALL);
+}
+
+extern "C" size_t flint_attn_f16_workspace_bytes(int32_t total_tokens, int32_t n_seqs,
+                                                 int32_t max_seqlen, int32_t num_kv_heads,
+                                                 int32_t head_dim) {
+  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return 0;
+  if (num_kv_heads != kG || head_dim != kD) return 0;
+  return make_layout(total_tokens, n_seqs, true, true).total;
+}
+
+extern "C" int flint_attn_fwd_f16(const float* q, const float* k, const float* v,
+                                  const float* q_norm_w, const float* k_norm_w, const float* sink,
+                                  const int32_t* positions, const int32_t* cu_seqlens,
+                                  const int32_t* seqused, int32_t n_seqs, int32_t max_seqlen,
+                                  int32_t total_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t window, int32_t use_rope,
+                                  float rope_theta, float eps, void* workspace,
+                                  size_t workspace_bytes, float* out, void* stream) {
+  return fwd_impl(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused, n_seqs,
+                  max_seqlen, total_tokens, num_q_heads, num_kv_heads, head_dim, window, use_rope,
+                  rope_theta, eps, workspace, workspace_bytes, out, nullptr, stream, FLINT_PHASE_ALL,
+                  true);
 }
 
 extern "C" int flint_attn_fwd(const void* q, const void* k, const void* v, const float* q_norm_w,

@@ -59,14 +59,15 @@ struct Ws {
 };
 
 struct Layout {
-  size_t hdr, rope_r, seq, tbase, qbase, tiles, items, kv, total;
+  size_t hdr, rope_r, seq, tbase, qbase, tiles, items, kv, q16, total;
   int64_t ntmax, nqmax;
 };
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace regions of the forward; the key-tile region only `with_kv`.
-static inline Layout make_layout(int64_t T, int64_t n, bool with_kv = true) {
+// Workspace regions of the forward; the key-tile region only `with_kv`, the
+// fp16 query rows of the FP16 variant only `with_q16`.
+static inline Layout make_layout(int64_t T, int64_t n, bool with_kv = true, bool with_q16 = false) {
   Layout L;
   L.ntmax = (T + kBN - 1) / kBN + n;
   L.nqmax = (T + kBM - 1) / kBM + n;
@@ -80,6 +81,8 @@ static inline Layout make_layout(int64_t T, int64_t n, bool with_kv = true) {
   L.items = o; o = align_up(o + (size_t)L.nqmax * sizeof(int2), 256);
   L.kv = o;
   if (with_kv) o = align_up(o + (size_t)kG * (size_t)L.ntmax * kTileBytes, 256);
+  L.q16 = o;
+  if (with_q16) o = align_up(o + (size_t)T * kH * kD * 2, 256);
   L.total = o;
   return L;
 }

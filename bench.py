@@ -13,6 +13,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config tstar|c1|c2
        python bench.py --decode [--decode-batch B] [--decode-len L] [--decode-window W]
                                          (one decode step per sequence over an L-token
                                           KV cache: HBM GB/s against 8 TB/s)
+       python bench.py --backward [--config ...]   (one flint_attn_bwd call per step)
+       python bench.py --fp16 [--config ...]       (the FP16 attention-compute variant)
        python bench.py --copy-probe     (plain device copy of known size, for
                                           calibrating FETCH_SIZE / WRITE_SIZE)
 Prints one JSON line.
@@ -309,6 +311,80 @@ def backward_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def fp16_bench(args):
+    """The FP16 attention-compute variant: FP32 projections in, fp16 products,
+    FP32 output. One step = one flint_attn_fwd_f16 call (schedule, K/V and
+    query preparation, attention kernel); FLOPs counted as for the bf16 path."""
+    import torch
+
+    import attention_head_rmsnorm_amd as fa
+    from workload import make_workload
+
+    cfg = args.config
+    li = 0
+    if cfg == "c4full":
+        cfg, li = "c4", 1
+    wl = make_workload(cfg)
+    layer = wl.layers[li]
+    dev = torch.device("cuda", 0)
+    fa.load_library()
+    q, k, v = wl.q.float().to(dev), wl.k.float().to(dev), wl.v.float().to(dev)
+    qw, kw, sk = wl.q_norm_w.to(dev), wl.k_norm_w.to(dev), wl.sinks.to(dev)
+    cu = wl.cu_seqlens.to(dev)
+    su = None if wl.seqused is None else wl.seqused.to(dev)
+    pos = None if wl.positions is None else wl.positions.to(dev)
+    T, n, mx = wl.total_tokens, wl.n_seqs, wl.max_seqlen
+    out = torch.empty_like(q)
+    nbytes = fa.flint_attn_f16_workspace_bytes(T, n, mx)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    p = lambda t: 0 if t is None else int(t.data_ptr())  # noqa: E731
+    call = [p(q), p(k), p(v), p(qw), p(kw), p(sk), p(pos), p(cu), p(su), n, mx, T, 32, 4, 128,
+            layer.window, int(layer.use_rope), layer.theta, layer.eps, p(ws), nbytes, p(out),
+            int(stream.cuda_stream)]
+    for _ in range(args.warmup):
+        st = fa.flint_attn_fwd_f16(*call)
+        if st != 0:
+            raise RuntimeError(fa.flint_attn_strerror(st))
+    torch.cuda.synchronize()
+    st, flags = fa.flint_attn_device_status(p(ws), int(stream.cuda_stream))
+    if st != 0:
+        raise RuntimeError(f"device data error flags {flags}")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        fa.flint_attn_fwd_f16(*call)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+    pairs = unmasked_pairs(wl.cu_seqlens.numpy(), None if wl.seqused is None else wl.seqused.numpy(),
+                           layer.window)
+    flops = 16384.0 * pairs
+    value = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "sink-attention prefill TFLOP/s (unmasked FLOPs), FP16 attention compute, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) FP32 q/k/v, N(1,0.1) norm weights, N(0,1) sinks)",
+        "config": {"workload": wl.description, "name": wl.name, "layer": layer.name,
+                   "total_tokens": T, "n_seqs": n, "window": layer.window,
+                   "use_rope": layer.use_rope},
+        "pct_f16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
+        "unmasked_flops": flops,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -320,6 +396,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--fp16", action="store_true")
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--decode-len", type=int, default=8192)
     ap.add_argument("--decode-window", type=int, default=0)
@@ -340,6 +417,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.fp16:
+        fp16_bench(args)
         return
 
     import attention_head_rmsnorm_amd as fa

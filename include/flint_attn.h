@@ -240,6 +240,34 @@ int flint_attn_decode(const void* q, const void* k, const void* v, const float* 
                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * FP16 attention-compute variant ([flint page] Numerical comparison:
+ * attention_compute_dtype = fp16 casts the normalized, rotated Q/K/V to FP16
+ * at the attention boundary and restores FP32 before the output projection;
+ * the projections stay FP32).
+ *
+ * q [T][32][128], k and v [T][4][128] are FP32 (the projections); RMSNorm and
+ * RoPE run in FP32, q', k' and v are rounded to fp16 once, the products run on
+ * fp16 MFMA with FP32 accumulation, and out [T][32][128] is FP32 holding the
+ * fp16-rounded output (0 on padded rows). Everything else - flags, sequence
+ * description, errors, asynchrony - is as for flint_attn_fwd. Meant for
+ * comparison and inference: the pages note fp16 underflow of tiny gradients
+ * without loss scaling, so the training path stays bf16.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace size in bytes for flint_attn_fwd_f16 (it adds the fp16 query
+ * rows, 8 KiB per token, to flint_attn_workspace_bytes). */
+size_t flint_attn_f16_workspace_bytes(int32_t total_tokens, int32_t n_seqs, int32_t max_seqlen,
+                                      int32_t num_kv_heads, int32_t head_dim);
+
+int flint_attn_fwd_f16(const float* q, const float* k, const float* v, const float* q_norm_w,
+                       const float* k_norm_w, const float* sink, const int32_t* positions,
+                       const int32_t* cu_seqlens, const int32_t* seqused, int32_t n_seqs,
+                       int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t window, int32_t use_rope,
+                       float rope_theta, float eps, void* workspace, size_t workspace_bytes,
+                       float* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * Training: forward with the row normalizer, and the backward.
  *
  * The backward is what the pages' training recipes need (Hugging Face

@@ -50,7 +50,7 @@ def valid_rows(wl):
     return ell < i64(wl.seqused)[s]
 
 
-def grade(got, ref, wl, rows=None, what=""):
+def grade(got, ref, wl, rows=None, what="", max_frac=MAX_ERR_FRAC, mean_frac=MEAN_ERR_FRAC):
     """Asserts the tolerance on valid rows and exact zeros on padded rows.
 
     got, ref: [len(rows), 32, 128] (rows=None: every token). Returns stats.
@@ -66,8 +66,8 @@ def grade(got, ref, wl, rows=None, what=""):
     stats = dict(max_err=max_err, mean_err=mean_err, vmax=vmax,
                  max_frac=max_err / vmax, mean_frac=mean_err / vmax, rows=int(ok.sum()))
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
-    assert max_err <= MAX_ERR_FRAC * vmax, f"{what}: max err {max_err:.4g} > {MAX_ERR_FRAC}*{vmax:.4g}"
-    assert mean_err <= MEAN_ERR_FRAC * vmax, f"{what}: mean err {mean_err:.4g} > {MEAN_ERR_FRAC}*{vmax:.4g}"
+    assert max_err <= max_frac * vmax, f"{what}: max err {max_err:.4g} > {max_frac}*{vmax:.4g}"
+    assert mean_err <= mean_frac * vmax, f"{what}: mean err {mean_err:.4g} > {mean_frac}*{vmax:.4g}"
     if (~ok).any():
         assert np.all(g[~ok] == 0.0), f"{what}: padded rows are not exact zeros"
     return stats

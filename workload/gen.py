@@ -193,14 +193,16 @@ def make_workload(name: str) -> Workload:
 
 def make_custom(seed: int, lengths: Sequence[int], *, layout: str = "thd", seqused=None,
                 layers=(SLIDING,), sink_std: float = 1.0, positions: str = "local",
-                q_scale: float = 1.0, norm_scale: float = 1.0) -> Workload:
+                q_scale: float = 1.0, norm_scale: float = 1.0, dtype: str = "bf16") -> Workload:
     """A small seeded workload for tests.
 
     ``lengths`` are sequence lengths (BSHD needs equal lengths). ``seqused``
     gives trailing-padding valid lengths. ``positions`` is "local" (index in the
     sequence, passed explicitly), "none" (argument left out) or "random"
     (arbitrary non-negative integers). ``norm_scale`` multiplies both RMSNorm
-    weights (large weights give large logits).
+    weights (large weights give large logits). ``dtype`` "float32" keeps q, k, v
+    as the float32 draws (the FP32 projections the FP16 attention-compute
+    variant takes) instead of rounding them to bfloat16.
     """
     rng = np.random.default_rng(seed)
     lengths = [int(x) for x in lengths]
@@ -224,8 +226,9 @@ def make_custom(seed: int, lengths: Sequence[int], *, layout: str = "thd", sequs
     su = None if seqused is None else torch.tensor(list(seqused), dtype=torch.int32)
     B = len(lengths) if layout == "bshd" else 0
     S = lengths[0] if layout == "bshd" and lengths else 0
-    return Workload(name=f"custom{seed}", seed=seed, layout=layout, q=_bf16(q), k=_bf16(k),
-                    v=_bf16(v), q_norm_w=qw, k_norm_w=kw, sinks=sinks,
+    cast = _bf16 if dtype == "bf16" else (lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)))
+    return Workload(name=f"custom{seed}", seed=seed, layout=layout, q=cast(q), k=cast(k),
+                    v=cast(v), q_norm_w=qw, k_norm_w=kw, sinks=sinks,
                     cu_seqlens=torch.from_numpy(cu.astype(np.int32)), seqused=su, positions=pos,
                     layers=list(layers), batch=B, seqlen=S)
 
