@@ -14,3 +14,4 @@ from .flint_oracle import (  # noqa: F401
     sink_softmax,
 )
 from .flint_oracle_bwd import flint_attention_backward  # noqa: F401,E402
+from .flint_oracle_bshd import flint_attention_bshd  # noqa: F401,E402

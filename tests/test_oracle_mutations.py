@@ -197,3 +197,88 @@ def test_backward_mutation_is_caught(name, monkeypatch):
             caught.append(pin.__name__)
             break
     assert caught, f"no backward pin caught the planted mistake '{name}'"
+
+
+# ----------------------------------------------------------------- BSHD documents and padding
+
+import oracle.flint_oracle_bshd as fd  # noqa: E402
+
+from . import oracle_bshd_pins  # noqa: E402
+
+_doc_structure = fd.document_structure
+_doc_allowed = fd._allowed
+
+
+def _allowed_window_in_columns(rank, doc, window):
+    cols = np.where(rank >= 0, np.arange(len(rank)), -1)
+    ok = _doc_allowed(rank, doc, 0)
+    if window > 0:
+        ok &= (cols[:, None] - cols[None, :]) <= (window - 1)
+    return ok
+
+
+def _allowed_window_off_by_one(rank, doc, window):
+    return _doc_allowed(rank, doc, window + 1 if window > 0 else 0)
+
+
+def _allowed_not_causal(rank, doc, window):
+    ok = _doc_allowed(rank, doc, 0) | _doc_allowed(rank, doc, 0).T
+    if window > 0:
+        ok &= np.abs(rank[:, None] - rank[None, :]) <= (window - 1)
+    return ok
+
+
+def _docs_by_id(valid, ids):
+    rank, doc, local = _doc_structure(valid, ids)
+    doc = np.where(doc >= 0, np.asarray(ids, np.int64), -1)
+    for s in range(len(valid)):
+        if doc[s] >= 0:
+            local[s] = int(np.sum(doc[:s] == doc[s]))
+    return rank, doc, local
+
+
+def _positions_are_columns(valid, ids):
+    # (counting from the row's first valid token instead of the document's is
+    # no mistake: RoPE logits see position differences only)
+    rank, doc, _ = _doc_structure(valid, ids)
+    return rank, doc, np.where(rank >= 0, np.arange(len(rank)), -1)
+
+
+def _padding_splits_documents(valid, ids):
+    S = len(valid)
+    rank, doc, local = _doc_structure(valid, ids)
+    d = -1
+    start = 0
+    for s in range(S):
+        if not valid[s]:
+            continue
+        if s == 0 or not valid[s - 1] or ids[s] != ids[s - 1]:
+            d += 1
+            start = rank[s]
+        doc[s] = d
+        local[s] = rank[s] - start
+    return rank, doc, local
+
+
+BSHD_MUTATIONS = {
+    "window counts columns": ("_allowed", _allowed_window_in_columns),
+    "window off by one": ("_allowed", _allowed_window_off_by_one),
+    "not causal": ("_allowed", _allowed_not_causal),
+    "documents by id equality": ("document_structure", _docs_by_id),
+    "default positions are row columns": ("document_structure", _positions_are_columns),
+    "padding splits a document": ("document_structure", _padding_splits_documents),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BSHD_MUTATIONS))
+def test_bshd_mutation_is_caught(name, monkeypatch):
+    attr, bad = BSHD_MUTATIONS[name]
+    monkeypatch.setattr(fd, attr, bad)
+    caught = []
+    for pin in oracle_bshd_pins.ALL_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no BSHD pin caught the planted mistake '{name}'"
