@@ -54,6 +54,9 @@ EXPORTED = (
     "flint_attn_bwd",
     "flint_attn_f16_workspace_bytes",
     "flint_attn_fwd_f16",
+    "flint_attn_bshd_plan_bytes",
+    "flint_attn_bshd_plan",
+    "flint_attn_copy_rows",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -112,6 +115,12 @@ def load_library() -> ctypes.CDLL:
     lib.flint_attn_f16_workspace_bytes.restype = sz
     lib.flint_attn_fwd_f16.argtypes = lib.flint_attn_fwd.argtypes
     lib.flint_attn_fwd_f16.restype = ctypes.c_int
+    lib.flint_attn_bshd_plan_bytes.argtypes = [i32, i32]
+    lib.flint_attn_bshd_plan_bytes.restype = sz
+    lib.flint_attn_bshd_plan.argtypes = [vp, vp, i32, i32, vp, sz, vp]
+    lib.flint_attn_bshd_plan.restype = ctypes.c_int
+    lib.flint_attn_copy_rows.argtypes = [vp, vp, i32, i32, ctypes.c_uint32, vp, vp]
+    lib.flint_attn_copy_rows.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -177,6 +186,23 @@ def flint_attn_fwd_f16(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens,
                                                  total_tokens, num_q_heads, num_kv_heads,
                                                  head_dim, window, use_rope, rope_theta, eps,
                                                  workspace, workspace_bytes, out, stream))
+
+
+def flint_attn_bshd_plan_bytes(batch: int, seqlen: int) -> int:
+    return int(load_library().flint_attn_bshd_plan_bytes(batch, seqlen))
+
+
+def flint_attn_bshd_plan(attention_mask, document_ids, batch, seqlen, plan, plan_bytes,
+                         stream) -> int:
+    """THD description of BSHD input with a mask and/or document ids; returns the status."""
+    return int(load_library().flint_attn_bshd_plan(attention_mask, document_ids, batch, seqlen,
+                                                   plan, plan_bytes, stream))
+
+
+def flint_attn_copy_rows(src, index, n_rows, row_bytes, fill, dst, stream) -> int:
+    """dst row r = src row index[r] (fill words where index[r] < 0); returns the status."""
+    return int(load_library().flint_attn_copy_rows(src, index, n_rows, row_bytes, fill, dst,
+                                                   stream))
 
 
 def flint_attn_bwd_workspace_bytes(total_tokens: int, n_seqs: int, max_seqlen: int,
@@ -277,9 +303,86 @@ def seqused_from_mask(attention_mask):
     return seqused
 
 
+class _Args:
+    """The THD description of a call: T tokens in n sequences (cu, seqused,
+    positions); for packed BSHD input also `pack` (source row of each stream
+    token) and `unpack` (stream token of each source row, -1 on padding)."""
+
+    def __init__(self, T, n, mx, cu, seqused, positions, pack=None, unpack=None):
+        self.T, self.n, self.mx = T, n, mx
+        self.cu, self.seqused, self.positions = cu, seqused, positions
+        self.pack, self.unpack = pack, unpack
+
+    def gather(self, t):
+        """Rows of t (leading dims flattened) in stream order (t itself when not packed)."""
+        import torch
+
+        if self.pack is None:
+            return t
+        rows = t.reshape(self.unpack.numel(), -1)
+        dst = torch.empty((self.T,) + tuple(t.shape[2:]), dtype=t.dtype, device=t.device)
+        _copy_rows(rows, self.pack, self.T, dst)
+        return dst
+
+    def scatter(self, packed, out, fill=0):
+        """Stream-order rows back to out's rows, `fill` (a 32-bit word) on padding."""
+        if self.pack is not None:
+            _copy_rows(packed.reshape(self.T, -1), self.unpack, self.unpack.numel(), out, fill)
+        return out
+
+
+def _copy_rows(src, index, n_rows, dst, fill=0):
+    """dst (n_rows rows) row r = src row index[r], `fill` words where index[r] < 0."""
+    if n_rows == 0:
+        return
+    row_bytes = dst.numel() * dst.element_size() // n_rows
+    st = flint_attn_copy_rows(_ptr(src), _ptr(index), n_rows, row_bytes, fill, _ptr(dst),
+                              _stream_handle(dst.device))
+    if st != FLINT_OK:
+        raise FlintError(st, "flint_attn_copy_rows")
+
+
+def bshd_plan(attention_mask, document_ids, batch: int, seqlen: int, device):
+    """Runs the plan kernel and reads its counts (one host synchronization).
+
+    Returns (info, cu, seqused, pack, unpack): info = (n_seqs, max_seqlen,
+    total_tokens, packed, valid tokens, documents); the rest are views of the
+    plan on the device."""
+    import torch
+
+    m = None
+    if attention_mask is not None:
+        if tuple(attention_mask.shape) != (batch, seqlen):
+            raise ValueError("attention_mask must be [batch, seqlen]")
+        m = attention_mask if attention_mask.dtype == torch.uint8 else (attention_mask != 0).to(torch.uint8)
+        m = m.contiguous()
+    d = None
+    if document_ids is not None:
+        if tuple(document_ids.shape) != (batch, seqlen):
+            raise ValueError("document_ids must be [batch, seqlen]")
+        d = document_ids.to(torch.int32).contiguous()
+    N = batch * seqlen
+    nbytes = flint_attn_bshd_plan_bytes(batch, seqlen)
+    plan = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
+    st = flint_attn_bshd_plan(_ptr(m), _ptr(d), batch, seqlen, _ptr(plan), nbytes,
+                              _stream_handle(device))
+    if st != FLINT_OK:
+        raise FlintError(st, "flint_attn_bshd_plan")
+    info = tuple(int(x) for x in plan[:8].cpu())
+    n = info[0]
+    cu = plan[8:8 + n + 1]
+    seqused = plan[9 + N:9 + N + n]
+    pack = plan[9 + 2 * N:9 + 2 * N + info[2]] if info[3] else None
+    unpack = plan[9 + 3 * N:9 + 4 * N] if info[3] else None
+    return info, cu, seqused, pack, unpack
+
+
+_NEG_INF_BITS = 0xFF800000  # float32 -inf as a 32-bit word
+
+
 def _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, attention_mask,
-                seqused, max_seqlen, dtype=None):
-    """Checks the layer's tensors; returns (T, n, max_seqlen, cu, seqused, positions)."""
+                seqused, max_seqlen, dtype=None, document_ids=None) -> _Args:
+    """Checks the layer's tensors; returns the call's THD description."""
     import torch
 
     if not q.is_cuda:
@@ -296,6 +399,7 @@ def _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, atten
     for name, t in (("q_norm_w", q_norm_w), ("k_norm_w", k_norm_w), ("sinks", sinks)):
         if t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev:
             raise TypeError(f"{name} must be a contiguous float32 tensor on {dev}")
+    pack = unpack = None
     if q.dim() == 4:
         B, S = q.shape[0], q.shape[1]
         T = B * S
@@ -304,16 +408,21 @@ def _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, atten
         cu = torch.arange(0, T + 1, max(S, 1), dtype=torch.int32, device=dev)[:B + 1]
         n = B
         mx = S
-        if attention_mask is not None:
+        if attention_mask is not None or document_ids is not None:
             if seqused is not None:
-                raise ValueError("pass attention_mask or seqused, not both")
-            if tuple(attention_mask.shape) != (B, S):
-                raise ValueError("attention_mask must be [batch, seqlen]")
-            seqused = seqused_from_mask(attention_mask)
+                raise ValueError("pass attention_mask / document_ids or seqused, not both")
+            info, cu, seqused, pack, unpack = bshd_plan(attention_mask, document_ids, B, S, dev)
+            n, mx, T = info[0], info[1], info[2]
+            if positions is not None and pack is not None:
+                if positions.dtype != torch.int32 or positions.numel() != B * S:
+                    raise TypeError("positions must be int32 [batch, seqlen] on the device")
+                pp = torch.empty(T, dtype=torch.int32, device=dev)
+                _copy_rows(positions.reshape(B * S, 1).contiguous(), pack, T, pp)
+                positions = pp
     elif q.dim() == 3:
         T = q.shape[0]
-        if attention_mask is not None:
-            raise ValueError("THD input takes cu_seqlens, not attention_mask")
+        if attention_mask is not None or document_ids is not None:
+            raise ValueError("THD input takes cu_seqlens, not attention_mask or document_ids")
         if cu_seqlens is None:
             cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
             mx = T
@@ -334,52 +443,58 @@ def _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, atten
         if positions.dtype != torch.int32 or positions.device != dev or positions.numel() != T:
             raise TypeError("positions must be int32 with one entry per token, on the device")
         positions = positions.contiguous()
-    return T, n, mx, cu, seqused, positions
+    return _Args(T, n, mx, cu, seqused, positions, pack, unpack)
 
 
 def flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens=None,
-               attention_mask=None, seqused=None, max_seqlen: Optional[int] = None,
-               window: int = 513, use_rope: bool = True, rope_theta: float = 1.0e6,
-               eps: float = 1.0e-6, out=None, workspace=None, return_lse: bool = False):
+               attention_mask=None, document_ids=None, seqused=None,
+               max_seqlen: Optional[int] = None, window: int = 513, use_rope: bool = True,
+               rope_theta: float = 1.0e6, eps: float = 1.0e-6, out=None, workspace=None,
+               return_lse: bool = False):
     """Sink-aware GQA attention forward on torch tensors.
 
     q: bf16 [B, S, 32, 128] (BSHD) or [T, 32, 128] (THD); k, v: bf16 with 4
     heads in the same layout. q_norm_w, k_norm_w: fp32 [128]; sinks: fp32 [32].
     THD takes ``cu_seqlens`` (int32 [n+1], device) and, optionally,
-    ``max_seqlen``; BSHD takes ``attention_mask`` [B, S] (trailing padding) or
-    ``seqused`` [B]. ``positions`` is int32 [B, S] or [T] (default: index in
-    the sequence). Returns the output in q's layout; with ``return_lse`` also
-    the per-row normalizer, float32 [..., 32] in natural-log units (what the
-    backward takes).
+    ``max_seqlen``; BSHD takes ``attention_mask`` [B, S] (any padding) and/or
+    ``document_ids`` [B, S] (documents = runs of equal id among the valid
+    tokens), or ``seqused`` [B]. ``positions`` is int32 [B, S] or [T] (default:
+    index in the sequence or document). Returns the output in q's layout; with
+    ``return_lse`` also the per-row normalizer, float32 [..., 32] in
+    natural-log units (what the backward takes; -inf on padding).
     """
     import torch
 
-    T, n, mx, cu, seqused, positions = _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions,
-                                                   cu_seqlens, attention_mask, seqused, max_seqlen)
+    a = _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, attention_mask,
+                    seqused, max_seqlen, document_ids=document_ids)
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
-    nbytes = flint_attn_workspace_bytes(T, n, mx, k.shape[-2], k.shape[-1])
-    if workspace is None:
+    qq, kk, vv = a.gather(q), a.gather(k), a.gather(v)
+    o = out if a.pack is None else torch.empty_like(qq)
+    nbytes = flint_attn_workspace_bytes(a.T, a.n, a.mx, k.shape[-2], k.shape[-1])
+    if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(sinks),
-            _ptr(positions), _ptr(cu), _ptr(seqused), n, mx, T, q.shape[-2], k.shape[-2],
-            q.shape[-1], int(window), int(bool(use_rope)), float(rope_theta), float(eps),
-            _ptr(workspace), workspace.numel(), _ptr(out))
+    args = (_ptr(qq), _ptr(kk), _ptr(vv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(sinks),
+            _ptr(a.positions), _ptr(a.cu), _ptr(a.seqused), a.n, a.mx, a.T, q.shape[-2],
+            k.shape[-2], q.shape[-1], int(window), int(bool(use_rope)), float(rope_theta),
+            float(eps), _ptr(workspace), workspace.numel(), _ptr(o))
     if not return_lse:
         st = flint_attn_fwd(*args, _stream_handle(dev))
         if st != FLINT_OK:
             raise FlintError(st, "flint_attn_fwd")
-        return out
+        return a.scatter(o, out)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
-    st = flint_attn_fwd_lse(*args, _ptr(lse), _stream_handle(dev))
+    ls = lse if a.pack is None else torch.empty((a.T, q.shape[-2]), dtype=torch.float32, device=dev)
+    st = flint_attn_fwd_lse(*args, _ptr(ls), _stream_handle(dev))
     if st != FLINT_OK:
         raise FlintError(st, "flint_attn_fwd_lse")
-    return out, lse
+    return a.scatter(o, out), a.scatter(ls, lse, fill=_NEG_INF_BITS)
 
 
 def flint_attn_f16(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens=None,
-                   attention_mask=None, seqused=None, max_seqlen: Optional[int] = None,
+                   attention_mask=None, document_ids=None, seqused=None,
+                   max_seqlen: Optional[int] = None,
                    window: int = 513, use_rope: bool = True, rope_theta: float = 1.0e6,
                    eps: float = 1.0e-6, out=None, workspace=None):
     """The FP16 attention-compute variant on torch tensors: q, k, v float32 (the
@@ -387,27 +502,28 @@ def flint_attn_f16(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seq
     the fp16-rounded attention result."""
     import torch
 
-    T, n, mx, cu, seqused, positions = _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions,
-                                                   cu_seqlens, attention_mask, seqused, max_seqlen,
-                                                   dtype=torch.float32)
+    a = _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, attention_mask,
+                    seqused, max_seqlen, dtype=torch.float32, document_ids=document_ids)
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
-    nbytes = flint_attn_f16_workspace_bytes(T, n, mx, k.shape[-2], k.shape[-1])
+    qq, kk, vv = a.gather(q), a.gather(k), a.gather(v)
+    o = out if a.pack is None else torch.empty_like(qq)
+    nbytes = flint_attn_f16_workspace_bytes(a.T, a.n, a.mx, k.shape[-2], k.shape[-1])
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    st = flint_attn_fwd_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(sinks),
-                            _ptr(positions), _ptr(cu), _ptr(seqused), n, mx, T, q.shape[-2],
-                            k.shape[-2], q.shape[-1], int(window), int(bool(use_rope)),
-                            float(rope_theta), float(eps), _ptr(workspace), workspace.numel(),
-                            _ptr(out), _stream_handle(dev))
+    st = flint_attn_fwd_f16(_ptr(qq), _ptr(kk), _ptr(vv), _ptr(q_norm_w), _ptr(k_norm_w),
+                            _ptr(sinks), _ptr(a.positions), _ptr(a.cu), _ptr(a.seqused), a.n,
+                            a.mx, a.T, q.shape[-2], k.shape[-2], q.shape[-1], int(window),
+                            int(bool(use_rope)), float(rope_theta), float(eps), _ptr(workspace),
+                            workspace.numel(), _ptr(o), _stream_handle(dev))
     if st != FLINT_OK:
         raise FlintError(st, "flint_attn_fwd_f16")
-    return out
+    return a.scatter(o, out)
 
 
 def flint_attn_backward(dout, q, k, v, q_norm_w, k_norm_w, sinks, out, lse, *, positions=None,
-                        cu_seqlens=None, attention_mask=None, seqused=None,
+                        cu_seqlens=None, attention_mask=None, document_ids=None, seqused=None,
                         max_seqlen: Optional[int] = None, window: int = 513,
                         use_rope: bool = True, rope_theta: float = 1.0e6, eps: float = 1.0e-6,
                         workspace=None):
@@ -419,8 +535,8 @@ def flint_attn_backward(dout, q, k, v, q_norm_w, k_norm_w, sinks, out, lse, *, p
     """
     import torch
 
-    T, n, mx, cu, seqused, positions = _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions,
-                                                   cu_seqlens, attention_mask, seqused, max_seqlen)
+    a = _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, attention_mask,
+                    seqused, max_seqlen, document_ids=document_ids)
     dev = q.device
     for name, t, dt in (("dout", dout, torch.bfloat16), ("out", out, torch.bfloat16),
                         ("lse", lse, torch.float32)):
@@ -428,23 +544,27 @@ def flint_attn_backward(dout, q, k, v, q_norm_w, k_norm_w, sinks, out, lse, *, p
             raise TypeError(f"{name} must be a contiguous {dt} tensor on {dev}")
     if dout.shape != q.shape or out.shape != q.shape or lse.shape != q.shape[:-1]:
         raise ValueError("dout and out must have q's shape and lse q's shape without head_dim")
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    qq, kk, vv = a.gather(q), a.gather(k), a.gather(v)
+    oo, ll, dd = a.gather(out), a.gather(lse), a.gather(dout)
+    dq, dk, dv = torch.empty_like(qq), torch.empty_like(kk), torch.empty_like(vv)
     dqw = torch.empty_like(q_norm_w)
     dkw = torch.empty_like(k_norm_w)
     dsk = torch.empty_like(sinks)
-    nbytes = flint_attn_bwd_workspace_bytes(T, n, mx, k.shape[-2], k.shape[-1])
+    nbytes = flint_attn_bwd_workspace_bytes(a.T, a.n, a.mx, k.shape[-2], k.shape[-1])
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    st = flint_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(sinks),
-                        _ptr(positions), _ptr(cu), _ptr(seqused), n, mx, T, q.shape[-2],
-                        k.shape[-2], q.shape[-1], int(window), int(bool(use_rope)),
-                        float(rope_theta), float(eps), _ptr(out), _ptr(lse), _ptr(dout),
-                        _ptr(workspace), workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv),
-                        _ptr(dqw), _ptr(dkw), _ptr(dsk), _stream_handle(dev))
+    st = flint_attn_bwd(_ptr(qq), _ptr(kk), _ptr(vv), _ptr(q_norm_w), _ptr(k_norm_w),
+                        _ptr(sinks), _ptr(a.positions), _ptr(a.cu), _ptr(a.seqused), a.n, a.mx,
+                        a.T, q.shape[-2], k.shape[-2], q.shape[-1], int(window),
+                        int(bool(use_rope)), float(rope_theta), float(eps), _ptr(oo), _ptr(ll),
+                        _ptr(dd), _ptr(workspace), workspace.numel(), _ptr(dq), _ptr(dk),
+                        _ptr(dv), _ptr(dqw), _ptr(dkw), _ptr(dsk), _stream_handle(dev))
     if st != FLINT_OK:
         raise FlintError(st, "flint_attn_bwd")
+    if a.pack is not None:
+        dq = a.scatter(dq, torch.empty_like(q))
+        dk = a.scatter(dk, torch.empty_like(k))
+        dv = a.scatter(dv, torch.empty_like(v))
     return dq, dk, dv, dqw, dkw, dsk
 
 

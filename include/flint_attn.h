@@ -240,6 +240,51 @@ int flint_attn_decode(const void* q, const void* k, const void* v, const float* 
                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * BSHD input with document ids and arbitrary padding ([layers page]
+ * FlintAttention.forward: attention_mask [B, S] marks valid tokens, padded
+ * queries and keys leave attention while the sink stays valid, arbitrary
+ * padding is THD packing; integer document_ids [B, S] give a block-diagonal
+ * mask). Documents are the maximal runs of equal id among a row's valid
+ * tokens; the window counts a document's valid tokens; default positions are
+ * the index in the document.
+ *
+ * flint_attn_bshd_plan turns the mask (uint8 [B][S], nonzero = valid, or NULL:
+ * all valid) and the ids (int32 [B][S], or NULL: one document per row) into a
+ * THD description, written to `plan`, an int32 array of
+ * flint_attn_bshd_plan_bytes(B, S) bytes with N = B*S:
+ *   info     [8]   at 0        n_seqs, max_seqlen, total_tokens, packed,
+ *                              valid tokens, documents, 0, 0
+ *   cu       [N+1] at 8        cu_seqlens, n_seqs + 1 entries used
+ *   seqused  [N]   at 9+N      valid length of each sequence
+ *   pack     [N]   at 9+2N     packed mode: source token (b*S+s) of each stream token
+ *   unpack   [N]   at 9+3N     stream token of each source token, -1 on padding
+ *   scratch  [2N+2]
+ * packed = 0: the B*S tokens in memory are the THD stream (no document has a
+ * padded token inside it): pass q, k, v, positions and out as they are, with
+ * total_tokens = N. packed = 1: the stream is the valid tokens in order; gather
+ * q, k, v (and positions) with flint_attn_copy_rows(src, pack, total_tokens,
+ * ...), run the layer, and scatter the output with
+ * flint_attn_copy_rows(packed_out, unpack, N, ..., fill 0, out).
+ * The plan is device data: read info after the stream has reached it.
+ * Asynchronous on `stream`; errors as for flint_attn_fwd (host checks only:
+ * every mask and id array is valid input). N must be below 2^30.
+ * ------------------------------------------------------------------------ */
+
+size_t flint_attn_bshd_plan_bytes(int32_t batch, int32_t seqlen);
+
+int flint_attn_bshd_plan(const uint8_t* attention_mask, const int32_t* document_ids,
+                         int32_t batch, int32_t seqlen, void* plan, size_t plan_bytes,
+                         void* stream);
+
+/* dst row r = src row index[r] for r in [0, n_rows), or rows of the 32-bit
+ * word `fill` where index[r] < 0. row_bytes is a multiple of 4 (16-byte
+ * vectors when it is a multiple of 16 and both pointers are 16-byte aligned).
+ * Device pointers; index entries must name rows that exist in src (the
+ * caller's contract, not checked). Asynchronous on `stream`. */
+int flint_attn_copy_rows(const void* src, const int32_t* index, int32_t n_rows, int32_t row_bytes,
+                         uint32_t fill, void* dst, void* stream);
+
+/* ------------------------------------------------------------------------
  * FP16 attention-compute variant ([flint page] Numerical comparison:
  * attention_compute_dtype = fp16 casts the normalized, rotated Q/K/V to FP16
  * at the attention boundary and restores FP32 before the output projection;
