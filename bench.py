@@ -15,6 +15,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config tstar|c1|c2
                                           KV cache: HBM GB/s against 8 TB/s)
        python bench.py --backward [--config ...]   (one flint_attn_bwd call per step)
        python bench.py --fp16 [--config ...]       (the FP16 attention-compute variant)
+       python bench.py --bshd-docs                 (BSHD rows of packed documents, in place and with holes)
        python bench.py --copy-probe     (plain device copy of known size, for
                                           calibrating FETCH_SIZE / WRITE_SIZE)
 Prints one JSON line.
@@ -385,6 +386,111 @@ def fp16_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def bshd_docs_bench(args):
+    """BSHD rows of packed documents on a sliding layer (513, RoPE): B=8 rows of
+    S=8192 tokens, document lengths log-uniform in [64, 8192] (a packed
+    long-context batch), and the same rows with 2% of the tokens masked out
+    inside documents. One step = the plan kernel, then the attention call
+    (in place), or plan + gather of q, k, v + attention + scatter of the output
+    (holes). The plan's counts are read once before timing, as a training loop
+    reads them once per batch."""
+    import torch
+
+    import attention_head_rmsnorm_amd as fa
+    from workload import make_custom
+    from workload.gen import SLIDING
+
+    B, S = 8, 8192
+    rng = np.random.default_rng(2024)
+    ids = np.zeros((B, S), np.int32)
+    for b in range(B):
+        lens, left = [], S
+        while left > 0:
+            n = int(min(left, np.exp(rng.uniform(np.log(64), np.log(S)))))
+            lens.append(n)
+            left -= n
+        ids[b] = np.repeat(np.arange(len(lens)), lens)
+    holes = np.ones((B, S), np.uint8)
+    holes[rng.random((B, S)) < 0.02] = 0
+    wl = make_custom(2024, [S] * B, layout="bshd")
+    layer = SLIDING
+    dev = torch.device("cuda", 0)
+    fa.load_library()
+    q = wl.q.to(dev).view(B, S, 32, 128)
+    k = wl.k.to(dev).view(B, S, 4, 128)
+    v = wl.v.to(dev).view(B, S, 4, 128)
+    qw, kw, sk = wl.q_norm_w.to(dev), wl.k_norm_w.to(dev), wl.sinks.to(dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+    p = lambda t: 0 if t is None else int(t.data_ptr())  # noqa: E731
+    ids_t = torch.from_numpy(ids).to(dev)
+    recs = {}
+    for name, mask in (("in_place", None), ("holes_2pct", holes)):
+        m_t = None if mask is None else torch.from_numpy(mask).to(dev)
+        info, cu, su, pack, unpack = fa.bshd_plan(m_t, ids_t, B, S, dev)
+        n, mx, T, packed = info[:4]
+        nbytes = fa.flint_attn_bshd_plan_bytes(B, S)
+        plan = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+        wsb = fa.flint_attn_workspace_bytes(T, n, mx)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        # the plan the timed steps rewrite holds the same description as `cu`, `su`
+        pcu = plan[8:8 + n + 1]
+        psu = plan[9 + B * S:9 + B * S + n]
+        ppk = plan[9 + 2 * B * S:]
+        pup = plan[9 + 3 * B * S:]
+        qq = torch.empty((T, 32, 128), dtype=torch.bfloat16, device=dev) if packed else q
+        kk = torch.empty((T, 4, 128), dtype=torch.bfloat16, device=dev) if packed else k
+        vv = torch.empty((T, 4, 128), dtype=torch.bfloat16, device=dev) if packed else v
+        oo = torch.empty((T, 32, 128), dtype=torch.bfloat16, device=dev) if packed else None
+        out = torch.empty_like(q)
+
+        def step():
+            st = fa.flint_attn_bshd_plan(p(m_t), p(ids_t), B, S, p(plan), nbytes, sh)
+            if packed:
+                st |= fa.flint_attn_copy_rows(p(q), p(ppk), T, 8192, 0, p(qq), sh)
+                st |= fa.flint_attn_copy_rows(p(k), p(ppk), T, 1024, 0, p(kk), sh)
+                st |= fa.flint_attn_copy_rows(p(v), p(ppk), T, 1024, 0, p(vv), sh)
+            st |= fa.flint_attn_fwd(p(qq), p(kk), p(vv), p(qw), p(kw), p(sk), 0, p(pcu), p(psu), n,
+                                    mx, T, 32, 4, 128, layer.window, 1, layer.theta, layer.eps,
+                                    p(ws), wsb, p(oo if packed else out), sh)
+            if packed:
+                st |= fa.flint_attn_copy_rows(p(oo), p(pup), B * S, 8192, 0, p(out), sh)
+            if st != 0:
+                raise RuntimeError("BSHD documents step failed")
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        pairs = unmasked_pairs(cu.cpu().numpy(), su.cpu().numpy(), layer.window)
+        recs[name] = {"ms_per_step": round(ms, 5), "tflops": round(16384.0 * pairs / (ms * 1e-3) / 1e12, 3),
+                      "n_seqs": n, "total_tokens": T, "packed": bool(packed),
+                      "valid_tokens": info[4], "documents": info[5]}
+    rec = {
+        "metric": "sink-attention prefill TFLOP/s (unmasked FLOPs), BSHD packed documents, 1 GPU",
+        "value": recs["in_place"]["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": recs["in_place"]["ms_per_step"],
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v; document lengths log-uniform 64..8192)",
+        "config": {"workload": "BSHD B=8 S=8192 packed documents, sliding 513 RoPE",
+                   "window": layer.window, "use_rope": True},
+        "variants": recs,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -397,6 +503,7 @@ def main():
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--backward", action="store_true")
     ap.add_argument("--fp16", action="store_true")
+    ap.add_argument("--bshd-docs", action="store_true")
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--decode-len", type=int, default=8192)
     ap.add_argument("--decode-window", type=int, default=0)
@@ -420,6 +527,9 @@ def main():
         return
     if args.fp16:
         fp16_bench(args)
+        return
+    if args.bshd_docs:
+        bshd_docs_bench(args)
         return
 
     import attention_head_rmsnorm_amd as fa

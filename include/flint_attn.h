@@ -258,7 +258,7 @@ int flint_attn_decode(const void* q, const void* k, const void* v, const float* 
  *   seqused  [N]   at 9+N      valid length of each sequence
  *   pack     [N]   at 9+2N     packed mode: source token (b*S+s) of each stream token
  *   unpack   [N]   at 9+3N     stream token of each source token, -1 on padding
- *   scratch  [2N+2]
+ *   scratch  [2N+2+3*ceil(N/1024)]
  * packed = 0: the B*S tokens in memory are the THD stream (no document has a
  * padded token inside it): pass q, k, v, positions and out as they are, with
  * total_tokens = N. packed = 1: the stream is the valid tokens in order; gather

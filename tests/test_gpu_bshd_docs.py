@@ -321,3 +321,22 @@ def test_long_packed_rows_sampled():
     err = np.abs(got - ref)
     _log(f"      sampled rows {len(rows)}: max_frac {err.max() / vmax:.3g} mean_frac {err.mean() / vmax:.3g}")
     assert err.max() <= MAX_FRAC * vmax and err.mean() <= MEAN_FRAC * vmax
+
+
+@pytest.mark.parametrize("holes", [False, True])
+def test_plan_many_blocks(holes):
+    """More than 1,024 blocks of tokens (each phase sums over earlier blocks in strides)."""
+    B, S = 130, 8192
+    rng = np.random.default_rng(18)
+    ids = np.cumsum(rng.random((B, S)) < 1e-3, axis=1).astype(np.int32)
+    mask = np.ones((B, S), np.uint8)
+    mask[rng.random((B, S)) < (0.01 if holes else 0.0)] = 0
+    mask[:, -5:] = 0
+    d = _dev()
+    info, cu, used, pack, unpack = fa.bshd_plan(torch.from_numpy(mask).to(d),
+                                                torch.from_numpy(ids).to(d), B, S, d)
+    exp = expected_plan(mask, ids)
+    _log(f"[gpu] plan {B}x{S} holes={holes}: {info[:4]}")
+    assert info[:4] == (exp["n"], exp["mx"], exp["T"], exp["packed"])
+    assert np.array_equal(cu.cpu().numpy(), np.array(exp["cu"]))
+    assert np.array_equal(used.cpu().numpy(), np.array(exp["used"]))
