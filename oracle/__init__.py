@@ -15,3 +15,4 @@ from .flint_oracle import (  # noqa: F401
 )
 from .flint_oracle_bwd import flint_attention_backward  # noqa: F401,E402
 from .flint_oracle_bshd import flint_attention_bshd  # noqa: F401,E402
+from .flint_oracle_block import flint_attention_block, linear  # noqa: F401,E402

@@ -282,3 +282,48 @@ def test_bshd_mutation_is_caught(name, monkeypatch):
             caught.append(pin.__name__)
             break
     assert caught, f"no BSHD pin caught the planted mistake '{name}'"
+
+
+# ----------------------------------------------------------------- attention block
+
+import oracle.flint_oracle_block as fblk  # noqa: E402
+
+from . import oracle_block_pins  # noqa: E402
+
+_linear = fblk.linear
+_split = fblk.split_heads
+
+
+def _split_dim_major(y, head_dim):
+    T = y.shape[0]
+    return y.reshape(T, head_dim, y.shape[1] // head_dim).transpose(0, 2, 1)
+
+
+def _linear_plus_bias(x, w):
+    return _linear(x, w) + 0.01
+
+
+def _linear_weight_transposed_blocks(x, w):
+    # rows of W taken in reversed order: the output channels come out reversed
+    return _linear(x, np.asarray(w)[::-1])
+
+
+BLOCK_MUTATIONS = {
+    "heads split dim-major": ("split_heads", _split_dim_major),
+    "projection with a bias": ("linear", _linear_plus_bias),
+    "output channels reversed": ("linear", _linear_weight_transposed_blocks),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BLOCK_MUTATIONS))
+def test_block_mutation_is_caught(name, monkeypatch):
+    attr, bad = BLOCK_MUTATIONS[name]
+    monkeypatch.setattr(fblk, attr, bad)
+    caught = []
+    for pin in oracle_block_pins.ALL_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no block pin caught the planted mistake '{name}'"
