@@ -12,6 +12,8 @@ There is no fallback: without the built library every call raises.
 from __future__ import annotations
 
 import ctypes
+
+import numpy as np
 import os
 from typing import Optional
 
@@ -57,6 +59,8 @@ EXPORTED = (
     "flint_attn_bshd_plan_bytes",
     "flint_attn_bshd_plan",
     "flint_attn_copy_rows",
+    "flint_proj_qkv",
+    "flint_proj_out",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -121,6 +125,10 @@ def load_library() -> ctypes.CDLL:
     lib.flint_attn_bshd_plan.restype = ctypes.c_int
     lib.flint_attn_copy_rows.argtypes = [vp, vp, i32, i32, ctypes.c_uint32, vp, vp]
     lib.flint_attn_copy_rows.restype = ctypes.c_int
+    lib.flint_proj_qkv.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.flint_proj_qkv.restype = ctypes.c_int
+    lib.flint_proj_out.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.flint_proj_out.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -203,6 +211,19 @@ def flint_attn_copy_rows(src, index, n_rows, row_bytes, fill, dst, stream) -> in
     """dst row r = src row index[r] (fill words where index[r] < 0); returns the status."""
     return int(load_library().flint_attn_copy_rows(src, index, n_rows, row_bytes, fill, dst,
                                                    stream))
+
+
+def flint_proj_qkv(x, w_q, w_k, w_v, total_tokens, hidden, num_q_heads, num_kv_heads, head_dim,
+                   q, k, v, stream) -> int:
+    """q, k, v projections of the hidden states in one launch; returns the status."""
+    return int(load_library().flint_proj_qkv(x, w_q, w_k, w_v, total_tokens, hidden, num_q_heads,
+                                             num_kv_heads, head_dim, q, k, v, stream))
+
+
+def flint_proj_out(o, w_o, total_tokens, hidden, num_q_heads, head_dim, y, stream) -> int:
+    """Output projection of the layer's output; returns the status."""
+    return int(load_library().flint_proj_out(o, w_o, total_tokens, hidden, num_q_heads, head_dim,
+                                             y, stream))
 
 
 def flint_attn_bwd_workspace_bytes(total_tokens: int, n_seqs: int, max_seqlen: int,
@@ -566,6 +587,68 @@ def flint_attn_backward(dout, q, k, v, q_norm_w, k_norm_w, sinks, out, lse, *, p
         dk = a.scatter(dk, torch.empty_like(k))
         dv = a.scatter(dv, torch.empty_like(v))
     return dq, dk, dv, dqw, dkw, dsk
+
+
+def _check_bf16(name, t, dev, shape=None):
+    import torch
+
+    if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != dev:
+        raise TypeError(f"{name} must be a contiguous bfloat16 tensor on {dev}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+
+
+def qkv_projection(x, w_q, w_k, w_v):
+    """q, k, v = x W^T for hidden states x [..., hidden] (bf16); returns
+    q [..., 32, 128], k and v [..., 4, 128] (bf16)."""
+    import torch
+
+    dev = x.device
+    hidden = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    T = int(np.prod(lead)) if lead else 1
+    _check_bf16("x", x, dev)
+    _check_bf16("w_q", w_q, dev, (NUM_Q_HEADS * HEAD_DIM, hidden))
+    _check_bf16("w_k", w_k, dev, (NUM_KV_HEADS * HEAD_DIM, hidden))
+    _check_bf16("w_v", w_v, dev, (NUM_KV_HEADS * HEAD_DIM, hidden))
+    q = torch.empty(lead + (NUM_Q_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    k = torch.empty(lead + (NUM_KV_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    st = flint_proj_qkv(_ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), T, hidden, NUM_Q_HEADS,
+                        NUM_KV_HEADS, HEAD_DIM, _ptr(q), _ptr(k), _ptr(v), _stream_handle(dev))
+    if st != FLINT_OK:
+        raise FlintError(st, "flint_proj_qkv")
+    return q, k, v
+
+
+def output_projection(o, w_o):
+    """y = o W_o^T for the layer's output o [..., 32, 128] (bf16); returns y [..., hidden]."""
+    import torch
+
+    dev = o.device
+    hidden = w_o.shape[0]
+    lead = tuple(o.shape[:-2])
+    T = int(np.prod(lead)) if lead else 1
+    _check_bf16("o", o, dev)
+    _check_bf16("w_o", w_o, dev, (hidden, NUM_Q_HEADS * HEAD_DIM))
+    if tuple(o.shape[-2:]) != (NUM_Q_HEADS, HEAD_DIM):
+        raise ValueError("o must be [..., 32, 128]")
+    y = torch.empty(lead + (hidden,), dtype=torch.bfloat16, device=dev)
+    st = flint_proj_out(_ptr(o), _ptr(w_o), T, hidden, NUM_Q_HEADS, HEAD_DIM, _ptr(y),
+                        _stream_handle(dev))
+    if st != FLINT_OK:
+        raise FlintError(st, "flint_proj_out")
+    return y
+
+
+def flint_attention_block(hidden_states, w_q, w_k, w_v, w_o, q_norm_w, k_norm_w, sinks, **layer):
+    """FlintAttention.forward: projections, the layer (``flint_attn`` keyword
+    arguments: positions, cu_seqlens / attention_mask / document_ids, window,
+    use_rope, ...), output projection. hidden_states [B, S, hidden] or
+    [T, hidden] bf16; returns the same shape."""
+    q, k, v = qkv_projection(hidden_states, w_q, w_k, w_v)
+    o = flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, **layer)
+    return output_projection(o, w_o)
 
 
 class KVCache:

@@ -16,6 +16,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config tstar|c1|c2
        python bench.py --backward [--config ...]   (one flint_attn_bwd call per step)
        python bench.py --fp16 [--config ...]       (the FP16 attention-compute variant)
        python bench.py --bshd-docs                 (BSHD rows of packed documents, in place and with holes)
+       python bench.py --proj                      (q/k/v and output projections, and the whole block)
        python bench.py --copy-probe     (plain device copy of known size, for
                                           calibrating FETCH_SIZE / WRITE_SIZE)
 Prints one JSON line.
@@ -491,6 +492,105 @@ def bshd_docs_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def proj_bench(args):
+    """The projections at 8,192 tokens (hidden 2048): the q/k/v GEMM
+    (2048 -> 4096 + 512 + 512) and the output GEMM (4096 -> 2048), each timed
+    with HIP events on the launch stream; torch's bf16 linear (hipBLASLt) on the
+    same operands timed beside them for context; and the whole attention block
+    (projections + the full-attention NoPE layer) per step."""
+    import torch
+
+    import attention_head_rmsnorm_amd as fa
+    from workload import draw_block, make_workload
+
+    wl = make_workload("tstar")
+    layer = wl.layers[0]
+    T = wl.total_tokens
+    dev = torch.device("cuda", 0)
+    fa.load_library()
+    x, w_q, w_k, w_v, w_o = (t.to(dev) for t in draw_block(wl.seed, T))
+    q = torch.empty(T, 32, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(T, 4, 128, dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    o = torch.empty_like(q)
+    y = torch.empty(T, 2048, dtype=torch.bfloat16, device=dev)
+    qw, kw, sk = wl.q_norm_w.to(dev), wl.k_norm_w.to(dev), wl.sinks.to(dev)
+    cu = wl.cu_seqlens.to(dev)
+    nbytes = fa.flint_attn_workspace_bytes(T, 1, T)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+    p = lambda t: 0 if t is None else int(t.data_ptr())  # noqa: E731
+
+    def qkv():
+        if fa.flint_proj_qkv(p(x), p(w_q), p(w_k), p(w_v), T, 2048, 32, 4, 128, p(q), p(k), p(v), sh):
+            raise RuntimeError("flint_proj_qkv failed")
+
+    def out_proj():
+        if fa.flint_proj_out(p(o), p(w_o), T, 2048, 32, 128, p(y), sh):
+            raise RuntimeError("flint_proj_out failed")
+
+    def attn():
+        if fa.flint_attn_fwd(p(q), p(k), p(v), p(qw), p(kw), p(sk), 0, p(cu), 0, 1, T, T, 32, 4, 128,
+                             layer.window, int(layer.use_rope), layer.theta, layer.eps, p(ws), nbytes,
+                             p(o), sh):
+            raise RuntimeError("flint_attn_fwd failed")
+
+    w_qkv = torch.cat([w_q, w_k, w_v], 0)
+
+    def torch_qkv():
+        torch.nn.functional.linear(x, w_qkv)
+
+    def torch_out():
+        torch.nn.functional.linear(o.view(T, -1), w_o)
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    f_qkv = 2.0 * T * 2048 * 5120
+    f_out = 2.0 * T * 4096 * 2048
+    ms = {name: timed(fn, args.steps) for name, fn in
+          (("qkv", qkv), ("out", out_proj), ("torch_qkv", torch_qkv), ("torch_out", torch_out))}
+    ms["block"] = timed(lambda: (qkv(), attn(), out_proj()), args.steps)
+    attn_flops = 16384.0 * unmasked_pairs(wl.cu_seqlens.numpy(), None, layer.window)
+    tf = lambda f, t: f / (t * 1e-3) / 1e12  # noqa: E731
+    rec = {
+        "metric": "attention-block projections TFLOP/s (q/k/v and output GEMMs), 1 GPU",
+        "value": round(tf(f_qkv + f_out, ms["qkv"] + ms["out"]), 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms["qkv"] + ms["out"], 5),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 hidden states, N(0,0.02) bf16 weights)",
+        "config": {"workload": "8192 tokens, hidden 2048 -> q 4096 + k 512 + v 512, o 4096 -> 2048",
+                   "tokens": T},
+        "qkv_ms": round(ms["qkv"], 5), "qkv_tflops": round(tf(f_qkv, ms["qkv"]), 3),
+        "out_ms": round(ms["out"], 5), "out_tflops": round(tf(f_out, ms["out"]), 3),
+        "torch_linear_qkv_ms": round(ms["torch_qkv"], 5),
+        "torch_linear_out_ms": round(ms["torch_out"], 5),
+        "block_ms": round(ms["block"], 5),
+        "block_tflops": round(tf(f_qkv + f_out + attn_flops, ms["block"]), 3),
+        "roofline": {"bound": "mfma", "kernel": "proj_gemm_kernel (q/k/v)",
+                     "achieved": round(tf(f_qkv, ms["qkv"]), 3), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf(f_qkv, ms["qkv"]) / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -504,6 +604,7 @@ def main():
     ap.add_argument("--backward", action="store_true")
     ap.add_argument("--fp16", action="store_true")
     ap.add_argument("--bshd-docs", action="store_true")
+    ap.add_argument("--proj", action="store_true")
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--decode-len", type=int, default=8192)
     ap.add_argument("--decode-window", type=int, default=0)
@@ -530,6 +631,9 @@ def main():
         return
     if args.bshd_docs:
         bshd_docs_bench(args)
+        return
+    if args.proj:
+        proj_bench(args)
         return
 
     import attention_head_rmsnorm_amd as fa

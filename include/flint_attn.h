@@ -240,6 +240,33 @@ int flint_attn_decode(const void* q, const void* k, const void* v, const float* 
                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * Projections around the layer ([layers page] FlintAttention: separate q_proj,
+ * k_proj, v_proj and o_proj, nn.Linear without bias, y = x W^T with W
+ * [out, in]; [config page] hidden_size 2048). bf16 in and out, FP32
+ * accumulation, row-major, device pointers, asynchronous on `stream`.
+ *
+ * flint_proj_qkv: x [T][hidden]; w_q [32*128][hidden], w_k and w_v
+ * [4*128][hidden]; writes q [T][32][128], k and v [T][4][128] (channel
+ * h*128 + d of a projection is channel d of head h). One launch over the
+ * concatenated 5120 output channels. hidden must be a multiple of 32.
+ *
+ * flint_proj_out: o [T][32*128] (the layer's output), w_o [hidden][32*128];
+ * writes y [T][hidden]. hidden must be a multiple of 256.
+ *
+ * Errors: FLINT_ERR_UNSUPPORTED for other head layouts or hidden sizes,
+ * FLINT_ERR_NULL, FLINT_ERR_ALIGN (16-byte alignment of every pointer),
+ * FLINT_ERR_HIP. T = 0 does nothing.
+ * ------------------------------------------------------------------------ */
+
+int flint_proj_qkv(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                   int32_t total_tokens, int32_t hidden, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, void* q, void* k, void* v,
+                   void* stream);
+
+int flint_proj_out(const void* o, const void* w_o, int32_t total_tokens, int32_t hidden,
+                   int32_t num_q_heads, int32_t head_dim, void* y, void* stream);
+
+/* ------------------------------------------------------------------------
  * BSHD input with document ids and arbitrary padding ([layers page]
  * FlintAttention.forward: attention_mask [B, S] marks valid tokens, padded
  * queries and keys leave attention while the sink stays valid, arbitrary

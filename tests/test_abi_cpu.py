@@ -20,7 +20,7 @@ FAKE = 1 << 20  # an aligned non-NULL address that is never dereferenced
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(flint_attn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(flint_(?:attn|proj)_\w+)\s*\(", text)))
 
 
 def test_header_declares_binding_names():
@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True,
                         text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (flint_attn_\w+)", nm))
+    exported = set(re.findall(r"\bT (flint_(?:attn|proj)_\w+)", nm))
     assert set(_declared()) <= exported
 
 
@@ -149,3 +149,51 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 def test_c_struct_sizes():
     # int32 / float / size_t widths the ctypes declarations assume
     assert ctypes.sizeof(ctypes.c_size_t) == 8 and ctypes.sizeof(ctypes.c_void_p) == 8
+
+
+def test_proj_validation():
+    qkv = fa.flint_proj_qkv
+    ok = dict(x=FAKE, w_q=FAKE, w_k=FAKE, w_v=FAKE, total_tokens=64, hidden=2048, num_q_heads=32,
+              num_kv_heads=4, head_dim=128, q=FAKE, k=FAKE, v=FAKE, stream=0)
+
+    def c(**over):
+        a = dict(ok)
+        a.update(over)
+        return qkv(**a)
+    assert c(total_tokens=-1) == fa.FLINT_ERR_SHAPE
+    assert c(hidden=0) == fa.FLINT_ERR_SHAPE
+    assert c(hidden=2050) == fa.FLINT_ERR_UNSUPPORTED
+    assert c(num_kv_heads=8) == fa.FLINT_ERR_UNSUPPORTED
+    assert c(x=0) == fa.FLINT_ERR_NULL and c(v=0) == fa.FLINT_ERR_NULL
+    assert c(w_k=FAKE + 8) == fa.FLINT_ERR_ALIGN and c(q=FAKE + 2) == fa.FLINT_ERR_ALIGN
+    assert c(total_tokens=0, x=0, q=0) == fa.FLINT_OK
+    out = fa.flint_proj_out
+    assert out(FAKE, FAKE, 64, 2000, 32, 128, FAKE, 0) == fa.FLINT_ERR_UNSUPPORTED
+    assert out(FAKE, FAKE, 64, 2048, 16, 128, FAKE, 0) == fa.FLINT_ERR_UNSUPPORTED
+    assert out(0, FAKE, 64, 2048, 32, 128, FAKE, 0) == fa.FLINT_ERR_NULL
+    assert out(FAKE, FAKE, 64, 2048, 32, 128, FAKE + 4, 0) == fa.FLINT_ERR_ALIGN
+    assert out(0, 0, 0, 2048, 32, 128, 0, 0) == fa.FLINT_OK
+
+
+def test_bshd_plan_and_copy_validation():
+    nb = fa.flint_attn_bshd_plan_bytes
+    assert nb(-1, 4) == 0 and nb(2, 4) >= 4 * (8 + 6 * 8)
+    plan = fa.flint_attn_bshd_plan
+    assert plan(FAKE, FAKE, -1, 4, FAKE, 1 << 20, 0) == fa.FLINT_ERR_SHAPE
+    assert plan(FAKE, FAKE, 1 << 16, 1 << 15, FAKE, 1 << 40, 0) == fa.FLINT_ERR_SHAPE
+    assert plan(FAKE, FAKE, 2, 4, 0, 1 << 20, 0) == fa.FLINT_ERR_NULL
+    assert plan(FAKE, FAKE + 2, 2, 4, FAKE, 1 << 20, 0) == fa.FLINT_ERR_ALIGN
+    assert plan(FAKE, FAKE, 2, 4, FAKE, nb(2, 4) - 4, 0) == fa.FLINT_ERR_WORKSPACE
+    cp = fa.flint_attn_copy_rows
+    assert cp(FAKE, FAKE, -1, 16, 0, FAKE, 0) == fa.FLINT_ERR_SHAPE
+    assert cp(FAKE, FAKE, 4, 6, 0, FAKE, 0) == fa.FLINT_ERR_SHAPE
+    assert cp(0, FAKE, 4, 16, 0, FAKE, 0) == fa.FLINT_ERR_NULL
+    assert cp(FAKE + 2, FAKE, 4, 16, 0, FAKE, 0) == fa.FLINT_ERR_ALIGN
+    assert cp(0, 0, 0, 16, 0, 0, 0) == fa.FLINT_OK
+
+
+def test_f16_workspace_adds_query_rows():
+    a = fa.flint_attn_workspace_bytes(8192, 1, 8192)
+    b = fa.flint_attn_f16_workspace_bytes(8192, 1, 8192)
+    assert b >= a + 8192 * 32 * 128 * 2
+    assert fa.flint_attn_f16_workspace_bytes(8192, 1, 8192, 8, 128) == 0

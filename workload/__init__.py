@@ -13,5 +13,6 @@ from .gen import (  # noqa: F401
     make_workload,
     make_custom,
     make_long_decode,
+    draw_block,
     draw_dout,
 )

@@ -264,3 +264,18 @@ def draw_dout(seed: int, T: int, std: float = 1.0) -> torch.Tensor:
     the same seed) rounded to bfloat16."""
     rng = np.random.default_rng(seed + 7919)
     return _bf16(_normal(rng, (T, NUM_Q_HEADS, HEAD_DIM), std))
+
+
+def draw_block(seed: int, T: int, hidden: int = 2048):
+    """Inputs of the attention block: hidden states x [T, hidden] ~ N(0, 1)
+    (the block sees normalized hidden states) and the projection weights
+    ~ N(0, 0.02) (FlintConfig page, initializer_range 0.02): w_q [4096, hidden],
+    w_k and w_v [512, hidden], w_o [hidden, 4096]; all bf16. Returns
+    (x, w_q, w_k, w_v, w_o)."""
+    rng = np.random.default_rng(seed + 104729)
+    x = _bf16(_normal(rng, (T, hidden)))
+    w_q = _bf16(_normal(rng, (NUM_Q_HEADS * HEAD_DIM, hidden), 0.02))
+    w_k = _bf16(_normal(rng, (NUM_KV_HEADS * HEAD_DIM, hidden), 0.02))
+    w_v = _bf16(_normal(rng, (NUM_KV_HEADS * HEAD_DIM, hidden), 0.02))
+    w_o = _bf16(_normal(rng, (hidden, NUM_Q_HEADS * HEAD_DIM), 0.02))
+    return x, w_q, w_k, w_v, w_o
