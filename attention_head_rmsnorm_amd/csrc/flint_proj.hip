@@ -16,11 +16,12 @@
 // halves with the partner lane and stores 16 contiguous bytes of a token's
 // row. Wave w covers channels 128 (w & 1) + [0, 128) (one head) and tokens
 // 64 (w >> 1) + [0, 64): 4 x 2 blocks, 128 FP32 accumulators, two waves per
-// SIMD. k advances 32 at a time through a 4-stage LDS ring filled by direct
-// global-to-LDS loads, three stages ahead. Rows are 64 bytes in LDS; 16-byte
-// chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so the 16 lanes of an
-// operand read hit 16 different bank groups. Token rows past M read as zero
-// and their stores are dropped (buffer range checks).
+// SIMD. k advances 64 at a time through a 2-stage LDS ring (2 x 64 KiB) filled
+// by direct global-to-LDS loads one stage ahead; inside a stage the operands of
+// the next 16-wide k step are read while the MFMAs of this one run. Rows are
+// 128 bytes in LDS; 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7),
+// so the 16 lanes of an operand read hit 16 different bank groups. Token rows
+// past M read as zero and their stores are dropped (buffer range checks).
 
 #include <hip/hip_runtime.h>
 
@@ -30,14 +31,9 @@ namespace flint {
 
 namespace {
 
-constexpr int kPM = 256;                      // tokens per tile
-constexpr int kPN = 256;                      // output channels per tile
-constexpr int kPK = 32;                       // k per stage
-constexpr int kPStages = 4;                   // LDS ring depth
-constexpr int kPThreads = 512;                // 8 waves
-constexpr int kPHalf = kPN * kPK * 2;         // bytes of the W part of a stage (16 KiB)
-constexpr int kPStageBytes = 2 * kPHalf;      // W part, then X part (32 KiB)
-constexpr int kPStageVec = kPStageBytes / 16;
+constexpr int kPN = 256;          // output channels per tile
+constexpr int kProjKAlign = 64;   // K is a multiple of every tile configuration's k step
+constexpr int kProjMaxTM = 256;   // largest token tile (buffer offsets stay 32-bit)
 
 struct ProjRegions {
   const uint16_t* w[3];  // [n][K] per region
@@ -49,53 +45,100 @@ __device__ __forceinline__ f32x16 mma_bf16(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// This wave's share of one stage: W rows 32 wave + [0, 32) and X rows
-// 32 wave + [0, 32), 16 rows (1 KiB) per load. Lane L of a load lands at
-// LDS byte 16 L of its 1 KiB: row L / 4, chunk position L % 4, which holds
-// source chunk (L % 4) ^ ((row >> 2) & 3) = (L % 4) ^ ((L >> 4) & 3).
+// Tile shape: TM tokens x 256 channels, k advancing PK per stage through a
+// ring of STAGES stages with loads AHEAD stages ahead, WAVES waves of which
+// each covers 128 channels (one head) and TM / (WAVES / 2) tokens.
+template <int PK, int STAGES, int AHEAD, int WAVES, int TM>
+struct ProjCfg {
+  static constexpr int kChunks = PK / 8;              // 16-byte chunks per LDS row
+  static constexpr int kRowB = PK * 2;                // bytes per LDS row
+  static constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one wave-wide load fills
+  static constexpr int kWLoads = kPN / kRowsPerLoad;  // loads of the W part of a stage
+  static constexpr int kXLoads = TM / kRowsPerLoad;   // loads of the X part
+  static constexpr int kLoadsPerWave = (kWLoads + kXLoads) / WAVES;
+  static constexpr int kWBytes = kPN * kRowB;
+  static constexpr int kStageBytes = (kPN + TM) * kRowB;
+  static constexpr int kWaveTok = TM / (WAVES / 2);   // tokens per wave
+  static constexpr int kI = kWaveTok / 32;            // 32-token blocks per wave
+  static_assert((kWLoads + kXLoads) % WAVES == 0, "loads split evenly over the waves");
+  static_assert(AHEAD < STAGES, "a stage is reloaded only after it was read");
+  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS");
+};
+
+// 16-byte chunk c of LDS row r sits at chunk position c ^ swz(r): the 16
+// lanes of an operand read (16 consecutive rows, one chunk) then cover all 64
+// banks. 64-byte rows pack 4 rows per 256 bytes, 128-byte rows 2.
+template <int kChunks>
+__device__ __forceinline__ int swz(int r) {
+  return kChunks == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+}
+
+// This wave's loads of one stage. Load q of the stage fills rows
+// q * kRowsPerLoad + [0, kRowsPerLoad) of the W part (q < kWLoads) or the X
+// part; lane L lands at LDS byte 16 L of it: row L / kChunks, chunk position
+// L % kChunks, so it reads source chunk (L % kChunks) ^ swz(row).
+#define WAVES_OF(C) ((C::kWLoads + C::kXLoads) / C::kLoadsPerWave)
+
+template <class C>
 __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t xr,
-                                           int row_bytes, int kbyte, uint4* stage, int wave,
+                                           int row_bytes, int kbyte, char* stage, int wave,
                                            int lane) {
-  const int c = (lane & 3) ^ ((lane >> 4) & 3);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 32 * wave + 16 * i + (lane >> 2);
-    const int voff = row * row_bytes + c * 16;
-    char* base = reinterpret_cast<char*>(stage) + (32 * wave + 16 * i) * 64;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        wr, (__attribute__((address_space(3))) void*)base, 16, voff, kbyte, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        xr, (__attribute__((address_space(3))) void*)(base + kPHalf), 16, voff, kbyte, 0, 0);
+  for (int n = 0; n < C::kLoadsPerWave; ++n) {
+    const int q = wave + n * WAVES_OF(C);
+    const bool isw = q < C::kWLoads;
+    const int row0 = (isw ? q : q - C::kWLoads) * C::kRowsPerLoad;
+    const int row = row0 + lane / C::kChunks;
+    const int c = (lane % C::kChunks) ^ swz<C::kChunks>(row);
+    char* base = stage + (isw ? 0 : C::kWBytes) + row0 * C::kRowB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isw ? wr : xr,
+                                             (__attribute__((address_space(3))) void*)base, 16,
+                                             row * row_bytes + c * 16, kbyte, 0, 0);
   }
 }
 
 // Operand fragment of 32 rows starting at `row0` (a multiple of 16) for
 // k-step kk: lane reads row row0 + lane % 32, chunk 2 kk + lane / 32.
-__device__ __forceinline__ bf16x8 ld_operand(const uint4* part, int row0, int kk, int lane) {
-  const int r = lane & 31;
-  const int c = (2 * kk + (lane >> 5)) ^ ((r >> 2) & 3);
-  return __builtin_bit_cast(bf16x8, part[(row0 + r) * 4 + c]);
+template <class C>
+__device__ __forceinline__ bf16x8 ld_operand(const char* part, int row0, int kk, int lane) {
+  const int r = row0 + (lane & 31);
+  const int c = (2 * kk + (lane >> 5)) ^ swz<C::kChunks>(r);
+  return *reinterpret_cast<const bf16x8*>(part + r * C::kRowB + c * 16);
 }
 
-__device__ __forceinline__ void proj_barrier(int newer) {
-  switch (newer) {
-    case 8: ring_barrier_n<8>(); break;
-    case 4: ring_barrier_n<4>(); break;
-    default: ring_barrier_n<0>(); break;
+template <int N>
+__device__ __forceinline__ void proj_barrier_upto(int newer) {
+  if constexpr (N <= 0) {
+    ring_barrier_n<0>();
+  } else {
+    if (newer == N) ring_barrier_n<(N > 0 ? N : 0)>();
+    else proj_barrier_upto<N - 1>(newer);
   }
 }
 
-__global__ __launch_bounds__(kPThreads, 1) void proj_gemm_kernel(const uint16_t* __restrict__ x,
-                                                                  int M, int K, ProjRegions R) {
-  __shared__ uint4 smem[kPStages][kPStageVec];
+template <class C, int PK, int STAGES, int AHEAD, int WAVES, int TM, int MINB>
+__global__ __launch_bounds__(64 * WAVES, MINB) void proj_gemm_kernel(const uint16_t* __restrict__ x,
+                                                                   int M, int K, ProjRegions R) {
+  __shared__ __attribute__((aligned(16))) char smem[STAGES][C::kStageBytes];
   const int nt_n = (R.n[0] + R.n[1] + R.n[2]) / kPN;
-  const int nt_m = (M + kPM - 1) / kPM;
-  const int total = nt_m * nt_n;
-  // Consecutive ranks go to one XCD (workgroup b runs on XCD b % 8); a rank
-  // walks the channel tiles of one token tile, which stays in that L2.
+  const int nt_m = (M + TM - 1) / TM;
   const int b = blockIdx.x;
-  const int rank = (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
-  const int tm = rank / nt_n, tn = rank % nt_n;
+  int tm, tn;
+  if (nt_m % 32 == 0) {
+    // Workgroup b runs on XCD b % 8. Each XCD owns nt_m / 8 token tiles and
+    // runs them in groups of 4, taking the channel tiles in order for all 4
+    // together: the 32 workgroups an XCD runs at once are 4 token tiles x 8
+    // channel tiles, so each k slice it fetches is used 4 or 8 times from its
+    // L2.
+    const int per = nt_m / 8, r = b / 8;
+    const int g = r / (4 * nt_n), w = r % (4 * nt_n);
+    tn = w / 4;
+    tm = (b % 8) * per + 4 * g + w % 4;
+  } else {
+    // few token tiles: consecutive workgroups walk the channel tiles of one
+    tm = b / nt_n;
+    tn = b % nt_n;
+  }
   // the region of this channel tile (selects, not an indexed argument array)
   int c0 = tn * kPN;
   const int reg = c0 < R.n[0] ? 0 : (c0 < R.n[0] + R.n[1] ? 1 : 2);
@@ -103,8 +146,8 @@ __global__ __launch_bounds__(kPThreads, 1) void proj_gemm_kernel(const uint16_t*
   const int n_out = reg == 0 ? R.n[0] : (reg == 1 ? R.n[1] : R.n[2]);
   const uint16_t* wreg = reg == 0 ? R.w[0] : (reg == 1 ? R.w[1] : R.w[2]);
   uint16_t* oreg = reg == 0 ? R.out[0] : (reg == 1 ? R.out[1] : R.out[2]);
-  const int m0 = tm * kPM;
-  const int rows = min(M - m0, kPM);
+  const int m0 = tm * TM;
+  const int rows = min(M - m0, TM);
   const int row_bytes = K * 2;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(wreg + (size_t)c0 * K), 0, kPN * row_bytes, kBufferWord3);
@@ -114,47 +157,62 @@ __global__ __launch_bounds__(kPThreads, 1) void proj_gemm_kernel(const uint16_t*
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wc = wave & 1, wt = wave >> 1;
-  const int nk = K / kPK;
+  const int nk = K / PK;
 
-  f32x16 acc[2][4];
+  f32x16 acc[C::kI][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::kI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  for (int s = 0; s < 3 && s < nk; ++s) load_stage(wr, xr, row_bytes, s * kPK * 2, smem[s], wave, lane);
+  for (int s = 0; s < AHEAD && s < nk; ++s)
+    load_stage<C>(wr, xr, row_bytes, s * PK * 2, smem[s], wave, lane);
   for (int s = 0; s < nk; ++s) {
-    // stage s is in LDS once only the loads of the (up to two) later stages
-    // remain in flight; every wave has also finished reading stage s - 1
-    proj_barrier(4 * min(2, nk - 1 - s));
-    if (s + 3 < nk) load_stage(wr, xr, row_bytes, (s + 3) * kPK * 2, smem[(s + 3) % kPStages], wave, lane);
-    const uint4* wp = smem[s % kPStages];
-    const uint4* xp = wp + kPHalf / 16;
+    // stage s is in LDS once only the loads of the later stages already
+    // issued remain in flight; every wave has also finished reading stage s - 1
+    proj_barrier_upto<C::kLoadsPerWave * (AHEAD - 1)>(C::kLoadsPerWave * min(AHEAD - 1, nk - 1 - s));
+    if (s + AHEAD < nk)
+      load_stage<C>(wr, xr, row_bytes, (s + AHEAD) * PK * 2, smem[(s + AHEAD) % STAGES], wave, lane);
+    const char* wp = smem[s % STAGES];
+    const char* xp = wp + C::kWBytes;
+    // the operands of k-step kk + 1 are read while the MFMAs of kk run
+    constexpr int kF = C::kI + 4;  // fragments per k-step
+    bf16x8 f[2][kF];
+    auto read = [&](int kk, bf16x8* dst) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 fw[4], fx[2];
+      for (int i = 0; i < C::kI; ++i) dst[i] = ld_operand<C>(xp, C::kWaveTok * wt + 32 * i, kk, lane);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fw[j] = ld_operand(wp, 128 * wc + 32 * j, kk, lane);
+      for (int j = 0; j < 4; ++j) dst[C::kI + j] = ld_operand<C>(wp, 128 * wc + 32 * j, kk, lane);
+    };
+    read(0, f[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, kF, 0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fx[i] = ld_operand(xp, 64 * wt + 32 * i, kk, lane);
+    for (int kk = 0; kk < PK / 16; ++kk) {
+      if (kk + 1 < PK / 16) read(kk + 1, f[(kk + 1) & 1]);
+      const bf16x8* g = f[kk & 1];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < C::kI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mma_bf16(fw[j], fx[i], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma_bf16(g[C::kI + j], g[i], acc[i][j]);
+#pragma unroll
+      for (int m = 0; m < 4 * C::kI; ++m) {
+        if (kk + 1 < PK / 16 && m < kF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
     }
   }
 
   // Epilogue: lane (col, half) holds channels 32j + 8g + 4half + [0, 4) of
-  // token 64wt + 32i + col; a swap with the partner lane gives it channels
-  // 32j + 16r2 + 8half + [0, 8), 16 contiguous bytes per store.
+  // token kWaveTok wt + 32i + col; a swap with the partner lane gives it
+  // channels 32j + 16r2 + 8half + [0, 8), 16 contiguous bytes per store.
   const int col = lane & 31, half = lane >> 5;
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       oreg + (size_t)m0 * n_out, 0, rows * n_out * 2, kBufferWord3);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int tok = 64 * wt + 32 * i + col;
+  for (int i = 0; i < C::kI; ++i) {
+    const int tok = C::kWaveTok * wt + 32 * i + col;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -174,14 +232,29 @@ __global__ __launch_bounds__(kPThreads, 1) void proj_gemm_kernel(const uint16_t*
   }
 }
 
-int launch_proj(const void* x, int M, int K, const ProjRegions& R, hipStream_t st) {
+// Tile configuration (k step, ring stages, stages loaded ahead, waves, tokens
+// per tile, workgroups per CU). 64-wide k steps in a two-stage ring measured
+// fastest on gfx950: fewer barriers per MFMA than 32-wide steps in four stages.
+#ifndef FLINT_PROJ_CFG
+#define FLINT_PROJ_CFG 64, 2, 1, 8, 256, 1
+#endif
+
+template <int PK, int STAGES, int AHEAD, int WAVES, int TM, int MINB>
+int launch_proj_cfg(const void* x, int M, int K, const ProjRegions& R, hipStream_t st) {
+  using C = ProjCfg<PK, STAGES, AHEAD, WAVES, TM>;
   const int n = R.n[0] + R.n[1] + R.n[2];
-  const int64_t total = (int64_t)((M + kPM - 1) / kPM) * (n / kPN);
+  const int64_t total = (int64_t)((M + TM - 1) / TM) * (n / kPN);
   if (total == 0) return FLINT_OK;
+  if (K % PK != 0) return FLINT_ERR_UNSUPPORTED;
   (void)hipGetLastError();
-  proj_gemm_kernel<<<(unsigned)total, kPThreads, 0, st>>>(static_cast<const uint16_t*>(x), M, K, R);
+  proj_gemm_kernel<C, PK, STAGES, AHEAD, WAVES, TM, MINB>
+      <<<(unsigned)total, 64 * WAVES, 0, st>>>(static_cast<const uint16_t*>(x), M, K, R);
   if (hipGetLastError() != hipSuccess) return FLINT_ERR_HIP;
   return FLINT_OK;
+}
+
+int launch_proj(const void* x, int M, int K, const ProjRegions& R, hipStream_t st) {
+  return launch_proj_cfg<FLINT_PROJ_CFG>(x, M, K, R, st);
 }
 
 }  // namespace
@@ -196,13 +269,13 @@ extern "C" int flint_proj_qkv(const void* x, const void* w_q, const void* w_k, c
                               void* stream) {
   if (total_tokens < 0 || hidden <= 0) return FLINT_ERR_SHAPE;
   if (num_q_heads != kH || num_kv_heads != kG || head_dim != kD) return FLINT_ERR_UNSUPPORTED;
-  if (hidden % kPK != 0 || (int64_t)hidden * 2 * kPN >= ((int64_t)1 << 31)) return FLINT_ERR_UNSUPPORTED;
+  if (hidden % kProjKAlign != 0 || (int64_t)hidden * 2 * kPN >= ((int64_t)1 << 31))
+    return FLINT_ERR_UNSUPPORTED;
   if (total_tokens == 0) return FLINT_OK;
   if (!x || !w_q || !w_k || !w_v || !q || !k || !v) return FLINT_ERR_NULL;
   if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) ||
       !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
     return FLINT_ERR_ALIGN;
-  if ((int64_t)kPM * kH * kD * 2 >= ((int64_t)1 << 31)) return FLINT_ERR_SHAPE;
   ProjRegions R;
   R.w[0] = static_cast<const uint16_t*>(w_q);
   R.w[1] = static_cast<const uint16_t*>(w_k);
@@ -220,7 +293,8 @@ extern "C" int flint_proj_out(const void* o, const void* w_o, int32_t total_toke
                               int32_t num_q_heads, int32_t head_dim, void* y, void* stream) {
   if (total_tokens < 0 || hidden <= 0) return FLINT_ERR_SHAPE;
   if (num_q_heads != kH || head_dim != kD) return FLINT_ERR_UNSUPPORTED;
-  if (hidden % kPN != 0 || (int64_t)kPM * hidden * 2 >= ((int64_t)1 << 31)) return FLINT_ERR_UNSUPPORTED;
+  if (hidden % kPN != 0 || (int64_t)kProjMaxTM * hidden * 2 >= ((int64_t)1 << 31))
+    return FLINT_ERR_UNSUPPORTED;
   if (total_tokens == 0) return FLINT_OK;
   if (!o || !w_o || !y) return FLINT_ERR_NULL;
   if (!aligned(o, 16) || !aligned(w_o, 16) || !aligned(y, 16)) return FLINT_ERR_ALIGN;

@@ -545,7 +545,7 @@ def proj_bench(args):
         torch.nn.functional.linear(o.view(T, -1), w_o)
 
     def timed(fn, steps):
-        for _ in range(args.warmup):
+        for _ in range(max(args.warmup, 20)):  # the clocks settle under a steady GEMM load
             fn()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)

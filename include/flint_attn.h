@@ -248,7 +248,7 @@ int flint_attn_decode(const void* q, const void* k, const void* v, const float* 
  * flint_proj_qkv: x [T][hidden]; w_q [32*128][hidden], w_k and w_v
  * [4*128][hidden]; writes q [T][32][128], k and v [T][4][128] (channel
  * h*128 + d of a projection is channel d of head h). One launch over the
- * concatenated 5120 output channels. hidden must be a multiple of 32.
+ * concatenated 5120 output channels. hidden must be a multiple of 64.
  *
  * flint_proj_out: o [T][32*128] (the layer's output), w_o [hidden][32*128];
  * writes y [T][hidden]. hidden must be a multiple of 256.

@@ -162,7 +162,7 @@ def test_proj_validation():
         return qkv(**a)
     assert c(total_tokens=-1) == fa.FLINT_ERR_SHAPE
     assert c(hidden=0) == fa.FLINT_ERR_SHAPE
-    assert c(hidden=2050) == fa.FLINT_ERR_UNSUPPORTED
+    assert c(hidden=2050) == fa.FLINT_ERR_UNSUPPORTED and c(hidden=2080) == fa.FLINT_ERR_UNSUPPORTED
     assert c(num_kv_heads=8) == fa.FLINT_ERR_UNSUPPORTED
     assert c(x=0) == fa.FLINT_ERR_NULL and c(v=0) == fa.FLINT_ERR_NULL
     assert c(w_k=FAKE + 8) == fa.FLINT_ERR_ALIGN and c(q=FAKE + 2) == fa.FLINT_ERR_ALIGN
