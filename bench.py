@@ -224,7 +224,28 @@ def decode_bench(args):
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": alg, "traffic": None},
     }
+    if not args.no_cpu_baseline:
+        # the oracle's decode: the last row of a sequence of attended tokens
+        from oracle import flint_attention
+
+        n_seq = B  # every sequence of the batch
+        rng = np.random.default_rng(2002)
+        qkv = [rng.standard_normal((attended, h, 128)) for h in (32, 4, 4)]
+        t0c = time.perf_counter()
+        for _ in range(n_seq):
+            flint_attention(qkv[0], qkv[1], qkv[2], f64np(qw), f64np(kw), f64np(sinks),
+                            np.array([0, attended]), window=W, use_rope=use_rope,
+                            rows=np.array([attended - 1]))
+        dt = time.perf_counter() - t0c
+        rec["cpu_baseline"] = {"value": round(n_seq * (attended * 2048.0 + 72 * 256.0) / dt / 1e9, 6),
+                               "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle",
+                               "sample": f"{n_seq} sequences of {attended} attended tokens, the last "
+                                         f"row each, {dt:.2f} s, FP64 NumPy"}
     print(json.dumps(rec), flush=True)
+
+
+def f64np(t):
+    return t.detach().double().cpu().numpy()
 
 
 def backward_bench(args):
@@ -308,8 +329,28 @@ def backward_bench(args):
         "pct_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
         "algorithmic_flops": flops,
         "executed_mfma_tflops": round(3.5 * 16384.0 * pairs / (ms * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "mfma", "kernel": "flint_attn_bwd (all its kernels, one call)",
+                     "achieved": round(value, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / BF16_PEAK_TFLOPS, 4), "traffic": None},
         "wall_s_timed": round(wall, 4),
     }
+    if not args.no_cpu_baseline:
+        # the backward oracle on the workload's first 2,048 tokens as one sequence
+        from oracle import flint_attention_backward
+
+        n = min(2048, T)
+        sl = slice(0, n)
+        t0c = time.perf_counter()
+        flint_attention_backward(f64np(wl.q[sl]), f64np(wl.k[sl]), f64np(wl.v[sl]),
+                                 f64np(wl.q_norm_w), f64np(wl.k_norm_w), f64np(wl.sinks),
+                                 np.array([0, n]), f64np(dout[sl]), window=layer.window,
+                                 use_rope=layer.use_rope, theta=layer.theta, eps=layer.eps)
+        dt = time.perf_counter() - t0c
+        pc = unmasked_pairs(np.array([0, n]), None, layer.window)
+        rec["cpu_baseline"] = {"value": round(2.5 * 16384.0 * pc / dt / 1e12, 6),
+                               "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+                               "sample": f"the first {n} tokens as one sequence, every gradient, "
+                                         f"{pc} unmasked pairs, {dt:.2f} s, FP64 NumPy"}
     print(json.dumps(rec), flush=True)
 
 
@@ -382,8 +423,15 @@ def fp16_bench(args):
                    "use_rope": layer.use_rope},
         "pct_f16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
         "unmasked_flops": flops,
+        "roofline": {"bound": "mfma", "kernel": "flint_attn_fwd_f16 (one call)",
+                     "achieved": round(value, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / BF16_PEAK_TFLOPS, 4), "traffic": None},
         "wall_s_timed": round(wall, 4),
     }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, layer, min(args.cpu_rows, 2048))
+        rec["cpu_baseline"] = {k2: (round(v2, 6) if isinstance(v2, float) else v2)
+                               for k2, v2 in cb.items() if k2 != "seconds"}
     print(json.dumps(rec), flush=True)
 
 
@@ -488,7 +536,30 @@ def bshd_docs_bench(args):
         "config": {"workload": "BSHD B=8 S=8192 packed documents, sliding 513 RoPE",
                    "window": layer.window, "use_rope": True},
         "variants": recs,
+        "roofline": {"bound": "mfma", "kernel": "plan + flint_attn_fwd, in place (one step)",
+                     "achieved": recs["in_place"]["tflops"], "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s",
+                     "frac": round(recs["in_place"]["tflops"] / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
     }
+    if not args.no_cpu_baseline:
+        # the THD oracle on sampled rows of the documents (in place, no holes)
+        from oracle import flint_attention
+
+        info, cu, su, _, _ = fa.bshd_plan(None, ids_t, B, S, dev)
+        cu_np = cu.cpu().numpy().astype(np.int64)
+        rows = np.arange(0, B * S, 64, dtype=np.int64)
+        t0c = time.perf_counter()
+        flint_attention(f64np(wl.q), f64np(wl.k), f64np(wl.v), f64np(wl.q_norm_w),
+                        f64np(wl.k_norm_w), f64np(wl.sinks), cu_np, window=layer.window,
+                        use_rope=True, theta=layer.theta, eps=layer.eps, rows=rows)
+        dt = time.perf_counter() - t0c
+        pc = pairs_of_rows(cu_np, None, layer.window, rows)
+        rec["cpu_baseline"] = {"value": round(16384.0 * pc / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": cpu_threads(), "kind": "oracle",
+                               "sample": f"every 64th of {B * S} query rows over the "
+                                         f"{info[5]} documents, {pc} unmasked pairs, {dt:.2f} s, "
+                                         "FP64 NumPy"}
     print(json.dumps(rec), flush=True)
 
 
@@ -588,6 +659,23 @@ def proj_bench(args):
                      "unit": "TFLOP/s", "frac": round(tf(f_qkv, ms["qkv"]) / BF16_PEAK_TFLOPS, 4),
                      "traffic": None},
     }
+    if not args.no_cpu_baseline:
+        # the oracle's projections (FP64 products) on every token
+        from oracle import linear
+
+        xs = f64np(x)
+        wq, wk, wv, wo = (f64np(w) for w in (w_q, w_k, w_v, w_o))
+        t0c = time.perf_counter()
+        yq = linear(xs, wq)
+        linear(xs, wk)
+        linear(xs, wv)
+        linear(yq, wo)
+        dt = time.perf_counter() - t0c
+        n = xs.shape[0]
+        rec["cpu_baseline"] = {"value": round(n * 2.0 * (2048 * 5120 + 4096 * 2048) / dt / 1e12, 6),
+                               "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+                               "sample": f"all {n} tokens, both projections, "
+                                         f"{dt:.2f} s, FP64 NumPy"}
     print(json.dumps(rec), flush=True)
 
 
