@@ -654,11 +654,13 @@ def flint_attention_block(hidden_states, w_q, w_k, w_v, w_o, q_norm_w, k_norm_w,
 class KVCache:
     """One layer's KV cache for decode, in the layout the C ABI documents.
 
-    ``k`` is [batch, 4, cap, 128] bf16 (normalized, rotated keys) and ``vt``
-    [batch, 4, 128, cap] bf16 (values, transposed); ``length`` int32 [batch]
-    counts the tokens each sequence holds. ``window`` > 0 makes it a ring of
-    the last ``window`` tokens (cap is rounded up to a multiple of 32);
-    ``window`` = 0 keeps ``max_tokens`` tokens.
+    ``k`` [batch, 4, cap/32, 2, 4, 64, 8] and ``vt`` [batch, 4, cap/32, 8, 64, 8]
+    bf16 hold the normalized, rotated keys and the values in 32-slot blocks in
+    the order the decode kernel reads them (``dense_keys`` / ``dense_values``
+    unpack them to [batch, 4, cap, 128]); ``length`` int32 [batch] counts the
+    tokens each sequence holds. ``window`` > 0 makes it a ring of the last
+    ``window`` tokens (cap is rounded up to a multiple of 32); ``window`` = 0
+    keeps ``max_tokens`` tokens.
     """
 
     def __init__(self, batch: int, window: int, max_tokens: int = 0, *, use_rope: bool = True,
@@ -671,13 +673,26 @@ class KVCache:
         self.cap = (need + 31) // 32 * 32
         self.batch, self.window = batch, window
         self.use_rope, self.rope_theta, self.eps = use_rope, rope_theta, eps
-        self.k = torch.zeros(batch, NUM_KV_HEADS, self.cap, HEAD_DIM, dtype=torch.bfloat16,
+        nb = self.cap // 32
+        self.k = torch.zeros(batch, NUM_KV_HEADS, nb, 2, 4, 64, 8, dtype=torch.bfloat16,
                              device=device)
-        self.vt = torch.zeros(batch, NUM_KV_HEADS, HEAD_DIM, self.cap, dtype=torch.bfloat16,
+        self.vt = torch.zeros(batch, NUM_KV_HEADS, nb, 8, 64, 8, dtype=torch.bfloat16,
                               device=device)
         self.length = torch.zeros(batch, dtype=torch.int32, device=device)
         nbytes = flint_attn_decode_workspace_bytes(batch, self.cap)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+    def dense_keys(self):
+        """K' as [batch, 4, cap, 128] (slot-major), unpacked from the blocks."""
+        B, nb = self.batch, self.cap // 32
+        k = self.k.view(B, NUM_KV_HEADS, nb, 2, 4, 4, 16, 8)  # blk, kh, ds, qd, col, e
+        return k.permute(0, 1, 2, 3, 6, 4, 5, 7).reshape(B, NUM_KV_HEADS, self.cap, HEAD_DIM)
+
+    def dense_values(self):
+        """V as [batch, 4, cap, 128] (slot-major), unpacked from the blocks."""
+        B, nb = self.batch, self.cap // 32
+        v = self.vt.view(B, NUM_KV_HEADS, nb, 8, 4, 16, 2, 4)  # blk, db, qd, col, hi, lo
+        return v.permute(0, 1, 2, 6, 4, 7, 3, 5).reshape(B, NUM_KV_HEADS, self.cap, HEAD_DIM)
 
     def _check(self, name, t, dtype, shape):
         import torch

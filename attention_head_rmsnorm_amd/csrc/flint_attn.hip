@@ -999,6 +999,20 @@ constexpr int kDecBlock = 32;         // tokens per step of the decode attention
 constexpr int kDecMinSplitBlocks = 2;  // smallest split (64 tokens), sizes the workspace
 constexpr int kDecMaxSplitBlocks = 8;  // largest split (256 tokens)
 constexpr int kDecMergeLanes = 32;     // splits merged in parallel per (sequence, head)
+constexpr int kDecBlockElems = kDecBlock * kD;  // bf16 elements of one K' or V cache block
+
+// Position in its cache block of channel c of the key in slot kb of the block:
+// K' fragment 4kh + ds of lane 16qd + col holds key 16kh + col, channels
+// 32ds + 8qd .. +8; V fragment db of lane 16qd + col holds channel 16db + col
+// of keys 4qd .. +4 (elements 0-3) and 16 + 4qd .. +4 (elements 4-7).
+__device__ __forceinline__ int dec_k_index(int kb, int c) {
+  const int kh = kb >> 4, col = kb & 15, ds = c >> 5, qd = (c >> 3) & 3, e = c & 7;
+  return (((4 * kh + ds) * 64) + 16 * qd + col) * 8 + e;
+}
+__device__ __forceinline__ int dec_v_index(int kb, int c) {
+  const int db = c >> 4, col = c & 15, hi = kb >> 4, qd = (kb >> 2) & 3, e = 4 * hi + (kb & 3);
+  return ((db * 64) + 16 * qd + col) * 8 + e;
+}
 
 struct DecWs {
   int* hdr;        // [0] device-data error bits
@@ -1089,13 +1103,16 @@ __global__ __launch_bounds__(64 * (1 + kHpg)) void decode_append_kernel(
   float a, c;
   if (wave == 0) {
     norm_rope_row(k + (tok * kG + g) * kD, k_norm_w, eps, rope, pos, r, 1.0f, lane, a, c);
-    uint16_t* kr = k_cache + (((size_t)b * kG + g) * cap + slot) * kD;
-    kr[lane] = bf16_bits(a);
-    kr[lane + 64] = bf16_bits(c);
+    // block of 32 slots in the decode operand order (see DecFrags)
+    const size_t blk = ((size_t)b * kG + g) * (cap / kDecBlock) + slot / kDecBlock;
+    const int kb = slot % kDecBlock;
+    uint16_t* kblk = k_cache + blk * kDecBlockElems;
+    kblk[dec_k_index(kb, lane)] = bf16_bits(a);
+    kblk[dec_k_index(kb, lane + 64)] = bf16_bits(c);
     const uint16_t* vr = v + (tok * kG + g) * kD;
-    uint16_t* vt = vt_cache + ((size_t)b * kG + g) * kD * (size_t)cap + slot;
-    vt[(size_t)lane * cap] = vr[lane];
-    vt[(size_t)(lane + 64) * cap] = vr[lane + 64];
+    uint16_t* vblk = vt_cache + blk * kDecBlockElems;
+    vblk[dec_v_index(kb, lane)] = vr[lane];
+    vblk[dec_v_index(kb, lane + 64)] = vr[lane + 64];
   } else if (q) {
     const int h = g * kHpg + wave - 1;
     norm_rope_row(q + ((size_t)b * kH + h) * kD, q_norm_w, eps, rope, pos, r,
@@ -1129,25 +1146,21 @@ __device__ __forceinline__ void dec_range(int len, int window, int* t_lo, int* t
 // while the current one is computed.
 struct DecFrags {
   bf16x8_t k[2][4];  // K' key 16kh + col, channels 32ds + 8qd .. +8
-  bf16x8_t v[8];     // V^T channel 16db + col, keys 4qd .. +4 and 16 + 4qd .. +4
+  bf16x8_t v[8];     // V channel 16db + col, keys 4qd .. +4 and 16 + 4qd .. +4
 };
 
-__device__ __forceinline__ void dec_load(const uint16_t* kbase, const uint16_t* vbase, int slot0, int cap,
-                                         int col, int qd, DecFrags& f) {
+// A cache block holds these fragments lane by lane (K: fragment 4kh + ds,
+// V: fragment db; 16 bytes per lane), so each load reads 1 KiB in order.
+__device__ __forceinline__ void dec_load(const uint16_t* kblk, const uint16_t* vblk, int lane,
+                                         DecFrags& f) {
+  const uint4* kp = reinterpret_cast<const uint4*>(kblk) + lane;
+  const uint4* vp = reinterpret_cast<const uint4*>(vblk) + lane;
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
-      f.k[kh][ds] = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(kbase + (size_t)(slot0 + 16 * kh + col) * kD + 32 * ds + 8 * qd));
-  // V^T keys in the order in which this lane holds P: 4qd .. +4, then 16 + 4qd .. +4
+    for (int ds = 0; ds < 4; ++ds) f.k[kh][ds] = __builtin_bit_cast(bf16x8_t, kp[(4 * kh + ds) * 64]);
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    const uint16_t* vr = vbase + (size_t)(16 * db + col) * cap + slot0;
-    const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * qd);
-    const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * qd);
-    f.v[db] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-  }
+  for (int db = 0; db < 8; ++db) f.v[db] = __builtin_bit_cast(bf16x8_t, vp[db * 64]);
 }
 
 __global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__ cache_len, int cap,
@@ -1173,9 +1186,9 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__
       w = *reinterpret_cast<const uint4*>(ws.q + ((size_t)b * kH + g * kHpg + col) * kD + 32 * ds + 8 * qd);
     qf[ds] = __builtin_bit_cast(bf16x8_t, w);
   }
-  const uint16_t* kbase = k_cache + ((size_t)b * kG + g) * cap * (size_t)kD;
-  const uint16_t* vbase = vt_cache + ((size_t)b * kG + g) * kD * (size_t)cap;
-  auto slot_of = [&](int blk) { return window > 0 ? (blk * kDecBlock) % cap : blk * kDecBlock; };
+  const size_t blk0 = ((size_t)b * kG + g) * (cap / kDecBlock);
+  // cache block of token block blk (a ring of cap / 32 blocks on sliding layers)
+  auto cblk = [&](int blk) { return blk0 + (window > 0 ? blk % (cap / kDecBlock) : blk); };
 
   float m = -INFINITY, l = 0.f;
   f32x4 acc[8];
@@ -1183,9 +1196,12 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__
   for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   DecFrags cur, nxt;
-  dec_load(kbase, vbase, slot_of(blk_lo + bs), cap, col, qd, cur);
+  dec_load(k_cache + cblk(blk_lo + bs) * kDecBlockElems, vt_cache + cblk(blk_lo + bs) * kDecBlockElems,
+           lane, cur);
   for (int blk = blk_lo + bs; blk < blk_lo + be; ++blk) {
-    if (blk + 1 < blk_lo + be) dec_load(kbase, vbase, slot_of(blk + 1), cap, col, qd, nxt);
+    if (blk + 1 < blk_lo + be)
+      dec_load(k_cache + cblk(blk + 1) * kDecBlockElems, vt_cache + cblk(blk + 1) * kDecBlockElems, lane,
+               nxt);
     f32x4 sc[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {

@@ -190,10 +190,17 @@ const char* flint_attn_strerror(int status);
  * sinks, window, positions and flags.
  *
  * Cache layout (caller-owned device memory, one pair per layer), head-major so
- * that every (sequence, kv head) streams one contiguous region:
- *   k_cache  [batch][4][cache_cap][128] bf16: RMSNorm-ed, RoPE-rotated keys
- *            (as flint_attn_fwd forms them before its bf16 rounding);
- *   vt_cache [batch][4][128][cache_cap] bf16: values, transposed.
+ * that every (sequence, kv head) streams one contiguous region, in blocks of
+ * 32 slots stored in the order the decode products read them (each 8 KiB
+ * block is read as eight contiguous 1 KiB loads):
+ *   k_cache [batch][4][cache_cap/32][2][4][64][8] bf16: RMSNorm-ed,
+ *           RoPE-rotated keys (as flint_attn_fwd forms them before its bf16
+ *           rounding). Element [b][g][blk][kh][ds][l][e] is channel
+ *           32 ds + 8 (l / 16) + e of the key in slot 32 blk + 16 kh + l % 16.
+ *   vt_cache [batch][4][cache_cap/32][8][64][8] bf16: values. Element
+ *           [b][g][blk][db][l][e] is channel 16 db + l % 16 of the value in
+ *           slot 32 blk + 4 (l / 16) + e for e < 4 and
+ *           32 blk + 16 + 4 (l / 16) + e - 4 for e >= 4.
  * Token t of a sequence sits in slot t of a full layer (window = 0) and in
  * slot t % cache_cap of a sliding layer, which needs cache_cap >= window.
  * cache_cap must be a positive multiple of 32; both pointers 16-byte aligned.

@@ -144,7 +144,8 @@ def test_large_logits():
 
 
 def test_cache_contents_match_oracle_keys():
-    """K' rows are the oracle's RMSNorm + RoPE of k rounded to bf16; V^T holds v exactly."""
+    """K' rows are the oracle's RMSNorm + RoPE of k rounded to bf16; V holds v exactly
+    (both read back through the block layout the header documents)."""
     layer = SLIDING
     n = 700  # wraps the 544-slot ring: slots hold tokens 156..699
     wl = make_custom(4006, [n], layers=(layer,), positions="random")
@@ -154,12 +155,12 @@ def test_cache_contents_match_oracle_keys():
     cap = cache.cap
     tok = np.arange(n - cap, n)
     slots = tok % cap
-    got_k = cache.k[0].float().cpu().numpy().astype(np.float64)[:, slots, :]  # [4, cap, 128]
+    got_k = cache.dense_keys()[0].float().cpu().numpy().astype(np.float64)[:, slots, :]  # [4, n, 128]
     ref_k = kref[tok].transpose(1, 0, 2)
     err = np.abs(got_k - ref_k)
     assert np.all(err <= 2.0 ** -8 * np.abs(ref_k) + 1e-6), f"K' max err {err.max():.3g}"
-    got_v = cache.vt[0].cpu()[:, :, torch.as_tensor(slots)]  # [4, 128, cap]
-    ref_v = wl.v[torch.as_tensor(tok)].permute(1, 2, 0)
+    got_v = cache.dense_values()[0].cpu()[:, torch.as_tensor(slots), :]  # [4, n, 128]
+    ref_v = wl.v[torch.as_tensor(tok)].permute(1, 0, 2)
     assert torch.equal(got_v, ref_v)
 
 
