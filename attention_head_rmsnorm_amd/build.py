@@ -14,7 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SRCS = [os.path.join(CSRC, f) for f in ("flint_attn.hip", "flint_bwd.hip", "flint_bshd.hip", "flint_proj.hip")]
+SRCS = [os.path.join(CSRC, f) for f in ("flint_attn.hip", "flint_decode.hip", "flint_bwd.hip", "flint_bshd.hip", "flint_proj.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflint_attn.so")
 
