@@ -110,3 +110,35 @@ def test_random_backward(seed):
                      sink_std=float(rng.uniform(0.5, 3.0)))
     layer = Layer(window=int(rng.choice(WINDOWS)), use_rope=bool(rng.random() < 0.6))
     check_backward(wl, layer, f"random {seed} n={n} T={sum(lengths)} window={layer.window}")
+
+
+@pytest.mark.parametrize("seed", list(range(7300, 7304)))
+def test_random_decode(seed):
+    from .test_gpu_decode import _decode_and_check
+
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 9))
+    window = int(rng.choice([0, 64, 513]))
+    layer = Layer(window=window, use_rope=window > 0 or bool(rng.random() < 0.5))
+    prefix = [int(x) for x in rng.integers(0, 1500, B)]
+    steps = 2
+    wl = make_custom(seed, [p + steps for p in prefix], layers=(layer,),
+                     positions=["local", "random"][int(rng.integers(0, 2))],
+                     sink_std=float(rng.uniform(0.5, 3.0)))
+    cap = 0 if window > 0 else max(prefix) + steps + 32
+    _decode_and_check(wl, layer, prefix, steps, cap, f"random {seed} B={B} window={window}")
+
+
+@pytest.mark.parametrize("seed", list(range(7400, 7404)))
+def test_random_fp16_forward(seed):
+    from .test_gpu_fp16 import check
+
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 8))
+    lengths = [int(x) for x in rng.integers(1, 600, n)]
+    wl = make_custom(seed, lengths, layout="thd", dtype="float32",
+                     positions=["local", "random", "none"][int(rng.integers(0, 3))],
+                     norm_scale=float(rng.uniform(0.3, 2.0)))
+    layer = Layer(window=int(rng.choice(WINDOWS)), use_rope=bool(rng.random() < 0.6))
+    _log(f"[gpu] random FP16 {seed}: n={n} T={sum(lengths)} window={layer.window} rope={layer.use_rope}")
+    check(wl, layer, what=f"random fp16 {seed}")
