@@ -25,7 +25,7 @@ namespace flint {
 // occupies 32 consecutive slots.
 constexpr int kDecBlock = 32;         // tokens per step of the decode attention
 constexpr int kDecMinSplitBlocks = 2;  // smallest split (64 tokens), sizes the workspace
-constexpr int kDecMaxSplitBlocks = 8;  // largest split (256 tokens)
+constexpr int kDecMaxSplitBlocks = 16;  // largest split (512 tokens)
 constexpr int kDecMergeLanes = 32;     // splits merged in parallel per (sequence, head)
 constexpr int kDecBlockElems = kDecBlock * kD;  // bf16 elements of one K' or V cache block
 
