@@ -1027,7 +1027,7 @@ using namespace flint;
 extern "C" size_t flint_attn_workspace_bytes(int32_t total_tokens, int32_t n_seqs,
                                              int32_t max_seqlen, int32_t num_kv_heads,
                                              int32_t head_dim) {
-  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return 0;
+  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0 || max_seqlen > kMaxSeqLen) return 0;
   if (num_kv_heads != kG || head_dim != kD) return 0;
   return make_layout(total_tokens, n_seqs).total;
 }
@@ -1089,7 +1089,8 @@ static int fwd_impl(const void* q, const void* k, const void* v, const float* q_
                     float* lse, void* stream, int32_t phases, bool f16 = false) {
   if (phases <= 0 || (phases & ~FLINT_PHASE_ALL)) return FLINT_ERR_VALUE;
   if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return FLINT_ERR_SHAPE;
-  if (num_q_heads != kH || num_kv_heads != kG || head_dim != kD) return FLINT_ERR_UNSUPPORTED;
+  if (num_q_heads != kH || num_kv_heads != kG || head_dim != kD || max_seqlen > kMaxSeqLen)
+    return FLINT_ERR_UNSUPPORTED;
   if (window < 0 || !(eps > 0.f) || !isfinite(eps)) return FLINT_ERR_VALUE;
   if (use_rope && (!(rope_theta > 0.f) || !isfinite(rope_theta))) return FLINT_ERR_VALUE;
   if (total_tokens == 0) return FLINT_OK;
@@ -1178,7 +1179,7 @@ extern "C" int flint_attn_fwd_lse(const void* q, const void* k, const void* v,
 extern "C" size_t flint_attn_f16_workspace_bytes(int32_t total_tokens, int32_t n_seqs,
                                                  int32_t max_seqlen, int32_t num_kv_heads,
                                                  int32_t head_dim) {
-  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return 0;
+  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0 || max_seqlen > kMaxSeqLen) return 0;
   if (num_kv_heads != kG || head_dim != kD) return 0;
   return make_layout(total_tokens, n_seqs, true, true).total;
 }

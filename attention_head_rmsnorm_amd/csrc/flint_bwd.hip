@@ -1100,7 +1100,7 @@ using namespace flint;
 extern "C" size_t flint_attn_bwd_workspace_bytes(int32_t total_tokens, int32_t n_seqs,
                                                  int32_t max_seqlen, int32_t num_kv_heads,
                                                  int32_t head_dim) {
-  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return 0;
+  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0 || max_seqlen > kMaxSeqLen) return 0;
   if (num_kv_heads != kG || head_dim != kD) return 0;
   return make_bwd_layout(total_tokens, n_seqs).total;
 }
@@ -1115,7 +1115,8 @@ extern "C" int flint_attn_bwd(const void* q, const void* k, const void* v, const
                               size_t workspace_bytes, void* dq, void* dk, void* dv,
                               float* dq_norm_w, float* dk_norm_w, float* dsink, void* stream) {
   if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return FLINT_ERR_SHAPE;
-  if (num_q_heads != kH || num_kv_heads != kG || head_dim != kD) return FLINT_ERR_UNSUPPORTED;
+  if (num_q_heads != kH || num_kv_heads != kG || head_dim != kD || max_seqlen > kMaxSeqLen)
+    return FLINT_ERR_UNSUPPORTED;
   if (window < 0 || !(eps > 0.f) || !isfinite(eps)) return FLINT_ERR_VALUE;
   if (use_rope && (!(rope_theta > 0.f) || !isfinite(rope_theta))) return FLINT_ERR_VALUE;
   if (!dq_norm_w || !dk_norm_w || !dsink) return FLINT_ERR_NULL;

@@ -35,6 +35,10 @@ constexpr float kRescaleSlack = 8.0f;
 // and l <= 2^56 * 2^18 keys leave FP32 headroom for |v| up to ~2^50.
 constexpr float kStaticBound = 56.0f;
 constexpr int kStages = 4;  // LDS ring depth of the attention kernel
+// Longest sequence the kernels take (FLINT_MAX_SEQLEN): a buffer resource
+// covering one sequence's key tiles (32 KiB per 64 keys forward, 48 KiB
+// backward) then stays within its 32-bit byte count.
+constexpr int kMaxSeqLen = FLINT_MAX_SEQLEN;
 constexpr int kFragAhead = 4;  // MFMA operand fragments read ahead of their use
 constexpr int kHdrKMax = 4;    // header slots of the per-kv-head key-norm maxima
 // Word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs: 32-bit

@@ -82,9 +82,13 @@ typedef enum flint_status {
 #define FLINT_DEV_CACHE 32       /* decode: cache_len[b] < 0, or a full layer's cache
                                     cannot hold the token (cache_len[b] >= cache_cap) */
 
+/* Longest sequence (tokens) the prefill forward and backward take: 2^21. */
+#define FLINT_MAX_SEQLEN 2097152
+
 /*
  * Bytes of device workspace flint_attn_fwd needs for these sizes; 0 when the
- * sizes are invalid (negative, or heads / head_dim unsupported). The value
+ * sizes are invalid (negative, max_seqlen above FLINT_MAX_SEQLEN, or heads /
+ * head_dim unsupported). The value
  * only grows with each argument. It holds the work schedule and the
  * normalized, rotated K and the V tiles of every sequence, laid out for the
  * attention kernel (about 2 KiB per token and 256 KiB per sequence, rounded
@@ -107,7 +111,8 @@ size_t flint_attn_workspace_bytes(int32_t total_tokens, int32_t n_seqs, int32_t 
  *   seqused    int32 [n_seqs] valid prefix length of each sequence (trailing
  *              padding), or NULL when every token is valid
  *   n_seqs, max_seqlen, total_tokens (T): sizes; max_seqlen bounds every
- *              cu[s+1] - cu[s]
+ *              cu[s+1] - cu[s] and is at most FLINT_MAX_SEQLEN (else
+ *              FLINT_ERR_UNSUPPORTED)
  *   num_q_heads, num_kv_heads, head_dim: must be 32, 4, 128
  *   window     keys per query including the current token (513 on Flint's
  *              sliding layers), or 0 for full causal attention
@@ -378,8 +383,8 @@ int flint_attn_fwd_lse(const void* q, const void* k, const void* v, const float*
                        int32_t use_rope, float rope_theta, float eps, void* workspace,
                        size_t workspace_bytes, void* out, float* lse, void* stream);
 
-/* Workspace size in bytes for flint_attn_bwd (0 for invalid sizes or an
- * unsupported head layout). It holds the normalized operands, per-chunk FP32
+/* Workspace size in bytes for flint_attn_bwd (0 for invalid sizes,
+ * max_seqlen above FLINT_MAX_SEQLEN or an unsupported head layout). It holds the normalized operands, per-chunk FP32
  * partial sums of dk and dv, and the per-block terms of the parameter
  * gradients. */
 size_t flint_attn_bwd_workspace_bytes(int32_t total_tokens, int32_t n_seqs, int32_t max_seqlen,

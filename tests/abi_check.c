@@ -42,6 +42,9 @@ int main(void) {
   CHECK(flint_attn_decode_workspace_bytes(64, 8192) > 0);
   CHECK(flint_attn_bshd_plan_bytes(2, 4) >= 4 * (8 + 6 * 8));
   CHECK(flint_attn_bshd_plan_bytes(-1, 4) == 0);
+  CHECK(flint_attn_workspace_bytes(FLINT_MAX_SEQLEN, 1, FLINT_MAX_SEQLEN, 4, 128) > 0);
+  CHECK(flint_attn_workspace_bytes(FLINT_MAX_SEQLEN, 1, FLINT_MAX_SEQLEN + 1, 4, 128) == 0);
+  CHECK(flint_attn_bwd_workspace_bytes(64, 1, FLINT_MAX_SEQLEN + 1, 4, 128) == 0);
 
   /* forward: validation before any launch */
   CHECK(fwd(NULL, 64, 32, 513, ws) == FLINT_ERR_NULL);
@@ -51,6 +54,8 @@ int main(void) {
   CHECK(fwd(FAKE_AT(8), 64, 32, 513, ws) == FLINT_ERR_ALIGN);
   CHECK(fwd(FAKE, 64, 32, 513, 16) == FLINT_ERR_WORKSPACE);
   CHECK(fwd(NULL, 0, 32, 513, 0) == FLINT_OK); /* zero tokens: nothing to do */
+  CHECK(flint_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, NULL, 1, FLINT_MAX_SEQLEN + 1, 64, 32,
+                       4, 128, 0, 0, 1.0e6f, 1.0e-6f, FAKE, ws, FAKE, NULL) == FLINT_ERR_UNSUPPORTED);
   CHECK(flint_attn_fwd_phases(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, NULL, 1, 64, 64, 32, 4,
                               128, 513, 1, 1.0e6f, 1.0e-6f, FAKE, ws, FAKE, NULL, 0) == FLINT_ERR_VALUE);
   CHECK(flint_attn_fwd_phases(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, NULL, 1, 64, 64, 32, 4,
@@ -69,6 +74,9 @@ int main(void) {
                        FAKE, FAKE, NULL) == FLINT_ERR_SHAPE);
   CHECK(flint_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, NULL, 1, 64, 64, 16, 4, 128,
                        513, 1, 1.0e6f, 1.0e-6f, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
+                       FAKE, FAKE, NULL) == FLINT_ERR_UNSUPPORTED);
+  CHECK(flint_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, NULL, 1, FLINT_MAX_SEQLEN + 1, 64, 32,
+                       4, 128, 0, 0, 1.0e6f, 1.0e-6f, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
                        FAKE, FAKE, NULL) == FLINT_ERR_UNSUPPORTED);
 
   /* decode */

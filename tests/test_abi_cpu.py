@@ -61,6 +61,18 @@ def test_workspace_bytes_monotone_and_rejects_bad_sizes():
     assert ws(8192, 1, 8192) >= 4 * (8192 // 64 + 1) * 32768
 
 
+# FLINT_MAX_SEQLEN of the header: the longest sequence the prefill kernels take
+MAX_SEQLEN = int(re.search(r"#define FLINT_MAX_SEQLEN (\d+)", open(HEADER).read()).group(1))
+
+
+def test_sequence_length_limit():
+    assert MAX_SEQLEN == 1 << 21
+    for ws in (fa.flint_attn_workspace_bytes, fa.flint_attn_f16_workspace_bytes,
+               fa.flint_attn_bwd_workspace_bytes):
+        assert ws(MAX_SEQLEN, 1, MAX_SEQLEN) > 0
+        assert ws(MAX_SEQLEN, 1, MAX_SEQLEN + 1) == 0
+
+
 def _call(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, q_norm_w=FAKE, k_norm_w=FAKE, sink=FAKE, positions=0,
              cu_seqlens=FAKE, seqused=0, n_seqs=1, max_seqlen=64, total_tokens=64, num_q_heads=32,
@@ -78,6 +90,7 @@ def _call(**over):
     (dict(num_q_heads=16), fa.FLINT_ERR_UNSUPPORTED),
     (dict(num_kv_heads=8), fa.FLINT_ERR_UNSUPPORTED),
     (dict(head_dim=64), fa.FLINT_ERR_UNSUPPORTED),
+    (dict(max_seqlen=MAX_SEQLEN + 1), fa.FLINT_ERR_UNSUPPORTED),
     (dict(window=-1), fa.FLINT_ERR_VALUE),
     (dict(eps=0.0), fa.FLINT_ERR_VALUE),
     (dict(eps=float("nan")), fa.FLINT_ERR_VALUE),
