@@ -1,0 +1,109 @@
+"""GPU: one sequence of FLINT_MAX_SEQLEN tokens (2^21), the longest the prefill takes.
+
+At this size the host cannot hold FP64 copies of the inputs, so the checks are
+built to need none:
+- the sliding RoPE layer is checked row by row against the oracle on each
+  sampled row's own window (its 513 keys with their true positions), which is
+  the whole of what that row depends on;
+- the full NoPE layer uses inputs whose answer has a closed form at any size:
+  zero queries make every logit 0, so with a sink of -inf every row averages
+  the values of its keys 0..t uniformly. Value channels set to a ramp, ones and
+  an alternating sign then give prefix means, ones and (0 or 1/(t+1)). Wrong
+  tile data or offsets along the 32,768 key tiles of the last rows show in
+  them; per-row parity at long lengths is the 131,072-token sampled test.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import attention_head_rmsnorm_amd as fa
+from oracle import flint_attention
+from workload import draw_large, draw_large_params
+
+from .common import f64
+
+pytestmark = pytest.mark.gpu
+
+T = 1 << 21  # FLINT_MAX_SEQLEN of include/flint_attn.h
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()
+    torch.cuda.init()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def test_max_seqlen_sliding_rope_rows():
+    d = torch.device("cuda", 0)
+    _log(f"[gpu] max seqlen sliding RoPE: one sequence of {T} tokens")
+    q, k, v = draw_large(2021, T, d)
+    qw, kw, sk = draw_large_params(2021)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=d)
+    out = fa.flint_attn(q, k, v, qw.to(d), kw.to(d), sk.to(d), cu_seqlens=cu, max_seqlen=T,
+                        window=513, use_rope=True)
+    torch.cuda.synchronize()
+    vmax = float(v.abs().max())
+    rng = np.random.default_rng(7)
+    rows = sorted({0, 1, 63, 64, 511, 512, 513, 4095, 1 << 20, (1 << 20) + 31, T - 64, T - 33,
+                   T - 32, T - 1} | {int(x) for x in rng.integers(0, T, 26)})
+    errs = []
+    for t in rows:
+        lo = max(0, t - 512)
+        ref = flint_attention(f64(q[lo:t + 1].cpu()), f64(k[lo:t + 1].cpu()), f64(v[lo:t + 1].cpu()),
+                              f64(qw), f64(kw), f64(sk), np.array([0, t + 1 - lo]),
+                              positions=np.arange(lo, t + 1), window=513, use_rope=True,
+                              rows=[t - lo])[0]
+        errs.append(np.abs(out[t].float().cpu().numpy().astype(np.float64) - ref))
+    e = np.stack(errs)
+    _log(f"      rows {len(rows)} max_frac {e.max() / vmax:.3g} mean_frac {e.mean() / vmax:.3g}")
+    assert e.max() <= 2e-2 * vmax and e.mean() <= 1e-3 * vmax
+    del q, k, v, out
+
+
+def test_max_seqlen_full_uniform_weights():
+    d = torch.device("cuda", 0)
+    _log(f"[gpu] max seqlen full NoPE, closed form: one sequence of {T} tokens")
+    q = torch.zeros(T, 32, 128, dtype=torch.bfloat16, device=d)
+    k = draw_large(2022, T, d)[1]
+    j = torch.arange(T, device=d)
+    ramp = (j.double() / T).to(torch.bfloat16)
+    alt = (1 - 2 * (j % 2)).to(torch.bfloat16)
+    v = torch.zeros(T, 4, 128, dtype=torch.bfloat16, device=d)
+    v[:, :, 0] = ramp[:, None]
+    v[:, :, 1] = 1.0
+    v[:, :, 2] = alt[:, None]
+    qw, kw, _ = draw_large_params(2022)
+    sk = torch.full((32,), float("-inf"), dtype=torch.float32, device=d)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=d)
+    out = fa.flint_attn(q, k, v, qw.to(d), kw.to(d), sk, cu_seqlens=cu, max_seqlen=T, window=0,
+                        use_rope=False)
+    torch.cuda.synchronize()
+    del q, k
+    cnt = (j + 1).double()
+    exp_ramp = torch.cumsum(ramp.double(), 0) / cnt
+    exp_alt = torch.cumsum(alt.double(), 0) / cnt
+    assert bool((out[:, :, 1] == 1).all()), "the weights of a row do not sum to 1"
+    assert bool((out[:, :, 3:] == 0).all())
+    # Relative bound: the bf16 output rounding (2^-9) plus FP32 accumulation of
+    # up to 2^17 tile-step partial sums (4 per 64-key tile) into the running
+    # output, each add off by at most one unit in the last place (2^-23) when
+    # the matrix cores do not round to nearest: 2^17 * 2^-23 = 2^-6. Measured
+    # about 2e-3 on the ramp at 2^21 keys.
+    rel = 2.0 ** -9 + 2.0 ** -6
+    e0 = (out[:, :, 0].double() - exp_ramp[:, None]).abs()
+    e2 = (out[:, :, 2].double() - exp_alt[:, None]).abs()
+    tol0 = rel * exp_ramp[:, None] + 1e-9
+    tol2 = rel * exp_alt[:, None].abs() + 1e-9
+    _log(f"      ramp max rel {float((e0 / (exp_ramp[:, None] + 1e-30)).max()):.3g}, "
+         f"alternating max abs {float(e2.max()):.3g}")
+    assert bool((e0 <= tol0).all()) and bool((e2 <= tol2).all())
+    del v, out

@@ -15,4 +15,6 @@ from .gen import (  # noqa: F401
     make_long_decode,
     draw_block,
     draw_dout,
+    draw_large,
+    draw_large_params,
 )

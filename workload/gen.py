@@ -279,3 +279,27 @@ def draw_block(seed: int, T: int, hidden: int = 2048):
     w_v = _bf16(_normal(rng, (NUM_KV_HEADS * HEAD_DIM, hidden), 0.02))
     w_o = _bf16(_normal(rng, (hidden, NUM_Q_HEADS * HEAD_DIM), 0.02))
     return x, w_q, w_k, w_v, w_o
+
+
+def draw_large(seed: int, T: int, device, chunk: int = 1 << 16):
+    """q [T, 32, 128], k and v [T, 4, 128], bf16 ~ N(0, 1), drawn on `device`
+    in chunks of `chunk` tokens, for sizes whose host copy would not fit; the
+    same seed (and chunk) gives the same tensors. Norm weights and sinks come
+    from `draw_large_params`."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = []
+    for heads in (NUM_Q_HEADS, NUM_KV_HEADS, NUM_KV_HEADS):
+        t = torch.empty(T, heads, HEAD_DIM, dtype=torch.bfloat16, device=device)
+        for a in range(0, T, chunk):
+            b = min(T, a + chunk)
+            t[a:b] = torch.randn(b - a, heads, HEAD_DIM, generator=g, device=device).to(torch.bfloat16)
+        out.append(t)
+    return tuple(out)
+
+
+def draw_large_params(seed: int):
+    """q_norm_w, k_norm_w ~ N(1, 0.1) [128] and sinks ~ N(0, 1) [32], float32 on the host."""
+    rng = np.random.default_rng(seed + 15485863)
+    qw, kw, sk = _draw_params(rng, 1.0)
+    return qw, kw, sk
