@@ -240,8 +240,9 @@ int flint_attn_kv_append(const void* k, const void* v, const float* k_norm_w,
  * = cache_len[b]) to the cache as flint_attn_kv_append does, then writes its
  * attention output out [batch][32][128] bf16 over tokens
  * max(0, t - window + 1) .. t (window > 0) or 0 .. t (window = 0),
- * t = cache_len[b], with the sink. Split over the keys (256 per split) and
- * merged, so one sequence spreads over the GPU. Errors as for
+ * t = cache_len[b], with the sink. Split over the keys (64 to 512 per split,
+ * chosen from the batch and cache size) and merged, so one sequence spreads
+ * over the GPU. Errors as for
  * flint_attn_kv_append; a sequence with a device-data error gets zero rows. */
 int flint_attn_decode(const void* q, const void* k, const void* v, const float* q_norm_w,
                       const float* k_norm_w, const float* sink, const int32_t* positions,
