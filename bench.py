@@ -10,9 +10,10 @@ a seeded generator, resident in HBM before the timed region. One step = one
 flint_attn_fwd call (schedule, K/V prologue, attention kernel).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config tstar|c1|c2|c3|c4|c4full|c5]
-       python bench.py --decode [--decode-batch B] [--decode-len L] [--decode-window W]
+       python bench.py --decode [--decode-batch B] [--decode-len L] [--decode-window W] [--graph]
                                          (one decode step per sequence over an L-token
-                                          KV cache: HBM GB/s against 8 TB/s)
+                                          KV cache: HBM GB/s against 8 TB/s; --graph
+                                          replays the step from a HIP graph)
        python bench.py --backward [--config ...]   (one flint_attn_bwd call per step)
        python bench.py --fp16 [--config ...]       (the FP16 attention-compute variant)
        python bench.py --bshd-docs                 (BSHD rows of packed documents, in place and with holes)
@@ -193,8 +194,23 @@ def decode_bench(args):
         raise RuntimeError(f"decode device error flags {flags}")
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    graph = None
+    if args.graph:
+        # the whole step (its four launches) captured once and replayed: what a
+        # serving loop pays once launch overhead is gone
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            st = fa.flint_attn_decode(*call[:-1], int(torch.cuda.current_stream(dev).cuda_stream))
+        if st != 0:
+            raise RuntimeError(fa.flint_attn_strerror(st))
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+            continue
         st = fa.flint_attn_decode(*call)
         if st != 0:
             raise RuntimeError(fa.flint_attn_strerror(st))
@@ -217,9 +233,10 @@ def decode_bench(args):
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 cache contents, q, k, v)",
         "config": {"workload": f"decode, batch {B}, {L} cached tokens, "
-                               + (f"sliding window {W} (RoPE)" if W else "full attention (NoPE)"),
+                               + (f"sliding window {W} (RoPE)" if W else "full attention (NoPE)")
+                               + (", replayed from a HIP graph" if args.graph else ""),
                    "batch": B, "cached_tokens": L, "window": W, "attended_tokens": attended,
-                   "cache_cap": cache.cap},
+                   "cache_cap": cache.cap, "hip_graph": bool(args.graph)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": alg, "traffic": None},
@@ -696,6 +713,8 @@ def main():
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--decode-len", type=int, default=8192)
     ap.add_argument("--decode-window", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="with --decode: capture one step in a HIP graph and time its replays")
     args = ap.parse_args()
 
     if args.gpus != 1:

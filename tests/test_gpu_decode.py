@@ -234,3 +234,43 @@ def test_very_long_full_context():
     err = np.abs(to_np(out) - ref)
     _log(f"[decode] full {L}: max err {err.max() / vmax:.3e} x max|V|")
     assert err.max() <= 2e-2 * vmax and err.mean() <= 1e-3 * vmax
+
+
+def test_decode_step_replayed_from_a_hip_graph():
+    """One decode step (append, attention, merge: four launches) captured in a
+    HIP graph. Every replay, with eager work and synchronizations between the
+    replays, gives the eager step's output bit for bit (the step rewrites the
+    same cache slot, so it is idempotent)."""
+    d = _d()
+    B, L = 4, 700
+    rng = np.random.default_rng(31)
+    bf = lambda *shape: torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16).to(d)  # noqa: E731
+    qw = torch.from_numpy((1 + 0.1 * rng.standard_normal(128)).astype(np.float32)).to(d)
+    kw = torch.from_numpy((1 + 0.1 * rng.standard_normal(128)).astype(np.float32)).to(d)
+    sinks = torch.from_numpy(rng.standard_normal(32).astype(np.float32)).to(d)
+    cache = fa.KVCache(B, 0, max_tokens=L + 1, use_rope=False, device=d)
+    cache.append(bf(B, L, 4, 128), bf(B, L, 4, 128), kw)
+    q1, k1, v1 = bf(B, 32, 128), bf(B, 4, 128), bf(B, 4, 128)
+    p = lambda t: int(t.data_ptr())  # noqa: E731
+
+    def step(out, stream):
+        return fa.flint_attn_decode(p(q1), p(k1), p(v1), p(qw), p(kw), p(sinks), 0, p(cache.length), B,
+                                    p(cache.k), p(cache.vt), cache.cap, 32, 4, 128, 0, 0, 1.0e6, 1.0e-6,
+                                    p(cache.workspace), cache.workspace.numel(), p(out),
+                                    int(stream.cuda_stream))
+
+    out_e = torch.empty(B, 32, 128, dtype=torch.bfloat16, device=d)
+    assert step(out_e, torch.cuda.current_stream(d)) == 0
+    torch.cuda.synchronize()
+    out_g = torch.empty_like(out_e)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        assert step(out_g, torch.cuda.current_stream(d)) == 0
+    for i in range(4):
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {i} differs from the eager step"
+        float(torch.randn(1 << 20, device=d).sum())  # eager work between replays
+    assert cache.device_status()[0] == fa.FLINT_OK
