@@ -117,13 +117,22 @@ __global__ __launch_bounds__(64 * (1 + kHpg)) void decode_append_kernel(
     uint16_t* __restrict__ vt_cache, DecWs ws) {
   const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if ((i | g | b) == 0) {
+    // The call's device-data flags, written whole by this one block (so no
+    // reset launch is needed): a sequence whose length is negative or whose
+    // new tokens overflow a full layer's cache is skipped everywhere.
+    int bad = 0;
+    for (int s = threadIdx.x; s < gridDim.z; s += blockDim.x) {
+      const int l = cache_len[s];
+      bad |= (l < 0 || (window == 0 && l > cap - n_new)) ? 1 : 0;
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) ws.hdr[0] = bad ? FLINT_DEV_CACHE : 0;
+  }
   const int len = cache_len[b];
   const int t = len + i;
   const int slot = len >= 0 ? dec_slot(t, cap, window) : -1;
-  if (slot < 0) {
-    if (threadIdx.x == 0) atomicOr(&ws.hdr[0], FLINT_DEV_CACHE);
-    return;
-  }
+  if (slot < 0) return;
   const bool rope = use_rope != 0;
   const int pos = positions ? positions[(size_t)b * n_new + i] : t;
   const unsigned long long r = rope ? rope_r_of(theta, lane) : 0ull;
@@ -355,7 +364,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const int* __restrict
 
 // Clears the device-data error bits at the start of a decode call (a kernel,
 // not a memset, so the call can be captured in a graph).
-__global__ void decode_reset_kernel(DecWs ws) { ws.hdr[0] = 0; }
 
 }  // namespace flint
 
@@ -421,7 +429,6 @@ extern "C" int flint_attn_kv_append(const void* k, const void* v, const float* k
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int rope = use_rope ? 1 : 0;
   (void)hipGetLastError();
-  decode_reset_kernel<<<1, 1, 0, st>>>(ws);
   decode_append_kernel<<<dim3((unsigned)n_new, kG, (unsigned)batch), 64, 0, st>>>(
       nullptr, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), nullptr, k_norm_w,
       rope ? positions : nullptr, cache_len, n_new, cache_cap, window, rope, (double)rope_theta, eps,
@@ -465,7 +472,6 @@ extern "C" int flint_attn_decode(const void* q, const void* k, const void* v, co
   const uint16_t* kc = static_cast<const uint16_t*>(k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(vt_cache);
   (void)hipGetLastError();
-  decode_reset_kernel<<<1, 1, 0, st>>>(ws);
   decode_append_kernel<<<dim3(1, kG, (unsigned)batch), 64 * (1 + kHpg), 0, st>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       q_norm_w, k_norm_w, rope ? positions : nullptr, cache_len, 1, cache_cap, window, rope,
