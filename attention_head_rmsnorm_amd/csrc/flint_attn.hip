@@ -30,7 +30,9 @@
 //                     scale in log2 units, bf16) is fused in. S^T = K Q^T and
 //                     O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with FP32
 //                     accumulation, over the tiles inside the causal window
-//                     only.
+//                     only. Problems with fewer work items than CUs run on
+//                     attn_half_kernel instead: two 4-wave workgroups per item,
+//                     4 query heads each, so twice the CUs take part.
 //
 // Softmax shift. The QK RMSNorm bounds every logit: by Cauchy-Schwarz
 // |s| = |q'.k'| <= |q'| max|k'| = B for the rounded operands the MFMA
@@ -1068,6 +1070,218 @@ static int64_t attn_groups(int64_t nqmax) {
   return nqmax < per_head ? nqmax : per_head;
 }
 
+// ----------------------------------------------------------------- small problems
+
+// When there are fewer work items than CUs, each item runs on two workgroups
+// of 4 waves, one per query head of its half of the kv head's 8 heads, so the
+// small grid covers twice as many CUs and each workgroup's MFMA work per key
+// tile halves. A workgroup has its own 2-stage LDS ring (64 KiB), fills it with
+// the same direct-to-LDS tile copies, and runs the same logits, softmax and PV
+// steps per 64-key tile as attn_kernel, without the two-group stagger.
+constexpr int kHalfThreads = 256;
+constexpr int kHStages = 2;
+constexpr int kMaxItemsHalf = 512;
+
+// One 16-byte vector per lane of a 32 KiB tile into a stage, for 4 waves.
+__device__ __forceinline__ void load_vec_async4(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
+                                                uint4* stage, int i, int wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc,
+      (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(stage) + i * 4096 + wave * 1024),
+      16, voff, soff + i * 4096, 0, 0);
+}
+
+// tile_logits for 4-wave workgroups: eight tile loads per wave, one after
+// every second MFMA.
+__device__ __forceinline__ void tile_logits_h(const uint4* kt, int lane, const bf16x8* qf, f32x16& s0,
+                                              f32x16& s1, bool load, __amdgpu_buffer_rsrc_t rsrc,
+                                              int voff, int loff, uint4* lstage, int wave) {
+  bf16x8 f[16];
+#pragma unroll
+  for (int i = 0; i < kFragAhead; ++i)
+    f[i] = __builtin_bit_cast(bf16x8, kt[((i & 1) * 8 + (i >> 1)) * 64 + lane]);
+  __builtin_amdgcn_sched_group_barrier(0x100, kFragAhead, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + kFragAhead < 16) {
+      const int j = i + kFragAhead;
+      f[j] = __builtin_bit_cast(bf16x8, kt[((j & 1) * 8 + (j >> 1)) * 64 + lane]);
+    }
+    const int kk = i >> 1;
+    if (i & 1) {
+      s1 = kk == 0 ? mma<false>(f[i], qf[kk], f32x16{}) : mma<false>(f[i], qf[kk], s1);
+    } else {
+      s0 = kk == 0 ? mma<false>(f[i], qf[kk], f32x16{}) : mma<false>(f[i], qf[kk], s0);
+    }
+    if (i + kFragAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if ((i & 1) == 1 && load) load_vec_async4(rsrc, voff, loff, lstage, i >> 1, wave);
+  }
+}
+
+// Grid: 8 consecutive workgroups per group of items, bits 0-1 the kv head and
+// bit 2 which half of its query heads; items are dealt to the groups as in
+// attn_kernel.
+__global__ __launch_bounds__(kHalfThreads, 2) void attn_half_kernel(const uint16_t* __restrict__ q,
+                                                                     const float* __restrict__ q_norm_w,
+                                                                     const float* __restrict__ sink,
+                                                                     const int* __restrict__ positions,
+                                                                     int window, int use_rope, float eps,
+                                                                     Ws ws, void* __restrict__ outp,
+                                                                     float* __restrict__ lse) {
+  __shared__ uint4 smem[kHStages][kTileVec];
+  __shared__ float s_qw[kD];
+  __shared__ unsigned long long s_rope[kD / 2];
+  __shared__ int4 s_items[kMaxItemsHalf];
+  const int g = blockIdx.x & (kG - 1);
+  const int hh = (blockIdx.x >> 2) & 1;
+  const int wg = blockIdx.x >> 3, nwg = gridDim.x >> 3;
+  const int nitems = ws.hdr[2];
+  const int rounds = nitems / nwg, rem = nitems - rounds * nwg;
+  const int nj = min(rounds + (((rounds & 1) ? nwg - 1 - wg : wg) < rem ? 1 : 0), kMaxItemsHalf);
+  if (nj == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int h = g * kHpg + hh * 4 + wave;
+  const int voff = lane * 16 + wave * 1024;
+  const bool rope = use_rope != 0;
+  const bool qpos = rope && positions;
+  const float sk = sink[h] * kLog2e;
+  const float kmax = __uint_as_float((unsigned)ws.hdr[kHdrKMax + g]);
+  if (tid < kD) s_qw[tid] = q_norm_w[tid];
+  if (tid < kD / 2) s_rope[tid] = ws.rope_r[tid];
+  for (int jj = tid; jj < nj; jj += kHalfThreads) {
+    const int2 it = ws.items[item_rank(jj, wg, nwg)];
+    const int4 meta = ws.seq[it.x];
+    s_items[jj] = make_int4(meta.x, meta.z, it.y * kBM, meta.w);
+  }
+  __syncthreads();
+
+  int cj = 0, ck = 0, cn, ctf;
+  {
+    const Item c = item_from(s_items[0], window);
+    cn = c.ntiles;
+    ctf = c.tfirst;
+  }
+  int slot = 0;
+#define FLINT_NEXT_SLOT_H(LOAD, RSRC, LOFF)                     \
+  {                                                             \
+    LOAD = cj < nj;                                             \
+    if (LOAD) {                                                 \
+      RSRC = tiles_rsrc(ws, g, ctf, cn);                        \
+      LOFF = ck * kTileBytes;                                   \
+      if (++ck == cn) {                                         \
+        ck = 0;                                                 \
+        if (++cj < nj) {                                        \
+          const Item c = item_from(s_items[cj], window);        \
+          cn = c.ntiles;                                        \
+          ctf = c.tfirst;                                       \
+        }                                                       \
+      }                                                         \
+    }                                                           \
+  }
+  Item it = item_from(s_items[0], window);
+  {
+    bool ld;
+    __amdgpu_buffer_rsrc_t r;
+    int lo = 0;
+    FLINT_NEXT_SLOT_H(ld, r, lo);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_vec_async4(r, voff, lo, smem[0], i, wave);
+  }
+  QRaw qraw;
+  load_q(q, positions, qpos, it, h, col, half, qraw);
+  bf16x8 qf[8];
+  float qmax;
+  q_prologue<false>(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
+
+  for (int j = 0; j < nj; ++j) {
+    RowState st;
+    st.online = !(sk <= kStaticBound) || !(qmax * kmax * 1.0001f <= kStaticBound);
+    st.m = st.online ? sk : 0.f;
+    st.l0 = (half == 0 && sk != -INFINITY) ? __builtin_amdgcn_exp2f(sk - st.m) : 0.f;
+    st.l1 = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.acc[db][i] = 0.f;
+    const int qrow = it.t0 + col;
+    f32x16 s0, s1;
+    bf16x8 pk[4];
+    for (int k = 0; k < it.ntiles; ++k, ++slot) {
+      // this slot is in LDS, and every wave is done with the other stage,
+      // which the loads below refill
+      ring_barrier_n<0>();
+      bool ld;
+      __amdgpu_buffer_rsrc_t r;
+      int lo = 0;
+      FLINT_NEXT_SLOT_H(ld, r, lo);
+      tile_logits_h(smem[slot % kHStages], lane, qf, s0, s1, ld, r, voff, lo, smem[(slot + 1) % kHStages], wave);
+      tile_softmax<false>(s0, s1, st, pk, (it.tile_lo + k) * kBN, it.t0, qrow, it.u, window, half);
+      tile_pv<false>(smem[slot % kHStages] + kTileVec / 2, lane, pk, st);
+    }
+    const bool more = j + 1 < nj;
+    Item nx = it;
+    if (more) {
+      nx = item_from(s_items[j + 1], window);
+      load_q(q, positions, qpos, nx, h, col, half, qraw);
+    }
+    const float lsum = st.l0 + st.l1;
+    const float lt = lsum + __shfl_xor(lsum, 32);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    uint4 ow[8];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2) {
+        const f32x16& c = st.acc[db];
+        const int o = 8 * r2;
+        const unsigned a0 = pack2(c[o] * inv, c[o + 1] * inv), a1 = pack2(c[o + 2] * inv, c[o + 3] * inv);
+        const unsigned b0 = pack2(c[o + 4] * inv, c[o + 5] * inv), b1 = pack2(c[o + 6] * inv, c[o + 7] * inv);
+        const auto x0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto x1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        ow[2 * db + r2] = make_uint4(x0[0], x1[0], x0[1], x1[1]);
+      }
+    if (more) q_prologue<false>(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(outp) + ((size_t)(it.start + it.t0) * kH + h) * kD * 2, 0,
+        min(it.u - it.t0, kBM) * (kH * kD * 2), kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ob = col * (kH * kD * 2) + (32 * (i >> 1) + 16 * (i & 1) + 8 * half) * 2;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, ow[i]), orsrc, ob, 0, 0);
+    }
+    if (lse) {
+      const float m = st.online ? st.m : 0.f;
+      const float lv = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+      const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+          lse + (size_t)(it.start + it.t0) * kH + h, 0, min(it.u - it.t0, kBM) * (kH * 4), kBufferWord3);
+      if (half == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv), lr, col * (kH * 4), 0, 0);
+    }
+    it = nx;
+  }
+#undef FLINT_NEXT_SLOT_H
+}
+
+// Query blocks per kv head up to which the forward runs on attn_half_kernel:
+// half the CUs per kv head, so every item still gets its two workgroups.
+static int64_t small_limit() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  return n / kG;
+}
+
+// Workgroup pairs per kv head of attn_half_kernel.
+static int64_t attn_groups_half(int64_t nqmax) {
+  int64_t per_head = attn_groups(nqmax);
+  const int64_t need = (nqmax + kMaxItemsHalf - 1) / kMaxItemsHalf;
+  if (per_head < need) per_head = need;
+  return nqmax < per_head ? nqmax : per_head;
+}
+
 extern "C" int flint_attn_device_status(const void* workspace, void* stream, int32_t* flags) {
   if (!workspace || !flags) return FLINT_ERR_NULL;
   if (!aligned(workspace, 256)) return FLINT_ERR_ALIGN;
@@ -1136,6 +1350,9 @@ static int fwd_impl(const void* q, const void* k, const void* v, const float* q_
     if (f16)
       attn_kernel<true><<<grid, kAttnThreads, 0, st>>>(q16, q_norm_w, sink, pos, window, rope, eps,
                                                        ws, out, nullptr);
+    else if (L.nqmax * 2 <= small_limit())
+      attn_half_kernel<<<(unsigned)(attn_groups_half(L.nqmax) * kG * 2), kHalfThreads, 0, st>>>(
+          qh, q_norm_w, sink, pos, window, rope, eps, ws, oh, lse);
     else
       attn_kernel<false><<<grid, kAttnThreads, 0, st>>>(qh, q_norm_w, sink, pos, window, rope, eps,
                                                         ws, oh, lse);
