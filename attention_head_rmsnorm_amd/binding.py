@@ -41,6 +41,9 @@ FLINT_PHASE_KV = 2
 FLINT_PHASE_ATTEND = 4
 FLINT_PHASE_ALL = 7
 
+FLINT_KERNEL_WIDE = 1   # one 8-wave workgroup per work item
+FLINT_KERNEL_SPLIT = 2  # two 4-wave workgroups per work item (small problems)
+
 EXPORTED = (
     "flint_attn_workspace_bytes",
     "flint_attn_fwd",
@@ -61,6 +64,7 @@ EXPORTED = (
     "flint_attn_copy_rows",
     "flint_proj_qkv",
     "flint_proj_out",
+    "flint_attn_fwd_kernel",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -129,6 +133,8 @@ def load_library() -> ctypes.CDLL:
     lib.flint_proj_qkv.restype = ctypes.c_int
     lib.flint_proj_out.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
     lib.flint_proj_out.restype = ctypes.c_int
+    lib.flint_attn_fwd_kernel.argtypes = [i32, i32]
+    lib.flint_attn_fwd_kernel.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -256,6 +262,12 @@ def flint_attn_device_status(workspace, stream):
     flags = ctypes.c_int32(0)
     st = int(load_library().flint_attn_device_status(workspace, stream, ctypes.byref(flags)))
     return st, int(flags.value)
+
+
+def flint_attn_fwd_kernel(total_tokens: int, n_seqs: int) -> int:
+    """FLINT_KERNEL_WIDE or FLINT_KERNEL_SPLIT: the attention kernel a bf16
+    forward of these sizes launches (0 for no tokens, negative on bad sizes)."""
+    return int(load_library().flint_attn_fwd_kernel(total_tokens, n_seqs))
 
 
 def flint_attn_strerror(status: int) -> str:

@@ -44,8 +44,10 @@
 // P = exp2(acc) needs no running max, no per-tile max reduction and no
 // rescaling. Waves with a larger bound take the streaming path: a running max
 // that starts at the sink (m = sink, l = 1), subtracted before exp2 and
-// raised lazily with rescaling. max |k'| is taken over all keys of the kv
-// head, a bound for every item.
+// raised lazily with rescaling. The start is never below -B, the least logit
+// possible: a sink far below every logit (or -INF) then adds ~0 to l without
+// moving the shift away from the logits, where s - m would lose their bits.
+// max |k'| is taken over all keys of the kv head, a bound for every item.
 
 #include <hip/hip_runtime.h>
 
@@ -876,8 +878,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     // Softmax shift: none when the logit bound |q'| max|k'| and the sink stay
     // within kStaticBound; otherwise the streaming path.
     RowState st;
-    st.online = !(sk <= kBound) || !(qmax * kmax * 1.0001f <= kBound);
-    st.m = st.online ? sk : 0.f;
+    const float bnd = qmax * kmax * 1.0001f;
+    st.online = !(sk <= kBound) || !(bnd <= kBound);
+    // Every logit is at least -bnd: a sink far below that (or -INF) leaves
+    // the shift at -bnd, so s - m keeps the precision of the logits.
+    st.m = st.online ? fmaxf(sk, -bnd) : 0.f;
     st.l0 = (half == 0 && sk != -INFINITY) ? __builtin_amdgcn_exp2f(sk - st.m) : 0.f;
     st.l1 = 0.f;
 #pragma unroll
@@ -1198,8 +1203,9 @@ __global__ __launch_bounds__(kHalfThreads, 2) void attn_half_kernel(const uint16
 
   for (int j = 0; j < nj; ++j) {
     RowState st;
-    st.online = !(sk <= kStaticBound) || !(qmax * kmax * 1.0001f <= kStaticBound);
-    st.m = st.online ? sk : 0.f;
+    const float bnd = qmax * kmax * 1.0001f;
+    st.online = !(sk <= kStaticBound) || !(bnd <= kStaticBound);
+    st.m = st.online ? fmaxf(sk, -bnd) : 0.f;  // as in attn_kernel
     st.l0 = (half == 0 && sk != -INFINITY) ? __builtin_amdgcn_exp2f(sk - st.m) : 0.f;
     st.l1 = 0.f;
 #pragma unroll
@@ -1272,6 +1278,19 @@ static int64_t small_limit() {
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
   return n / kG;
+}
+
+// The attention kernel of a bf16 forward over these sizes: the split 4-wave
+// kernel when the query blocks per kv head are at most half the CUs per kv
+// head, else the 8-wave one.
+static bool use_split_kernel(int64_t nqmax) { return nqmax * 2 <= small_limit(); }
+
+extern "C" int flint_attn_fwd_kernel(int32_t total_tokens, int32_t n_seqs) {
+  if (total_tokens < 0 || n_seqs < 0) return FLINT_ERR_SHAPE;
+  if (total_tokens == 0) return 0;
+  if (n_seqs < 1) return FLINT_ERR_SHAPE;
+  return use_split_kernel(make_layout(total_tokens, n_seqs, false).nqmax) ? FLINT_KERNEL_SPLIT
+                                                                           : FLINT_KERNEL_WIDE;
 }
 
 // Workgroup pairs per kv head of attn_half_kernel.
@@ -1350,7 +1369,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const float* q_
     if (f16)
       attn_kernel<true><<<grid, kAttnThreads, 0, st>>>(q16, q_norm_w, sink, pos, window, rope, eps,
                                                        ws, out, nullptr);
-    else if (L.nqmax * 2 <= small_limit())
+    else if (use_split_kernel(L.nqmax))
       attn_half_kernel<<<(unsigned)(attn_groups_half(L.nqmax) * kG * 2), kHalfThreads, 0, st>>>(
           qh, q_norm_w, sink, pos, window, rope, eps, ws, oh, lse);
     else

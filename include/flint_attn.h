@@ -180,6 +180,21 @@ int flint_attn_seqused_from_mask(const uint8_t* mask, int32_t batch, int32_t seq
  */
 int flint_attn_device_status(const void* workspace, void* stream, int32_t* flags);
 
+/*
+ * Which attention kernel flint_attn_fwd (and flint_attn_fwd_lse) launches for
+ * a call of total_tokens tokens in n_seqs sequences; a host-side query that
+ * launches nothing. Problems with fewer 32-token query blocks than CUs run on
+ * two 4-wave workgroups per work item (four query heads each), so that twice
+ * the CUs take part; larger ones on one 8-wave workgroup per item that shares
+ * every key/value tile among the kv head's eight query heads. Both compute
+ * the same layer. Returns FLINT_KERNEL_WIDE or FLINT_KERNEL_SPLIT, 0 when
+ * total_tokens == 0, FLINT_ERR_SHAPE for negative sizes or n_seqs < 1 with
+ * tokens. (The FP16 variant always runs the 8-wave kernel.)
+ */
+#define FLINT_KERNEL_WIDE 1
+#define FLINT_KERNEL_SPLIT 2
+int flint_attn_fwd_kernel(int32_t total_tokens, int32_t n_seqs);
+
 /* A static, human-readable name of a flint_status value. */
 const char* flint_attn_strerror(int status);
 

@@ -46,6 +46,13 @@ int main(void) {
   CHECK(flint_attn_workspace_bytes(FLINT_MAX_SEQLEN, 1, FLINT_MAX_SEQLEN + 1, 4, 128) == 0);
   CHECK(flint_attn_bwd_workspace_bytes(64, 1, FLINT_MAX_SEQLEN + 1, 4, 128) == 0);
 
+  /* which attention kernel a forward launches: a host-side query */
+  CHECK(flint_attn_fwd_kernel(0, 1) == 0);
+  CHECK(flint_attn_fwd_kernel(-1, 1) == FLINT_ERR_SHAPE);
+  CHECK(flint_attn_fwd_kernel(64, 0) == FLINT_ERR_SHAPE);
+  CHECK(flint_attn_fwd_kernel(64, 1) == FLINT_KERNEL_SPLIT);
+  CHECK(flint_attn_fwd_kernel(8192, 1) == FLINT_KERNEL_WIDE);
+
   /* forward: validation before any launch */
   CHECK(fwd(NULL, 64, 32, 513, ws) == FLINT_ERR_NULL);
   CHECK(fwd(FAKE, 64, 16, 513, ws) == FLINT_ERR_UNSUPPORTED);

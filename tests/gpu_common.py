@@ -88,3 +88,41 @@ def check_against_oracle(wl, layer, rows=None, **gpu_kw):
         over["positions"] = None if pos is None else i64(torch.as_tensor(pos))
     ref = oracle_for(wl, layer, rows=rows, **over)
     return grade(got, ref, wl, rows=rows, what=f"{wl.name}/{layer.name}"), out
+
+
+def with_filler(wl, n_fill=2048, seed=90001):
+    """The workload as THD plus one extra seeded document of n_fill tokens.
+
+    THD documents are independent, so the rows of the original sequences keep
+    their exact values; the extra document only raises the number of work
+    items so that the forward runs on the 8-wave kernel (FLINT_KERNEL_WIDE)
+    instead of the split one. BSHD padding becomes THD seqused. Returns
+    (workload, rows of the original tokens)."""
+    from workload.gen import Workload
+
+    rng = np.random.default_rng(seed)
+    T = wl.total_tokens
+
+    def ext(t, shape):
+        x = torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32))
+        return torch.cat([t, x.to(t.dtype)], 0)
+
+    q = ext(wl.q, (n_fill, 32, 128))
+    k = ext(wl.k, (n_fill, 4, 128))
+    v = ext(wl.v, (n_fill, 4, 128))
+    cu = torch.cat([wl.cu_seqlens, torch.tensor([T + n_fill], dtype=torch.int32)])
+    su = None
+    if wl.seqused is not None:
+        su = torch.cat([wl.seqused, torch.tensor([n_fill], dtype=torch.int32)])
+    pos = None
+    if wl.positions is not None:
+        pos = torch.cat([wl.positions, torch.arange(n_fill, dtype=torch.int32)])
+    out = Workload(name=wl.name + "+fill", seed=wl.seed, layout="thd", q=q, k=k, v=v,
+                   q_norm_w=wl.q_norm_w, k_norm_w=wl.k_norm_w, sinks=wl.sinks, cu_seqlens=cu,
+                   seqused=su, positions=pos, layers=list(wl.layers))
+    return out, np.arange(T, dtype=np.int64)
+
+
+def kernel_of(wl):
+    """The attention kernel the forward launches for this workload."""
+    return fa.flint_attn_fwd_kernel(wl.total_tokens, wl.n_seqs)

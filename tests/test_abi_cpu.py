@@ -47,6 +47,25 @@ def test_strerror_covers_every_status():
     assert "unknown" in fa.flint_attn_strerror(-99)
 
 
+def test_fwd_kernel_query():
+    k = fa.flint_attn_fwd_kernel
+    assert k(0, 1) == 0
+    assert k(-1, 1) == fa.FLINT_ERR_SHAPE and k(64, 0) == fa.FLINT_ERR_SHAPE
+    # one 64-token sequence: 2 query blocks, far fewer than CUs -> the split kernel
+    assert k(64, 1) == fa.FLINT_KERNEL_SPLIT
+    # 8192 tokens: 256 query blocks per kv head -> the 8-wave kernel
+    assert k(8192, 1) == fa.FLINT_KERNEL_WIDE
+    # monotone in the number of query blocks
+    seen_wide = False
+    for T in range(32, 4096, 32):
+        r = k(T, 1)
+        assert r in (fa.FLINT_KERNEL_SPLIT, fa.FLINT_KERNEL_WIDE)
+        if r == fa.FLINT_KERNEL_WIDE:
+            seen_wide = True
+        else:
+            assert not seen_wide
+
+
 def test_workspace_bytes_monotone_and_rejects_bad_sizes():
     ws = fa.flint_attn_workspace_bytes
     assert ws(-1, 1, 1) == 0 and ws(1, -1, 1) == 0 and ws(1, 1, -1) == 0

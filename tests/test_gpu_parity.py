@@ -8,6 +8,7 @@ its keys.
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -19,6 +20,7 @@ from workload.gen import FULL, SLIDING
 
 from .common import f64, i64, oracle_for, seq_index
 from .gpu_common import check_against_oracle, grade, run_gpu, to_np
+from .oracle_rows import oracle_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -289,17 +291,26 @@ def test_c4_sampled(li):
     _log(f"      {stats}")
 
 
-def test_tstar_sampled():
+def test_tstar_all_rows():
+    """The benchmark's workload (full NoPE, B=1, S=8192), every row."""
     wl = make_workload("tstar")
-    rows = _rows_sample(wl, 96, 1007)
-    _log(f"[gpu] S=8192 full NoPE sampled parity rows={len(rows)}")
-    stats, _ = check_against_oracle(wl, wl.layers[0], rows=rows)
+    assert fa.flint_attn_fwd_kernel(wl.total_tokens, wl.n_seqs) == fa.FLINT_KERNEL_WIDE
+    _log("[gpu] S=8192 full NoPE parity, all 8192 rows")
+    stats, _ = check_against_oracle(wl, wl.layers[0])
     _log(f"      {stats}")
 
 
-def test_c5_sampled():
+def test_c5_rows_across_sequence():
+    """S=131,072 full NoPE: 1,024 rows evenly spread over the sequence plus the
+    first and last 16 (the oracle computes each row over all its keys)."""
     wl = make_workload("c5")
-    rows = _rows_sample(wl, 16, 1006)
-    _log(f"[gpu] c5 S=131072 sampled parity rows={len(rows)}")
-    stats, _ = check_against_oracle(wl, wl.layers[0], rows=rows)
+    S = wl.total_tokens
+    rows = np.unique(np.concatenate([np.linspace(0, S - 1, 1024).round().astype(np.int64),
+                                     np.arange(16), np.arange(S - 16, S)]))
+    _log(f"[gpu] c5 S=131072 parity rows={len(rows)}")
+    out = run_gpu(wl, wl.layers[0])
+    got = to_np(out[torch.as_tensor(rows, device=out.device)])
+    del out
+    ref = oracle_rows("c5", 0, rows, workers=min(16, os.cpu_count() or 1))
+    stats = grade(got, ref, wl, rows=rows, what="c5")
     _log(f"      {stats}")
