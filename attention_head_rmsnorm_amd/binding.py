@@ -33,6 +33,8 @@ FLINT_ERR_WORKSPACE = -5
 FLINT_ERR_ALIGN = -6
 FLINT_ERR_HIP = -7
 FLINT_ERR_DEVICE_DATA = -8
+FLINT_ERR_TOO_LARGE = -9
+FLINT_ATTN_STATIC_SCRATCH_BYTES = 64 << 20
 
 FLINT_DEV_CACHE = 32
 
@@ -65,6 +67,7 @@ EXPORTED = (
     "flint_proj_qkv",
     "flint_proj_out",
     "flint_attn_fwd_kernel",
+    "flint_attn_fwd_static",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -135,6 +138,9 @@ def load_library() -> ctypes.CDLL:
     lib.flint_proj_out.restype = ctypes.c_int
     lib.flint_attn_fwd_kernel.argtypes = [i32, i32]
     lib.flint_attn_fwd_kernel.restype = ctypes.c_int
+    lib.flint_attn_fwd_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                          i32, i32, i32, ctypes.c_float, ctypes.c_float, vp, vp]
+    lib.flint_attn_fwd_static.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -262,6 +268,17 @@ def flint_attn_device_status(workspace, stream):
     flags = ctypes.c_int32(0)
     st = int(load_library().flint_attn_device_status(workspace, stream, ctypes.byref(flags)))
     return st, int(flags.value)
+
+
+def flint_attn_fwd_static(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused, n_seqs,
+                          max_seqlen, total_tokens, num_q_heads, num_kv_heads, head_dim, window,
+                          use_rope, rope_theta, eps, out, stream) -> int:
+    """flint_attn_fwd with the library's static per-GPU scratch as workspace
+    (no allocation; FLINT_ERR_TOO_LARGE beyond FLINT_ATTN_STATIC_SCRATCH_BYTES)."""
+    return int(load_library().flint_attn_fwd_static(
+        q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused, n_seqs, max_seqlen,
+        total_tokens, num_q_heads, num_kv_heads, head_dim, window, use_rope, rope_theta, eps, out,
+        stream))
 
 
 def flint_attn_fwd_kernel(total_tokens: int, n_seqs: int) -> int:

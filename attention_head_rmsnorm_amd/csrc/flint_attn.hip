@@ -51,6 +51,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "flint_common.h"
 
 namespace flint {
@@ -1050,6 +1052,7 @@ extern "C" const char* flint_attn_strerror(int status) {
     case FLINT_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, workspace 256, int32 arrays 4)";
     case FLINT_ERR_HIP: return "HIP runtime error";
     case FLINT_ERR_DEVICE_DATA: return "invalid device data (cu_seqlens, seqused or mask)";
+    case FLINT_ERR_TOO_LARGE: return "the call needs more workspace than flint_attn_fwd_static's static scratch holds";
     default: return "unknown flint_attn status";
   }
 }
@@ -1445,6 +1448,55 @@ extern "C" int flint_attn_fwd(const void* q, const void* k, const void* v, const
                                n_seqs, max_seqlen, total_tokens, num_q_heads, num_kv_heads,
                                head_dim, window, use_rope, rope_theta, eps, workspace,
                                workspace_bytes, out, stream, FLINT_PHASE_ALL);
+}
+
+// ----------------------------------------------------------------- forward without allocation
+
+// The workspace of flint_attn_fwd_static: one array per GPU in the code
+// object's device memory, held until the process ends. Host code never passes
+// its name to a kernel (in host code it is only a stand-in for the device
+// symbol); it uses the device address that hipGetSymbolAddress returns,
+// looked up once per device.
+constexpr size_t kStaticScratchBytes = FLINT_ATTN_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+// Device address of this device's scratch array, or NULL when the lookup fails.
+static void* static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+extern "C" int flint_attn_fwd_static(const void* q, const void* k, const void* v,
+                                     const float* q_norm_w, const float* k_norm_w,
+                                     const float* sink, const int32_t* positions,
+                                     const int32_t* cu_seqlens, const int32_t* seqused,
+                                     int32_t n_seqs, int32_t max_seqlen, int32_t total_tokens,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t window, int32_t use_rope, float rope_theta, float eps,
+                                     void* out, void* stream) {
+  if (total_tokens < 0 || n_seqs < 0 || max_seqlen < 0) return FLINT_ERR_SHAPE;
+  if (num_q_heads != kH || num_kv_heads != kG || head_dim != kD || max_seqlen > kMaxSeqLen)
+    return FLINT_ERR_UNSUPPORTED;
+  if (total_tokens == 0) return FLINT_OK;
+  if (make_layout(total_tokens, n_seqs).total > kStaticScratchBytes) return FLINT_ERR_TOO_LARGE;
+  void* ws = static_scratch();
+  if (!ws) return FLINT_ERR_HIP;
+  return fwd_impl(q, k, v, q_norm_w, k_norm_w, sink, positions, cu_seqlens, seqused, n_seqs,
+                  max_seqlen, total_tokens, num_q_heads, num_kv_heads, head_dim, window, use_rope,
+                  rope_theta, eps, ws, kStaticScratchBytes, out, nullptr, stream, FLINT_PHASE_ALL);
 }
 
 extern "C" int flint_attn_seqused_from_mask(const uint8_t* mask, int32_t batch, int32_t seqlen,

@@ -70,7 +70,9 @@ typedef enum flint_status {
   FLINT_ERR_ALIGN = -6,       /* tensor pointers not 16-byte aligned, workspace
                                  not 256-byte aligned, int32 arrays not 4-byte    */
   FLINT_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed        */
-  FLINT_ERR_DEVICE_DATA = -8  /* cu_seqlens / seqused / mask content is invalid    */
+  FLINT_ERR_DEVICE_DATA = -8, /* cu_seqlens / seqused / mask content is invalid    */
+  FLINT_ERR_TOO_LARGE = -9    /* flint_attn_fwd_static: the sizes need more than its
+                                 static scratch (FLINT_ATTN_STATIC_SCRATCH_BYTES)   */
 } flint_status;
 
 /* Device-data error bits reported by flint_attn_device_status(). */
@@ -135,6 +137,34 @@ int flint_attn_fwd(const void* q, const void* k, const void* v, const float* q_n
                    int32_t num_kv_heads, int32_t head_dim, int32_t window, int32_t use_rope,
                    float rope_theta, float eps, void* workspace, size_t workspace_bytes, void* out,
                    void* stream);
+
+/*
+ * flint_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The workspace is a static array of
+ * FLINT_ATTN_STATIC_SCRATCH_BYTES in the library's device memory, one per
+ * GPU, held from the library's first call on that GPU until the process
+ * ends; its address is looked up once per device. The call allocates
+ * nothing and runs the same kernels as flint_attn_fwd, with the same
+ * arguments otherwise and the same results. Limits and caveats:
+ *   - sizes whose flint_attn_workspace_bytes() exceeds the scratch return
+ *     FLINT_ERR_TOO_LARGE and launch nothing (64 MiB: about 31,000 tokens
+ *     of one sequence);
+ *   - every call on a GPU uses that GPU's one array: calls that overlap on
+ *     one GPU (other streams, other threads) race and must be serialized by
+ *     the caller; each call rewrites what it reads, so the content a previous
+ *     call left does not matter;
+ *   - device-data errors (cu_seqlens, seqused) cannot be read back with
+ *     flint_attn_device_status; with FLINT_ATTN_DEBUG=1 the call synchronizes
+ *     and returns FLINT_ERR_DEVICE_DATA itself.
+ */
+#define FLINT_ATTN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int flint_attn_fwd_static(const void* q, const void* k, const void* v, const float* q_norm_w,
+                          const float* k_norm_w, const float* sink, const int32_t* positions,
+                          const int32_t* cu_seqlens, const int32_t* seqused, int32_t n_seqs,
+                          int32_t max_seqlen, int32_t total_tokens, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                          int32_t use_rope, float rope_theta, float eps, void* out, void* stream);
 
 /* Phases of flint_attn_fwd, in the order they must run on one stream. */
 #define FLINT_PHASE_SCHEDULE 1 /* check cu_seqlens/seqused; lay out tiles and query blocks */

@@ -46,6 +46,16 @@ int main(void) {
   CHECK(flint_attn_workspace_bytes(FLINT_MAX_SEQLEN, 1, FLINT_MAX_SEQLEN + 1, 4, 128) == 0);
   CHECK(flint_attn_bwd_workspace_bytes(64, 1, FLINT_MAX_SEQLEN + 1, 4, 128) == 0);
 
+  /* the forward on the static scratch: host checks before any launch */
+  CHECK(flint_attn_fwd_static(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, NULL, 1, 1 << 20, 1 << 20,
+                              32, 4, 128, 0, 0, 1.0e6f, 1.0e-6f, FAKE, NULL) == FLINT_ERR_TOO_LARGE);
+  CHECK(flint_attn_fwd_static(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, NULL, 1, 64, 64, 16, 4,
+                              128, 0, 0, 1.0e6f, 1.0e-6f, FAKE, NULL) == FLINT_ERR_UNSUPPORTED);
+  CHECK(flint_attn_fwd_static(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, NULL, 1, 64, -1, 32, 4,
+                              128, 0, 0, 1.0e6f, 1.0e-6f, FAKE, NULL) == FLINT_ERR_SHAPE);
+  CHECK(flint_attn_fwd_static(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, 0, 0, 32, 4,
+                              128, 0, 0, 1.0e6f, 1.0e-6f, NULL, NULL) == FLINT_OK);
+
   /* which attention kernel a forward launches: a host-side query */
   CHECK(flint_attn_fwd_kernel(0, 1) == 0);
   CHECK(flint_attn_fwd_kernel(-1, 1) == FLINT_ERR_SHAPE);
@@ -117,9 +127,9 @@ int main(void) {
     CHECK(flint_attn_device_status(NULL, NULL, &flags) == FLINT_ERR_NULL);
   }
   {
-    const char* seen[9];
+    const char* seen[10];
     int st;
-    for (st = 0; st >= -8; --st) {
+    for (st = 0; st >= -9; --st) {
       int j;
       const char* m = flint_attn_strerror(st);
       CHECK(m != NULL && strlen(m) > 0);

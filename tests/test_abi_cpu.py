@@ -39,11 +39,11 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_covers_every_status():
     seen = set()
-    for st in range(0, -9, -1):
+    for st in range(0, -10, -1):
         msg = fa.flint_attn_strerror(st)
         assert msg and "unknown" not in msg
         seen.add(msg)
-    assert len(seen) == 9
+    assert len(seen) == 10
     assert "unknown" in fa.flint_attn_strerror(-99)
 
 
