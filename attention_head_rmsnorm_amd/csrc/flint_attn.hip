@@ -10,16 +10,18 @@
 // logit per query head that joins the softmax max and denominator with zero
 // value and no 1/sqrt(d) scaling.
 //
-// Three kernels run in order on the caller's stream:
-//   schedule_kernel   one workgroup; checks cu_seqlens/seqused, lays out the
-//                     64-token key tiles of every sequence and the 32-token
-//                     query blocks, and orders the blocks by decreasing work.
-//   kv_prologue_kernel  per (key tile, kv head): RMSNorm + RoPE of K in FP32,
-//                     one bf16 rounding, stored as an MFMA-ready tile in
-//                     operand-fragment order; V transposed and key-permuted
-//                     into the PV operand order; zeros for padded keys; zero
-//                     rows of `out` for padded queries; the kv head's largest
-//                     |k'| into the workspace header.
+// Two launches run in order on the caller's stream:
+//   prep_kernel       block 0 runs the schedule: checks cu_seqlens/seqused,
+//                     lays out the 32-token query blocks, orders them by
+//                     decreasing work and lists the 64-row units that hold
+//                     padded rows; the other blocks, at the same time, one
+//                     per (64-key tile, kv head): RMSNorm + RoPE of K in
+//                     FP32, one bf16 rounding, stored as an MFMA-ready tile
+//                     in operand-fragment order; V transposed and
+//                     key-permuted into the PV operand order; zeros for
+//                     padded keys. A tile finds its sequence from cu_seqlens
+//                     alone (sequence s owns the tiles from cu[s] / 64 + s
+//                     on), so it does not wait for the schedule.
 //   attn_kernel       persistent: one workgroup per CU, each running a list
 //                     of work items (32 query tokens x the 8 query heads of one
 //                     kv head). Its 8 waves, one per query head, share each
@@ -30,7 +32,8 @@
 //                     scale in log2 units, bf16) is fused in. S^T = K Q^T and
 //                     O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with FP32
 //                     accumulation, over the tiles inside the causal window
-//                     only. Problems with fewer work items than CUs run on
+//                     only. It then writes the padded rows of `out` as
+//                     zeros. Problems with fewer work items than CUs run on
 //                     attn_half_kernel instead: two 4-wave workgroups per item,
 //                     4 query heads each, so twice the CUs take part.
 //
@@ -42,12 +45,13 @@
 // the sink adds exp2(sink) to the denominator, and O = sum P v / l is the
 // same ratio as with any shift. The MFMA accumulators start at zero and
 // P = exp2(acc) needs no running max, no per-tile max reduction and no
-// rescaling. Waves with a larger bound take the streaming path: a running max
+// rescaling; max |k'| is bounded from the key-norm weights (key_norm_bound),
+// so no pass over the keys has to run first. Waves with a larger bound take
+// the streaming path: a running max
 // that starts at the sink (m = sink, l = 1), subtracted before exp2 and
 // raised lazily with rescaling. The start is never below -B, the least logit
 // possible: a sink far below every logit (or -INF) then adds ~0 to l without
 // moving the shift away from the logits, where s - m would lose their bits.
-// max |k'| is taken over all keys of the kv head, a bound for every item.
 
 #include <hip/hip_runtime.h>
 
@@ -126,28 +130,42 @@ __device__ __forceinline__ float sumsq8t(const uint4& c) {
 
 // ----------------------------------------------------------------- schedule
 
-__global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ cu,
-                                                        const int* __restrict__ seqused, int n,
-                                                        int T, int max_seqlen, int window,
-                                                        double theta, Ws ws) {
-  __shared__ int tmp[1024];
-  __shared__ int hist[kBuckets];
-  __shared__ int sflags;
+// RoPE frequency of channel pair c: theta^(-c/64) / (2 pi) < 1/(2 pi), scaled
+// by 2^64 so that it fits an unsigned 64-bit integer (a 0.64 fraction).
+__device__ __forceinline__ unsigned long long rope_ratio(double theta, int c) {
+  const double r = pow(theta, -(double)c / 64.0) * 0.15915494309189533577;
+  return (unsigned long long)(r * 18446744073709551616.0);
+}
+
+// Shared memory of schedule_body with NT threads.
+template <int NT>
+struct SchedLds {
+  int tmp[NT / 64];
+  int hist[kBuckets];
+  int flags;
+};
+
+// The schedule, run by one block of NT threads: checks cu_seqlens / seqused,
+// writes the sequence table, the query-block bases and the work items sorted
+// by decreasing number of key tiles, and the RoPE frequencies. `fwd` selects
+// the forward layout: key tiles from tile_base (no tile list) and the bases of
+// the padded 64-row units (rows at or past a sequence's valid length, which
+// the attention kernel zeroes); otherwise the packed layout the backward uses,
+// tiles numbered back to back with a tile list.
+template <int NT>
+__device__ void schedule_body(const int* __restrict__ cu, const int* __restrict__ seqused, int n,
+                              int T, int max_seqlen, int window, double theta, Ws ws, bool fwd,
+                              SchedLds<NT>& sh) {
   const int tid = threadIdx.x;
-  if (tid == 0) sflags = 0;
-  if (tid < kG) ws.hdr[kHdrKMax + tid] = 0;
-  if (tid < 64) {
-    // theta^(-c/64) / (2 pi) < 1/(2 pi): scaled by 2^64 it fits an unsigned 64-bit integer
-    const double r = pow(theta, -(double)tid / 64.0) * 0.15915494309189533577;
-    ws.rope_r[tid] = (unsigned long long)(r * 18446744073709551616.0);
-  }
+  if (tid == 0) sh.flags = 0;
+  if (tid < 64) ws.rope_r[tid] = rope_ratio(theta, tid);
   __syncthreads();
 
   int flags = 0;
-  int carry_t = 0, carry_q = 0;
-  for (int base = 0; base < n; base += 1024) {
+  int carry_t = 0, carry_q = 0, carry_p = 0;
+  for (int base = 0; base < n; base += NT) {
     const int s = base + tid;
-    int nt = 0, nq = 0, a = 0, len = 0, u = 0;
+    int nt = 0, nq = 0, np = 0, a = 0, len = 0, u = 0;
     if (s < n) {
       a = cu[s];
       const int b = cu[s + 1];
@@ -163,72 +181,93 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ 
       }
       nt = (len + kBN - 1) / kBN;
       nq = (u + kBM - 1) / kBM;
+      np = u < len ? nt - u / kBN : 0;
     }
-    int tot_t, tot_q;
-    const int ex_t = block_excl_scan(nt, tmp, &tot_t);
-    const int ex_q = block_excl_scan(nq, tmp, &tot_q);
+    int tot_t, tot_q, tot_p;
+    const int ex_t = block_excl_scan_t<NT>(nt, sh.tmp, &tot_t);
+    const int ex_q = block_excl_scan_t<NT>(nq, sh.tmp, &tot_q);
+    const int ex_p = block_excl_scan_t<NT>(np, sh.tmp, &tot_p);
     if (s < n) {
-      ws.seq[s] = make_int4(a, len, u, carry_t + ex_t);
-      ws.tbase[s] = carry_t + ex_t;
+      const int tb = fwd ? tile_base(a, s) : carry_t + ex_t;
+      ws.seq[s] = make_int4(a, len, u, tb);
+      ws.tbase[s] = tb;
       ws.qbase[s] = carry_q + ex_q;
+      ws.pbase[s] = carry_p + ex_p;
     }
     carry_t += tot_t;
     carry_q += tot_q;
+    carry_p += tot_p;
   }
-  if (flags) atomicOr(&sflags, flags);
+  if (flags) atomicOr(&sh.flags, flags);
   __syncthreads();
-  const int f = sflags;
+  const int f = sh.flags;
   if (f) {  // invalid device data: schedule nothing
     if (tid == 0) {
       ws.hdr[0] = f;
       ws.hdr[1] = 0;
       ws.hdr[2] = 0;
+      ws.hdr[3] = 0;
     }
     return;
   }
   if (tid == 0) {
     ws.tbase[n] = carry_t;
     ws.qbase[n] = carry_q;
+    ws.pbase[n] = carry_p;
   }
-  const int NT = carry_t, NQ = carry_q;
-  for (int i = tid; i < kBuckets; i += 1024) hist[i] = 0;
+  const int NTL = carry_t, NQ = carry_q;
+  for (int i = tid; i < kBuckets; i += NT) sh.hist[i] = 0;
   __syncthreads();
 
-  for (int e = tid; e < NT; e += 1024) {
-    const int s = find_seq(ws.tbase, n, e);
-    ws.tiles[e] = make_int2(s, e - ws.tbase[s]);
+  if (!fwd) {
+    for (int e = tid; e < NTL; e += NT) {
+      const int s = find_seq(ws.tbase, n, e);
+      ws.tiles[e] = make_int2(s, e - ws.tbase[s]);
+    }
   }
-  for (int e = tid; e < NQ; e += 1024) {
+  for (int e = tid; e < NQ; e += NT) {
     const int s = find_seq(ws.qbase, n, e);
     const int c = min(block_cost(ws.seq[s].z, e - ws.qbase[s], window), kBuckets - 1);
-    atomicAdd(&hist[c], 1);
+    atomicAdd(&sh.hist[c], 1);
   }
   __syncthreads();
-  // bucket starts in order of decreasing cost; thread tid owns 4 buckets
-  int local[4], sum = 0;
-  for (int j = 0; j < 4; ++j) {
-    local[j] = hist[kBuckets - 1 - (4 * tid + j)];
+  // bucket starts in order of decreasing cost; thread tid owns kBuckets / NT buckets
+  constexpr int kPer = kBuckets / NT;
+  int local[kPer], sum = 0;
+  for (int j = 0; j < kPer; ++j) {
+    local[j] = sh.hist[kBuckets - 1 - (kPer * tid + j)];
     sum += local[j];
   }
   int tot;
-  int run = block_excl_scan(sum, tmp, &tot);
-  for (int j = 0; j < 4; ++j) {
-    hist[kBuckets - 1 - (4 * tid + j)] = run;
+  int run = block_excl_scan_t<NT>(sum, sh.tmp, &tot);
+  for (int j = 0; j < kPer; ++j) {
+    sh.hist[kBuckets - 1 - (kPer * tid + j)] = run;
     run += local[j];
   }
   __syncthreads();
-  for (int e = tid; e < NQ; e += 1024) {
+  // Items of equal cost keep runs of consecutive query blocks together: the
+  // lanes of a wave take their places in lane order.
+  for (int e = tid; e < NQ; e += NT) {
     const int s = find_seq(ws.qbase, n, e);
     const int qb = e - ws.qbase[s];
     const int c = min(block_cost(ws.seq[s].z, qb, window), kBuckets - 1);
-    const int pos = atomicAdd(&hist[c], 1);
+    const int pos = atomicAdd(&sh.hist[c], 1);
     ws.items[pos] = make_int2(s, qb);
   }
   if (tid == 0) {
     ws.hdr[0] = 0;
-    ws.hdr[1] = NT;
+    ws.hdr[1] = fwd ? 0 : NTL;
     ws.hdr[2] = NQ;
+    ws.hdr[3] = fwd ? carry_p : 0;
   }
+}
+
+__global__ __launch_bounds__(1024) void schedule_kernel(const int* __restrict__ cu,
+                                                        const int* __restrict__ seqused, int n,
+                                                        int T, int max_seqlen, int window,
+                                                        double theta, Ws ws) {
+  __shared__ SchedLds<1024> sh;
+  schedule_body<1024>(cu, seqused, n, T, max_seqlen, window, theta, ws, false, sh);
 }
 
 void launch_schedule(const int* cu, const int* seqused, int n, int T, int max_seqlen, int window,
@@ -238,30 +277,57 @@ void launch_schedule(const int* cu, const int* seqused, int n, int T, int max_se
 
 // ----------------------------------------------------------------- K/V prologue
 
-// F16: k, v and out are FP32, the tiles fp16 (the FP16 attention-compute
-// variant); otherwise all three are bf16.
+// The sequence of forward key tile e and its index in the sequence, from
+// cu_seqlens alone (tile_base layout); false for a tile slot no sequence owns
+// and for entries that cannot be valid (then nothing is read or written; the
+// schedule reports the error).
+struct TileOf {
+  int start, len, u, j;
+};
+
+__device__ __forceinline__ bool tile_of(const int* __restrict__ cu, const int* __restrict__ seqused,
+                                        int n, int T, int e, TileOf& r) {
+  const int s = tile_seq(cu, n, e);
+  const int a = cu[s], b = cu[s + 1];
+  if (a < 0 || b > T || b < a) return false;
+  r.start = a;
+  r.len = b - a;
+  r.j = e - tile_base(a, s);
+  if (r.j < 0 || r.j >= (r.len + kBN - 1) / kBN) return false;
+  const int u = seqused ? seqused[s] : r.len;
+  r.u = max(0, min(u, r.len));
+  return true;
+}
+
+// Shared memory of kv_tile.
+struct KvLds {
+  __attribute__((aligned(16))) uint16_t vt[kD * kBN];
+  unsigned long long rope[kD / 2];
+};
+
+// One key tile e of kv head g, by 256 threads: RMSNorm + RoPE of K in FP32,
+// one rounding, stored as an MFMA-ready tile in operand-fragment order; V
+// transposed and key-permuted into the PV operand order; zeros for padded
+// keys. F16: k and v are FP32 and the tiles fp16 (the FP16 attention-compute
+// variant); otherwise k and v are bf16.
 template <bool F16>
-__global__ __launch_bounds__(256) void kv_prologue_kernel(const void* __restrict__ kp,
-                                                          const void* __restrict__ vp,
-                                                          const float* __restrict__ k_norm_w,
-                                                          const int* __restrict__ positions,
-                                                          float eps, int use_rope, Ws ws,
-                                                          void* __restrict__ outp,
-                                                          float* __restrict__ lse) {
+__device__ void kv_tile(int e, int g, const void* __restrict__ kp, const void* __restrict__ vp,
+                        const float* __restrict__ k_norm_w, const int* __restrict__ positions,
+                        const int* __restrict__ cu, const int* __restrict__ seqused, int n, int T,
+                        float eps, int use_rope, double theta, Ws ws, KvLds& sh) {
   const uint16_t* k = static_cast<const uint16_t*>(kp);
   const uint16_t* v = static_cast<const uint16_t*>(vp);
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kD * kBN];
-  __shared__ float red[4];
-  const int e = blockIdx.x, g = blockIdx.y;
-  if (e >= ws.hdr[1]) return;
-  const int2 te = ws.tiles[e];
-  const int4 meta = ws.seq[te.x];
-  const int start = meta.x, len = meta.y, u = meta.z;
+  uint16_t* vt = sh.vt;
+  TileOf to;
+  if (!tile_of(cu, seqused, n, T, e, to)) return;
+  const int start = to.start, u = to.u;
   const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
-  const int ell = te.y * kBN + r;
+  if (use_rope && tid < kD / 2) sh.rope[tid] = rope_ratio(theta, tid);
+  const int ell = to.j * kBN + r;
   const bool valid = ell < u;
   const size_t t = (size_t)start + ell;
-  char* tile = ws.kv + ((size_t)g * ws.ntmax + meta.w + te.y) * kTileBytes;
+  char* tile = ws.kv + ((size_t)g * ws.ntmax + e) * kTileBytes;
+  __syncthreads();
 
   // K: this thread owns channels [16p, 16p+16) and their RoPE partners +64.
   float x[32];
@@ -299,7 +365,7 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const void* __restrict
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float c, s;
-      rope_cos_sin(pos, ws.rope_r[16 * p + i], &c, &s);
+      rope_cos_sin(pos, sh.rope[16 * p + i], &c, &s);
       const float a = x[i], b = x[16 + i];
       x[i] = a * c - b * s;
       x[16 + i] = b * c + a * s;
@@ -308,21 +374,10 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const void* __restrict
   {
     uint4* kfrag = reinterpret_cast<uint4*>(tile);
     const int b = r >> 5, col = r & 31;
-    const uint4 w0 = pack8t<F16>(x), w1 = pack8t<F16>(x + 8), w2 = pack8t<F16>(x + 16),
-                w3 = pack8t<F16>(x + 24);
-    kfrag[frag_index(b, 8, p, 0, col)] = w0;      // channels 16p .. 16p+7
-    kfrag[frag_index(b, 8, p, 1, col)] = w1;      // 16p+8 .. 16p+15
-    kfrag[frag_index(b, 8, 4 + p, 0, col)] = w2;  // 64+16p .. 64+16p+7
-    kfrag[frag_index(b, 8, 4 + p, 1, col)] = w3;  // 64+16p+8 .. 64+16p+15
-    // |k'| of the rounded key, for the logit bound of the attention kernel
-    float n2 = sumsq8t<F16>(w0) + sumsq8t<F16>(w1) + sumsq8t<F16>(w2) + sumsq8t<F16>(w3);
-    n2 += __shfl_xor(n2, 1);
-    n2 += __shfl_xor(n2, 2);
-    // tile max of |k'|: wave max, then across the four waves
-    float kn = sqrtf(n2);
-#pragma unroll
-    for (int off = 4; off < 64; off <<= 1) kn = fmaxf(kn, __shfl_xor(kn, off));
-    if ((tid & 63) == 0) red[tid >> 6] = kn;
+    kfrag[frag_index(b, 8, p, 0, col)] = pack8t<F16>(x);           // channels 16p .. 16p+7
+    kfrag[frag_index(b, 8, p, 1, col)] = pack8t<F16>(x + 8);       // 16p+8 .. 16p+15
+    kfrag[frag_index(b, 8, 4 + p, 0, col)] = pack8t<F16>(x + 16);  // 64+16p .. 64+16p+7
+    kfrag[frag_index(b, 8, 4 + p, 1, col)] = pack8t<F16>(x + 24);  // 64+16p+8 .. 64+16p+15
   }
 
   // V: transpose through LDS; this thread owns channels [32p, 32p+32) of key r.
@@ -357,9 +412,6 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const void* __restrict
     }
   }
   __syncthreads();
-  if (tid == 0)
-    atomicMax(reinterpret_cast<unsigned*>(&ws.hdr[kHdrKMax + g]),
-              __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
   {
     uint4* vtile = reinterpret_cast<uint4*>(tile + kHalfTile);
 #pragma unroll
@@ -370,18 +422,39 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const void* __restrict
           *reinterpret_cast<const uint4*>(&vt[d * kBN + c * 8]);
     }
   }
+}
 
-  // Padded query rows of this kv head's 8 query heads are exact zeros.
-  if (ell >= u && ell < len) {
-    constexpr int kVecPerThread = F16 ? 64 : 32;  // a token's 8 rows: 4 KiB FP32 or 2 KiB bf16
-    uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(outp) + (t * kH + (size_t)g * kHpg) * kD * (F16 ? 4 : 2));
-    const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll 4
-    for (int i = 0; i < kVecPerThread; ++i) dst[p * kVecPerThread + i] = z;
-    if (lse && p < 2)  // an empty softmax: log 0
-      *reinterpret_cast<float4*>(lse + t * kH + g * kHpg + 4 * p) =
-          make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+// What prep_kernel runs.
+constexpr int kPrepSchedule = 1;
+constexpr int kPrepKv = 2;
+
+// The forward's preparation in one launch of 256-thread blocks: block 0 runs
+// the schedule (kPrepSchedule), blocks 1.. the K/V tiles (kPrepKv), tile
+// (b - 1) / 4 of kv head (b - 1) % 4 for block b. The tiles do not depend on
+// the schedule (tile_base layout), so both run at once; the attention kernel
+// reads both. Tile slots that no sequence owns are skipped.
+template <bool F16>
+__global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ kp, const void* __restrict__ vp,
+                                                   const float* __restrict__ k_norm_w,
+                                                   const int* __restrict__ positions,
+                                                   const int* __restrict__ cu,
+                                                   const int* __restrict__ seqused, int n, int T,
+                                                   int max_seqlen, int window, double theta,
+                                                   float eps, int use_rope, Ws ws, int parts) {
+  __shared__ union {
+    SchedLds<256> sched;
+    KvLds kv;
+  } sh;
+  int b = blockIdx.x;
+  if (parts & kPrepSchedule) {
+    if (b == 0) {
+      schedule_body<256>(cu, seqused, n, T, max_seqlen, window, theta, ws, true, sh.sched);
+      return;
+    }
+    --b;
   }
+  kv_tile<F16>(b >> 2, b & 3, kp, vp, k_norm_w, positions, cu, seqused, n, T, eps, use_rope, theta, ws,
+               sh.kv);
 }
 
 // ----------------------------------------------------------------- FP16 query prep
@@ -395,16 +468,17 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(const void* __restrict
 __global__ __launch_bounds__(256) void q16_prep_kernel(const float* __restrict__ q,
                                                        const float* __restrict__ q_norm_w,
                                                        const int* __restrict__ positions,
+                                                       const int* __restrict__ cu,
+                                                       const int* __restrict__ seqused, int n, int T,
                                                        float eps, int use_rope, Ws ws,
                                                        uint16_t* __restrict__ q16) {
   const int e = blockIdx.x, g = blockIdx.y;
-  if (e >= ws.hdr[1]) return;
-  const int2 te = ws.tiles[e];
-  const int4 meta = ws.seq[te.x];
+  TileOf to;
+  if (!tile_of(cu, seqused, n, T, e, to)) return;
   const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
-  const int ell = te.y * kBN + r;
-  if (ell >= meta.z) return;  // padding; the shuffles below stay within valid quads
-  const size_t t = (size_t)meta.x + ell;
+  const int ell = to.j * kBN + r;
+  if (ell >= to.u) return;  // padding; the shuffles below stay within valid quads
+  const size_t t = (size_t)to.start + ell;
   float cs[16], sn[16];
   if (use_rope) {
     const int pos = positions ? positions[t] : ell;
@@ -453,49 +527,54 @@ __global__ __launch_bounds__(256) void q16_prep_kernel(const float* __restrict__
 
 // ----------------------------------------------------------------- attention
 
-// Direct global->LDS copy of one 32 KiB tile into an LDS stage: each of the
-// 512 threads moves four 16-byte vectors with buffer_load ... lds, which
-// writes lane L's vector at the wave-uniform LDS base (M0) + 16 L, so the tile
-// lands in LDS with the byte order it has in the workspace. `rsrc` covers this
-// item's tiles only (reads past it return zeros), `tile_off` is the tile's
-// byte offset in it and `voff` = 16 lane + 1024 wave.
-__device__ __forceinline__ void load_vec_async(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
-                                               uint4* stage, int i, int wave) {
+// Direct global->LDS copy of a 32 KiB tile into an LDS stage by four waves
+// (w = 0..3): each lane moves eight 16-byte vectors with buffer_load ... lds,
+// which writes lane L's vector at the wave-uniform LDS base (M0) + 16 L, so the
+// tile lands in LDS with the byte order it has in the workspace. `rsrc` covers
+// one item's tiles only (reads past it return zeros), `soff` is the tile's
+// byte offset in it, `voff` = 16 lane + 1024 w, and vector i of the lane is
+// byte 4096 i + voff of the tile.
+__device__ __forceinline__ void load_vec_async4(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
+                                                uint4* stage, int i, int wave) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       rsrc,
-      (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(stage) + i * 8192 + wave * 1024),
-      16, voff, soff + i * 8192, 0, 0);
+      (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(stage) + i * 4096 + wave * 1024),
+      16, voff, soff + i * 4096, 0, 0);
 }
 
-__device__ __forceinline__ void load_tile_async(__amdgpu_buffer_rsrc_t rsrc, int voff, int tile_off,
-                                                uint4* stage, int wave) {
+__device__ __forceinline__ void load_tile_async4(__amdgpu_buffer_rsrc_t rsrc, int voff, int tile_off,
+                                                 uint4* stage, int wave) {
 #pragma unroll
-  for (int i = 0; i < kTileVec / kAttnThreads; ++i) load_vec_async(rsrc, voff, tile_off, stage, i, wave);
+  for (int i = 0; i < 8; ++i) load_vec_async4(rsrc, voff, tile_off, stage, i, wave);
 }
 
-// Inside an item, from its third slot on, the only newer operations are the
-// next slot's loads (4) or none. An item's first two slots were loaded before
-// the item's query rows; loads complete in issue order, so waiting for those
-// rows (n = the operations issued since: output stores, 8, the normalizer
-// store when it is written, 1, and the third slot's loads, 4) waits for the
-// slots as well. The FP32 output of the FP16 variant takes 16 stores (and
-// writes no normalizer).
+// Group A (waves 0-3) moves every tile into LDS, 8 loads per wave and slot,
+// issued after its logits of the slot two earlier (before any later vector-
+// memory operation);
+// group B issues none, and reaches LDS data only through the barrier, after
+// group A has waited for it. For a wave of group A, inside an item and from
+// its third slot on, the only newer operations are the next slot's loads (8)
+// or none. An item's first two slots were loaded before the item's query rows;
+// loads complete in issue order, so waiting for those rows (n = the
+// operations issued since: output stores, 8, the normalizer store when it is
+// written, 1, and for group A the third slot's loads, 8) waits for the slots
+// as well. The FP32 output of the FP16 variant takes 16 stores (and writes no
+// normalizer).
 template <bool F16>
 __device__ __forceinline__ void ring_barrier(int n) {
   if constexpr (F16) {
     switch (n) {
-      case 4: ring_barrier_n<4>(); break;
+      case 8: ring_barrier_n<8>(); break;
       case 16: ring_barrier_n<16>(); break;
-      case 20: ring_barrier_n<20>(); break;
+      case 24: ring_barrier_n<24>(); break;
       default: ring_barrier_n<0>(); break;
     }
   } else {
     switch (n) {
-      case 4: ring_barrier_n<4>(); break;
       case 8: ring_barrier_n<8>(); break;
       case 9: ring_barrier_n<9>(); break;
-      case 12: ring_barrier_n<12>(); break;
-      case 13: ring_barrier_n<13>(); break;
+      case 16: ring_barrier_n<16>(); break;
+      case 17: ring_barrier_n<17>(); break;
       default: ring_barrier_n<0>(); break;
     }
   }
@@ -509,15 +588,10 @@ struct RowState {
 };
 
 // S^T for the 64 keys of a tile: two 32x32 logit blocks, accumulators from
-// zero. Operand fragments are read kFragAhead MFMAs ahead of their use. When
-// `load` is set, this wave's four direct-to-LDS loads of a later tile (byte
-// offset `loff`, into `lstage`) are spread over the MFMAs, one after every
-// fourth, so the loads of all waves do not reach the texture unit in one burst.
+// zero. Operand fragments are read kFragAhead MFMAs ahead of their use.
 template <bool F16>
 __device__ __forceinline__ void tile_logits(const uint4* kt, int lane, const bf16x8* qf,
-                                            f32x16& s0, f32x16& s1, bool load,
-                                            __amdgpu_buffer_rsrc_t rsrc, int voff, int loff,
-                                            uint4* lstage, int wave) {
+                                            f32x16& s0, f32x16& s1) {
   bf16x8 f[16];
 #pragma unroll
   for (int i = 0; i < kFragAhead; ++i)
@@ -537,7 +611,6 @@ __device__ __forceinline__ void tile_logits(const uint4* kt, int lane, const bf1
     }
     if (i + kFragAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // this MFMA
-    if ((i & 3) == 3 && load) load_vec_async(rsrc, voff, loff, lstage, i >> 2, wave);
   }
 }
 
@@ -627,6 +700,53 @@ __device__ __forceinline__ void tile_pv(const uint4* vt, int lane, const bf16x8*
   }
 }
 
+// Largest |k'| any key can have, from the key-norm weights: RMSNorm gives a
+// head vector of norm sqrt(128 ms / (ms + eps)) <= sqrt(128), the weight scales
+// each channel by at most max |w|, RoPE turns channel pairs without changing
+// their norm, and one rounding to bf16 or fp16 adds at most 2^-8 relatively.
+// Every wave reads the 128 weights itself (two per lane).
+__device__ __forceinline__ float key_norm_bound(const float* __restrict__ k_norm_w, int lane) {
+  float w = fmaxf(fabsf(k_norm_w[lane]), fabsf(k_norm_w[lane + 64]));
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) w = fmaxf(w, __shfl_xor(w, off));
+  w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w)));
+  return 11.313708498984761f * w * 1.00390625f;
+}
+
+// Padded rows (index in the sequence at or past the valid length) of `out`
+// are exact zeros and their normalizer -INF (an empty softmax). The schedule
+// lists them in 64-row units (ws.pbase); unit i goes to workgroup i % nw of
+// the ones serving kv head g, which zeroes its `heads` query heads from
+// h0 = g * 8 + hoff on, with its NT threads. Nothing is written when the
+// schedule found invalid device data.
+template <bool F16, int NT>
+__device__ void zero_padded_rows(const Ws& ws, int n, int g, int hoff, int heads, int w, int nw,
+                                 void* __restrict__ outp, float* __restrict__ lse) {
+  if (ws.hdr[0] != 0) return;
+  const int nu = ws.hdr[3];
+  constexpr int kElem = F16 ? 4 : 2;
+  const int row_vec = heads * kD * kElem / 16;  // 16-byte vectors of one token's rows
+  const int h0 = g * kHpg + hoff;
+  const int tid = threadIdx.x;
+  for (int i = w; i < nu; i += nw) {
+    const int s = find_seq(ws.pbase, n, i);
+    const int4 meta = ws.seq[s];  // start, length, valid length
+    const int j = meta.z / kBN + (i - ws.pbase[s]);
+    const int r0 = max(j * kBN, meta.z), r1 = min(j * kBN + kBN, meta.y);
+    for (int idx = tid; idx < (r1 - r0) * row_vec; idx += NT) {
+      const int rr = r0 + idx / row_vec, c = idx - (idx / row_vec) * row_vec;
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(outp) +
+                                            ((size_t)(meta.x + rr) * kH + h0) * kD * kElem) + c;
+      *dst = make_uint4(0, 0, 0, 0);
+    }
+    if (lse)
+      for (int idx = tid; idx < (r1 - r0) * heads; idx += NT) {
+        const int rr = r0 + idx / heads;
+        lse[(size_t)(meta.x + rr) * kH + h0 + idx % heads] = -INFINITY;
+      }
+  }
+}
+
 // One work item = 32 query tokens x the 8 query heads of one kv head. A
 // workgroup keeps the list of its items in LDS as {sequence start, valid
 // length, first query, first tile of the sequence}; the rest follows.
@@ -659,6 +779,15 @@ __device__ __forceinline__ Item item_from(int4 e, int window) {
 // stay close.
 __device__ __forceinline__ int item_rank(int j, int w, int nw) {
   return j * nw + ((j & 1) ? nw - 1 - w : w);
+}
+
+// Place of workgroup wg (of nwg serving one kv head) in the snake. Workgroup
+// b = 4 wg + g of attn_kernel runs on XCD b % 8 = g + 4 (wg & 1), so the even
+// workgroups take the first half of each round and the odd ones the second:
+// consecutive ranks, which for equal costs are neighbouring query blocks of a
+// sequence sharing most of their key tiles, then share an XCD and its L2.
+__device__ __forceinline__ int snake_pos(int wg, int nwg) {
+  return (wg & 1) ? (nwg + 1) / 2 + (wg >> 1) : (wg >> 1);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tiles_rsrc(const Ws& ws, int g, int tfirst, int ntiles) {
@@ -773,8 +902,9 @@ __device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw,
 // the same SIMD. Group B runs half a tile behind group A, so on each SIMD one
 // wave feeds the matrix cores while the other runs its softmax. Key tiles
 // flow through a 4-stage LDS ring that does not stop at item boundaries: the
-// tile two slots ahead streams in meanwhile, and the next item's query rows
-// are fetched while the current item runs.
+// tile two slots ahead streams in meanwhile, copied by group A alone (group A
+// waits at the ring barrier for group B, which is the critical path), and the
+// next item's query rows are fetched while the current item runs.
 //
 // F16 (the FP16 attention-compute variant): q holds the prepared fp16 rows,
 // the tiles are fp16, the products v_mfma_f32_32x32x16_f16, and `out` is FP32
@@ -784,10 +914,11 @@ __device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw,
 template <bool F16>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __restrict__ q,
                                                             const float* __restrict__ q_norm_w,
+                                                            const float* __restrict__ k_norm_w,
                                                             const float* __restrict__ sink,
                                                             const int* __restrict__ positions,
                                                             int window, int use_rope, float eps,
-                                                            Ws ws, void* __restrict__ outp,
+                                                            Ws ws, int n, void* __restrict__ outp,
                                                             float* __restrict__ lse) {
   constexpr float kBound = F16 ? 15.0f : kStaticBound;
   __shared__ uint4 smem[kStages][kTileVec];
@@ -801,23 +932,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   // launch keeps nj within kMaxItemsPerGroup.
   const int nitems = ws.hdr[2];
   const int rounds = nitems / nwg, rem = nitems - rounds * nwg;
-  const int nj = min(rounds + (((rounds & 1) ? nwg - 1 - wg : wg) < rem ? 1 : 0), kMaxItemsPerGroup);
-  if (nj == 0) return;
+  const int sp = snake_pos(wg, nwg);
+  const int nj = min(rounds + (((rounds & 1) ? nwg - 1 - sp : sp) < rem ? 1 : 0), kMaxItemsPerGroup);
+  if (nj > 0) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int col = lane & 31, half = lane >> 5;
   const int h = g * kHpg + wave;
   const bool group_b = wave >= 4;
-  const int voff = lane * 16 + wave * 1024;
+  const int voff = lane * 16 + (wave & 3) * 1024;  // group A's tile copies
   const bool rope = use_rope != 0;
   const bool qpos = rope && positions;
   const int q_ops = qpos ? 9 : 8;
+  const int slot_ops = group_b ? 0 : 8;  // tile loads per slot
   const float sk = sink[h] * kLog2e;
-  const float kmax = __uint_as_float((unsigned)ws.hdr[kHdrKMax + g]);  // max |k'| of this kv head
+  const float kmax = key_norm_bound(k_norm_w, lane);  // |k'| of every key is at most this
   if (tid < kD) s_qw[tid] = q_norm_w[tid];
   if (tid < kD / 2) s_rope[tid] = ws.rope_r[tid];
   for (int jj = tid; jj < nj; jj += kAttnThreads) {
-    const int2 it = ws.items[item_rank(jj, wg, nwg)];
+    const int2 it = ws.items[item_rank(jj, sp, nwg)];
     const int4 meta = ws.seq[it.x];
     s_items[jj] = make_int4(meta.x, meta.z, it.y * kBM, meta.w);
   }
@@ -843,7 +976,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     if (LOAD) {                                                 \
       RSRC = tiles_rsrc(ws, g, ctf, cn);                        \
       LOFF = ck * kTileBytes;                                   \
-      ops += 4;                                                 \
+      ops += slot_ops;                                          \
       if (++ck == cn) {                                         \
         ck = 0;                                                 \
         if (++cj < nj) {                                        \
@@ -862,16 +995,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     __amdgpu_buffer_rsrc_t r;
     int lo = 0;
     FLINT_NEXT_SLOT(ld, r, lo);
-    load_tile_async(r, voff, lo, smem[0], wave);
+    if (!group_b) load_tile_async4(r, voff, lo, smem[0], wave);
     end0 = ops;
     FLINT_NEXT_SLOT(ld, r, lo);
-    if (ld) load_tile_async(r, voff, lo, smem[1], wave);
+    if (ld && !group_b) load_tile_async4(r, voff, lo, smem[1], wave);
     end1 = ops;
   }
   QRaw qraw;
   load_q(q, positions, qpos, it, h, col, half, qraw);
   ops += q_ops;
   int endq = ops;  // `ops` after the current item's query loads
+  // group A's pending copies of the tile two slots ahead
+  bool pend = false;
+  __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, kBufferWord3);
+  int plo = 0;
+  uint4* pst = smem[0];
   bf16x8 qf[8];
   float qmax;
   q_prologue<F16>(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
@@ -901,6 +1039,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     for (int k = 0; k < it.ntiles; ++k, ++slot) {
       if (group_b) ring_barrier<F16>(k < 2 ? ops - endq : ops - end0);
       if (k > 0) {
+        if (pend) {  // group A's copies of the tile two slots ahead (see below)
+          load_tile_async4(pr, voff, plo, pst, wave);
+          pend = false;
+        }
         tile_softmax<F16>(s0, s1, st, pk, (it.tile_lo + k - 1) * kBN, it.t0, qrow, it.u, window, half);
         tile_pv<F16>(smem[(slot - 1) % kStages] + kTileVec / 2, lane, pk, st);
       }
@@ -909,8 +1051,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
       __amdgpu_buffer_rsrc_t r;
       int lo = 0;
       FLINT_NEXT_SLOT(ld, r, lo);
-      tile_logits<F16>(smem[slot % kStages], lane, qf, s0, s1, ld, r, voff, lo, smem[(slot + 2) % kStages],
-                       wave);
+      tile_logits<F16>(smem[slot % kStages], lane, qf, s0, s1);
+      // Group A copies the tile of slot + 2 into the stage the barrier freed,
+      // in one burst after its logits, at the top of the next body (or before
+      // the next item's query loads): measured faster than spreading the
+      // copies over the logits or the PV products, than the same burst in the
+      // block of the logits, and than issuing them from group B (which runs
+      // half a tile behind and is the critical path: group A waits for it at
+      // the barrier).
+      pend = ld && !group_b;
+      pr = r;
+      plo = lo;
+      pst = smem[(slot + 2) % kStages];
       end0 = end1;
       end1 = ops;
     }
@@ -918,6 +1070,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     // softmax and PV.
     const bool more = j + 1 < nj;
     Item nx = it;
+    if (pend) {  // before the next item's query rows, as the accounting assumes
+      load_tile_async4(pr, voff, plo, pst, wave);
+      pend = false;
+    }
     if (more) {
       nx = item_from(s_items[j + 1], window);
       load_q(q, positions, qpos, nx, h, col, half, qraw);
@@ -993,6 +1149,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     it = nx;
   }
 #undef FLINT_NEXT_SLOT
+  }  // nj > 0
+  zero_padded_rows<F16, kAttnThreads>(ws, n, g, 0, kHpg, wg, nwg, outp, lse);
 }
 
 // ----------------------------------------------------------------- mask helper
@@ -1090,15 +1248,6 @@ constexpr int kHalfThreads = 256;
 constexpr int kHStages = 2;
 constexpr int kMaxItemsHalf = 512;
 
-// One 16-byte vector per lane of a 32 KiB tile into a stage, for 4 waves.
-__device__ __forceinline__ void load_vec_async4(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff,
-                                                uint4* stage, int i, int wave) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rsrc,
-      (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(stage) + i * 4096 + wave * 1024),
-      16, voff, soff + i * 4096, 0, 0);
-}
-
 // tile_logits for 4-wave workgroups: eight tile loads per wave, one after
 // every second MFMA.
 __device__ __forceinline__ void tile_logits_h(const uint4* kt, int lane, const bf16x8* qf, f32x16& s0,
@@ -1132,10 +1281,11 @@ __device__ __forceinline__ void tile_logits_h(const uint4* kt, int lane, const b
 // attn_kernel.
 __global__ __launch_bounds__(kHalfThreads, 2) void attn_half_kernel(const uint16_t* __restrict__ q,
                                                                      const float* __restrict__ q_norm_w,
+                                                                     const float* __restrict__ k_norm_w,
                                                                      const float* __restrict__ sink,
                                                                      const int* __restrict__ positions,
                                                                      int window, int use_rope, float eps,
-                                                                     Ws ws, void* __restrict__ outp,
+                                                                     Ws ws, int n, void* __restrict__ outp,
                                                                      float* __restrict__ lse) {
   __shared__ uint4 smem[kHStages][kTileVec];
   __shared__ float s_qw[kD];
@@ -1147,7 +1297,7 @@ __global__ __launch_bounds__(kHalfThreads, 2) void attn_half_kernel(const uint16
   const int nitems = ws.hdr[2];
   const int rounds = nitems / nwg, rem = nitems - rounds * nwg;
   const int nj = min(rounds + (((rounds & 1) ? nwg - 1 - wg : wg) < rem ? 1 : 0), kMaxItemsHalf);
-  if (nj == 0) return;
+  if (nj > 0) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
@@ -1156,7 +1306,7 @@ __global__ __launch_bounds__(kHalfThreads, 2) void attn_half_kernel(const uint16
   const bool rope = use_rope != 0;
   const bool qpos = rope && positions;
   const float sk = sink[h] * kLog2e;
-  const float kmax = __uint_as_float((unsigned)ws.hdr[kHdrKMax + g]);
+  const float kmax = key_norm_bound(k_norm_w, lane);
   if (tid < kD) s_qw[tid] = q_norm_w[tid];
   if (tid < kD / 2) s_rope[tid] = ws.rope_r[tid];
   for (int jj = tid; jj < nj; jj += kHalfThreads) {
@@ -1272,6 +1422,8 @@ __global__ __launch_bounds__(kHalfThreads, 2) void attn_half_kernel(const uint16
     it = nx;
   }
 #undef FLINT_NEXT_SLOT_H
+  }  // nj > 0
+  zero_padded_rows<false, kHalfThreads>(ws, n, g, 4 * ((blockIdx.x >> 2) & 1), 4, wg, nwg, outp, lse);
 }
 
 // Query blocks per kv head up to which the forward runs on attn_half_kernel:
@@ -1353,31 +1505,37 @@ static int fwd_impl(const void* q, const void* k, const void* v, const float* q_
   const int* pos = rope ? positions : nullptr;
 
   (void)hipGetLastError();
-  if (phases & FLINT_PHASE_SCHEDULE)
-    launch_schedule(cu_seqlens, seqused, n_seqs, total_tokens, max_seqlen, window,
-                    (double)rope_theta, ws, st);
-  uint16_t* q16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.q16);
-  const dim3 kv_grid((unsigned)L.ntmax, kG);
-  if (phases & FLINT_PHASE_KV) {
-    if (f16) {
-      kv_prologue_kernel<true><<<kv_grid, 256, 0, st>>>(k, v, k_norm_w, pos, eps, rope, ws, out, lse);
-      q16_prep_kernel<<<kv_grid, 256, 0, st>>>(static_cast<const float*>(q), q_norm_w, pos, eps,
-                                               rope, ws, q16);
-    } else {
-      kv_prologue_kernel<false><<<kv_grid, 256, 0, st>>>(kh, vh, k_norm_w, pos, eps, rope, ws, oh, lse);
-    }
+  // The schedule and the K/V tiles in one launch (prep_kernel), then the
+  // attention kernel, which also zeroes the padded rows of `out`.
+  const int parts = ((phases & FLINT_PHASE_SCHEDULE) ? kPrepSchedule : 0) |
+                    ((phases & FLINT_PHASE_KV) ? kPrepKv : 0);
+  const double theta = (double)rope_theta;
+  if (parts) {
+    const unsigned grid = (unsigned)((parts & kPrepKv) ? L.ntmax * kG : 0) + ((parts & kPrepSchedule) ? 1u : 0u);
+    if (f16)
+      prep_kernel<true><<<grid, 256, 0, st>>>(k, v, k_norm_w, pos, cu_seqlens, seqused, n_seqs, total_tokens,
+                                              max_seqlen, window, theta, eps, rope, ws, parts);
+    else
+      prep_kernel<false><<<grid, 256, 0, st>>>(kh, vh, k_norm_w, pos, cu_seqlens, seqused, n_seqs,
+                                               total_tokens, max_seqlen, window, theta, eps, rope, ws,
+                                               parts);
   }
+  uint16_t* q16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.q16);
+  if (f16 && (phases & FLINT_PHASE_KV))  // reads the RoPE table the schedule wrote
+    q16_prep_kernel<<<dim3((unsigned)L.ntmax, kG), 256, 0, st>>>(
+        static_cast<const float*>(q), q_norm_w, pos, cu_seqlens, seqused, n_seqs, total_tokens, eps, rope,
+        ws, q16);
   if (phases & FLINT_PHASE_ATTEND) {
     const unsigned grid = (unsigned)(attn_groups(L.nqmax) * kG);
     if (f16)
-      attn_kernel<true><<<grid, kAttnThreads, 0, st>>>(q16, q_norm_w, sink, pos, window, rope, eps,
-                                                       ws, out, nullptr);
+      attn_kernel<true><<<grid, kAttnThreads, 0, st>>>(q16, q_norm_w, k_norm_w, sink, pos, window, rope,
+                                                       eps, ws, n_seqs, out, nullptr);
     else if (use_split_kernel(L.nqmax))
       attn_half_kernel<<<(unsigned)(attn_groups_half(L.nqmax) * kG * 2), kHalfThreads, 0, st>>>(
-          qh, q_norm_w, sink, pos, window, rope, eps, ws, oh, lse);
+          qh, q_norm_w, k_norm_w, sink, pos, window, rope, eps, ws, n_seqs, oh, lse);
     else
-      attn_kernel<false><<<grid, kAttnThreads, 0, st>>>(qh, q_norm_w, sink, pos, window, rope, eps,
-                                                        ws, oh, lse);
+      attn_kernel<false><<<grid, kAttnThreads, 0, st>>>(qh, q_norm_w, k_norm_w, sink, pos, window, rope,
+                                                        eps, ws, n_seqs, oh, lse);
   }
   if (hipGetLastError() != hipSuccess) return FLINT_ERR_HIP;
   if (debug_sync()) {

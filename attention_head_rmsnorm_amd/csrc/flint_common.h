@@ -40,7 +40,6 @@ constexpr int kStages = 4;  // LDS ring depth of the attention kernel
 // backward) then stays within its 32-bit byte count.
 constexpr int kMaxSeqLen = FLINT_MAX_SEQLEN;
 constexpr int kFragAhead = 4;  // MFMA operand fragments read ahead of their use
-constexpr int kHdrKMax = 4;    // header slots of the per-kv-head key-norm maxima
 // Word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs: 32-bit
 // data format, no swizzle, byte-granular range check against num_records.
 constexpr int kBufferWord3 = 0x00020000;
@@ -50,20 +49,21 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 
 struct Ws {
-  int* hdr;       // [0] device-data error bits, [1] key tiles, [2] query blocks,
-                  // [kHdrKMax + g] max |k'| of kv head g (FP32 bits, set by the K/V prologue)
+  int* hdr;       // [0] device-data error bits, [1] key tiles (packed layout), [2] query
+                  // blocks, [3] 64-row units holding padded rows (forward layout)
   unsigned long long* rope_r;  // [64] theta^(-c/64) / (2 pi) as a 0.64 fixed-point fraction
   int4* seq;      // [n] {start, length, valid length, first tile}
   int* tbase;     // [n+1] first key tile of each sequence
   int* qbase;     // [n+1] first query block of each sequence
-  int2* tiles;    // [ntmax] {sequence, tile in sequence}
+  int* pbase;     // [n+1] first padded 64-row unit of each sequence (forward layout)
+  int2* tiles;    // [ntmax] {sequence, tile in sequence} (packed layout)
   int2* items;    // [nqmax] {sequence, query block}, most work first
   char* kv;       // [kG][ntmax][kTileBytes]
   int ntmax;
 };
 
 struct Layout {
-  size_t hdr, rope_r, seq, tbase, qbase, tiles, items, kv, q16, total;
+  size_t hdr, rope_r, seq, tbase, qbase, pbase, tiles, items, kv, q16, total;
   int64_t ntmax, nqmax;
 };
 
@@ -81,6 +81,7 @@ static inline Layout make_layout(int64_t T, int64_t n, bool with_kv = true, bool
   L.seq = o;   o = align_up(o + (size_t)n * sizeof(int4), 256);
   L.tbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
   L.qbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
+  L.pbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
   L.tiles = o; o = align_up(o + (size_t)L.ntmax * sizeof(int2), 256);
   L.items = o; o = align_up(o + (size_t)L.nqmax * sizeof(int2), 256);
   L.kv = o;
@@ -157,9 +158,12 @@ __device__ __forceinline__ int frag_index(int blk, int steps, int kk, int half, 
   return (blk * steps + kk) * 64 + half * 32 + col;
 }
 
-// Exclusive scan over the 1024 threads of a block; *total gets the sum.
-// Wave-level shuffle scans, then a scan of the 16 wave totals.
-__device__ int block_excl_scan(int v, int* tmp, int* total) {
+// Exclusive scan over the NT threads of a block; *total gets the sum.
+// Wave-level shuffle scans, then a scan of the NT / 64 wave totals (tmp holds
+// at least that many ints).
+template <int NT>
+__device__ int block_excl_scan_t(int v, int* tmp, int* total) {
+  constexpr int W = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -170,19 +174,24 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < 16 ? tmp[lane] : 0;
+    int w = lane < W ? tmp[lane] : 0;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
+    for (int off = 1; off < W; off <<= 1) {
       const int y = __shfl_up(w, off);
       if (lane >= off) w += y;
     }
-    if (lane < 16) tmp[lane] = w;
+    if (lane < W) tmp[lane] = w;
   }
   __syncthreads();
   const int base = wave > 0 ? tmp[wave - 1] : 0;
-  *total = tmp[15];
+  *total = tmp[W - 1];
   __syncthreads();
   return base + x - v;
+}
+
+// The same over the 1024 threads of a block.
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  return block_excl_scan_t<1024>(v, tmp, total);
 }
 
 // Largest s in [0, n) with base[s] <= e (base non-decreasing, base[0] = 0).
@@ -191,6 +200,22 @@ __device__ __forceinline__ int find_seq(const int* base, int n, int e) {
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (base[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Key tiles of the forward layout: sequence s owns the tiles from
+// cu[s] / 64 + s on, one per 64 keys. These ranges never overlap (cu[s+1] / 64
+// + s + 1 >= cu[s] / 64 + s + ceil(len / 64)) and stay below T / 64 + n, and
+// a tile's sequence follows from cu_seqlens alone: the largest s with
+// cu[s] / 64 + s <= e (for valid cu_seqlens; any s in [0, n) otherwise).
+__device__ __forceinline__ int tile_base(int cu_s, int s) { return (cu_s >> 6) + s; }
+
+__device__ __forceinline__ int tile_seq(const int* cu, int n, int e) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_base(cu[mid], mid) <= e) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -239,6 +264,7 @@ static inline Ws ws_at(void* workspace, const Layout& L) {
   ws.seq = reinterpret_cast<int4*>(base + L.seq);
   ws.tbase = reinterpret_cast<int*>(base + L.tbase);
   ws.qbase = reinterpret_cast<int*>(base + L.qbase);
+  ws.pbase = reinterpret_cast<int*>(base + L.pbase);
   ws.tiles = reinterpret_cast<int2*>(base + L.tiles);
   ws.items = reinterpret_cast<int2*>(base + L.items);
   ws.kv = base + L.kv;
@@ -246,8 +272,9 @@ static inline Ws ws_at(void* workspace, const Layout& L) {
   return ws;
 }
 
-// Enqueues the schedule kernel of the forward (sequence table, key tiles,
-// query blocks sorted by work, RoPE frequencies) on `st`.
+// Enqueues the schedule kernel (sequence table, key tiles in the packed
+// layout, query blocks sorted by work, RoPE frequencies) on `st`; the
+// backward's layout.
 void launch_schedule(const int* cu, const int* seqused, int n, int T, int max_seqlen, int window,
                      double theta, const Ws& ws, hipStream_t st);
 

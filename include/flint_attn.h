@@ -43,7 +43,7 @@
  * workspace must not overlap on the device.
  *
  * Asynchrony. flint_attn_fwd validates its host arguments synchronously,
- * enqueues three kernels on `stream` and returns. Argument errors return a
+ * enqueues two kernels on `stream` and returns. Argument errors return a
  * negative status and launch nothing. Errors in device-resident data
  * (cu_seqlens, seqused) are detected on the device: the call then writes
  * nothing to `out` and records the error in the workspace, where
@@ -166,11 +166,13 @@ int flint_attn_fwd_static(const void* q, const void* k, const void* v, const flo
                           int32_t num_kv_heads, int32_t head_dim, int32_t window,
                           int32_t use_rope, float rope_theta, float eps, void* out, void* stream);
 
-/* Phases of flint_attn_fwd, in the order they must run on one stream. */
-#define FLINT_PHASE_SCHEDULE 1 /* check cu_seqlens/seqused; lay out tiles and query blocks */
-#define FLINT_PHASE_KV 2       /* normalize + rotate K, transpose V into the workspace;
-                                  zero the padded rows of out                        */
-#define FLINT_PHASE_ATTEND 4   /* the attention kernel; writes the valid rows of out  */
+/* Phases of flint_attn_fwd, in the order they must run on one stream
+ * (SCHEDULE and KV run in one launch when both are asked for). */
+#define FLINT_PHASE_SCHEDULE 1 /* check cu_seqlens/seqused; lay out the query blocks
+                                  and the padded rows                                */
+#define FLINT_PHASE_KV 2       /* normalize + rotate K, transpose V into the workspace */
+#define FLINT_PHASE_ATTEND 4   /* the attention kernel; writes every row of out
+                                  (padded rows as zeros)                             */
 #define FLINT_PHASE_ALL 7
 
 /*
