@@ -7,7 +7,11 @@ and the attention kernel's fraction of the bf16 dense MFMA peak.
 Default workload: full-attention NoPE prefill, batch 1, S = 8192, 32 query /
 4 key-value heads, head dim 128, FP32 sinks ~N(0,1), bf16 inputs ~N(0,1) from
 a seeded generator, resident in HBM before the timed region. One step = one
-flint_attn_fwd call (schedule, K/V prologue, attention kernel).
+flint_attn_fwd call: the preparation launch (schedule and K/V tiles) and the
+attention kernel. Before the W warm-up steps the step runs for --settle-ms
+(default 300 ms) so that the K timed steps see the GPU's steady clock; the
+JSON line records that run ("settle") and a manifest of the run (seed,
+SHA-256 of the inputs and of the sources, versions, GPU).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config tstar|c1|c2|c3|c4|c4full|c5]
        python bench.py --decode [--decode-batch B] [--decode-len L] [--decode-window W] [--graph]
@@ -149,6 +153,88 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": 3}), flush=True)
 
 
+def settle(fn, args):
+    """Runs fn until args.settle_ms of wall time have passed (synchronizing
+    every 10 calls), before the warm-up steps.
+
+    The GPU raises its clock over the first ~100 ms of sustained load: on one
+    box the default workload measured 1006 TFLOP/s with 20 steps after 5
+    warm-up steps from idle, 1100 after 50 warm-up steps... and 1146 after
+    200 steps and 50 warm-ups. Settling first makes the K timed steps measure
+    the steady throughput whatever K and W are; the timed region is unchanged
+    (exactly K whole steps). Returns what was run, for the JSON line."""
+    import torch
+
+    ms = max(0.0, float(args.settle_ms))
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms and n < 100000:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        n += 10
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "steps": n}
+
+
+def tensor_sha256(*tensors):
+    """SHA-256 over the bytes of the given host or device tensors, in order."""
+    import torch
+
+    h = hashlib.sha256()
+    for t in tensors:
+        if t is None:
+            h.update(b"none")
+            continue
+        c = t.detach().contiguous().cpu()
+        h.update(str(tuple(c.shape)).encode() + str(c.dtype).encode())
+        h.update(c.view(torch.uint8).numpy().tobytes() if c.numel() else b"")
+    return h.hexdigest()
+
+
+def sources_sha256():
+    """SHA-256 over every source the measured library and this script are built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_head_rmsnorm_amd", "csrc")
+    paths = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    paths += [os.path.join(ROOT, "include", "flint_attn.h"), os.path.abspath(__file__)]
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + f.read())
+    return h.hexdigest()
+
+
+def manifest(seed=None, inputs=None):
+    """What the run was: the seeds, hashes of the inputs and of the sources,
+    the software versions and the GPU (the record a numerical comparison keeps)."""
+    import platform
+    import subprocess
+
+    import torch
+
+    git = None
+    try:
+        git = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except Exception:
+        pass
+    props = torch.cuda.get_device_properties(0)
+    rec = {
+        "seed": seed,
+        "inputs_sha256": inputs,
+        "sources_sha256": sources_sha256(),
+        "git_head": git,
+        "torch": torch.__version__,
+        "hip": getattr(torch.version, "hip", None),
+        "python": platform.python_version(),
+        "gpu": torch.cuda.get_device_name(0),
+        "gpu_arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "gpu_max_clock_mhz": getattr(props, "clock_rate", 0) / 1000.0 or None,
+        "host_cpus": os.cpu_count(),
+    }
+    return rec
+
+
 def decode_bench(args):
     """Decode step: append the new token, attend over the cache, merge the splits.
 
@@ -186,6 +272,7 @@ def decode_bench(args):
     call = [p(q), p(k1), p(v1), p(qw), p(kw), p(sinks), 0, p(cache.length), B, p(cache.k),
             p(cache.vt), cache.cap, 32, 4, 128, W, int(use_rope), 1.0e6, 1.0e-6,
             p(cache.workspace), cache.workspace.numel(), p(out), int(stream.cuda_stream)]
+    settled = settle(lambda: fa.flint_attn_decode(*call), args)
     for _ in range(args.warmup):
         fa.flint_attn_decode(*call)
     torch.cuda.synchronize()
@@ -227,6 +314,7 @@ def decode_bench(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settled,
         "ms_per_step": round(ms, 5),
         "tokens_per_s": round(B / (ms * 1e-3), 1),
         "higher_is_better": True,
@@ -307,6 +395,7 @@ def backward_bench(args):
     call = [p(q), p(k), p(v), p(qw), p(kw), p(sk), p(pos), p(cu), p(su), n, mx, T, 32, 4, 128,
             layer.window, int(layer.use_rope), layer.theta, layer.eps, p(out), p(lse), p(dout),
             p(ws), nbytes, p(dq), p(dk), p(dv), p(dqw), p(dkw), p(dsk), int(stream.cuda_stream)]
+    settled = settle(lambda: fa.flint_attn_bwd(*call), args)
     for _ in range(args.warmup):
         st = fa.flint_attn_bwd(*call)
         if st != 0:
@@ -336,6 +425,7 @@ def backward_bench(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settled,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "dtype": "bf16",
@@ -402,6 +492,7 @@ def fp16_bench(args):
     call = [p(q), p(k), p(v), p(qw), p(kw), p(sk), p(pos), p(cu), p(su), n, mx, T, 32, 4, 128,
             layer.window, int(layer.use_rope), layer.theta, layer.eps, p(ws), nbytes, p(out),
             int(stream.cuda_stream)]
+    settled = settle(lambda: fa.flint_attn_fwd_f16(*call), args)
     for _ in range(args.warmup):
         st = fa.flint_attn_fwd_f16(*call)
         if st != 0:
@@ -431,6 +522,7 @@ def fp16_bench(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settled,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "dtype": "f16",
@@ -524,6 +616,7 @@ def bshd_docs_bench(args):
             if st != 0:
                 raise RuntimeError("BSHD documents step failed")
 
+        settled = settle(step, args)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -546,6 +639,7 @@ def bshd_docs_bench(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settled,
         "ms_per_step": recs["in_place"]["ms_per_step"],
         "higher_is_better": True,
         "dtype": "bf16",
@@ -702,6 +796,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="tstar")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="run the step this long before the warm-up steps (GPU clock ramp); 0 = off")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--copy-probe", action="store_true")
@@ -781,6 +877,7 @@ def main():
         if st != 0:
             raise RuntimeError(f"flint_attn_fwd_phases failed: {fa.flint_attn_strerror(st)}")
 
+    settled = settle(step, args)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -863,6 +960,10 @@ def main():
             "traffic_GBs": None if traffic is None else round(traffic / (attn_ms * 1e-3) / 1e9, 1),
         },
         "wall_s_timed": round(wall, 4),
+        "settle": settled,
+        "manifest": manifest(seed=wl.seed, inputs=tensor_sha256(wl.q, wl.k, wl.v, wl.q_norm_w, wl.k_norm_w,
+                                                                 wl.sinks, wl.cu_seqlens, wl.seqused,
+                                                                 wl.positions)),
     }
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wl, layer, args.cpu_rows)
