@@ -330,8 +330,12 @@ def _stream_handle(device) -> int:
     return int(torch.cuda.current_stream(device).cuda_stream)
 
 
-def seqused_from_mask(attention_mask):
-    """[B, S] binary mask (1 = valid, trailing padding only) -> int32 [B] on the device."""
+def seqused_from_mask(attention_mask, check: bool = True):
+    """[B, S] binary mask (1 = valid, trailing padding only) -> int32 [B] on the device.
+
+    With ``check`` the host reads the count of rows that are not trailing
+    padding and raises if there is one (a synchronization); without it such
+    rows get length -1, which the forward reports as a device-data error."""
     import torch
 
     if attention_mask.dim() != 2:
@@ -347,7 +351,7 @@ def seqused_from_mask(attention_mask):
                                       _stream_handle(m.device))
     if st != FLINT_OK:
         raise FlintError(st, "flint_attn_seqused_from_mask")
-    if int(n_bad.item()) != 0:
+    if check and int(n_bad.item()) != 0:
         raise ValueError("attention_mask has non-trailing padding; arbitrary padding uses THD "
                          "packing (pass cu_seqlens)")
     return seqused
@@ -430,9 +434,19 @@ def bshd_plan(attention_mask, document_ids, batch: int, seqlen: int, device):
 _NEG_INF_BITS = 0xFF800000  # float32 -inf as a 32-bit word
 
 
+FLINT_MAX_SEQLEN = 2097152
+
+
 def _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, attention_mask,
-                seqused, max_seqlen, dtype=None, document_ids=None) -> _Args:
-    """Checks the layer's tensors; returns the call's THD description."""
+                seqused, max_seqlen, dtype=None, document_ids=None, sync=True) -> _Args:
+    """Checks the layer's tensors; returns the call's THD description.
+
+    Reads nothing back from the device except, with ``sync`` (the default),
+    the counts of the BSHD plan when there is an attention_mask or
+    document_ids. Without ``sync``, an attention_mask alone is taken as
+    trailing padding (its lengths stay on the device; a row with a hole is
+    reported by the forward as a device-data error), and document_ids are
+    refused."""
     import torch
 
     if not q.is_cuda:
@@ -458,9 +472,15 @@ def _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, atten
         cu = torch.arange(0, T + 1, max(S, 1), dtype=torch.int32, device=dev)[:B + 1]
         n = B
         mx = S
-        if attention_mask is not None or document_ids is not None:
-            if seqused is not None:
-                raise ValueError("pass attention_mask / document_ids or seqused, not both")
+        if (attention_mask is not None or document_ids is not None) and seqused is not None:
+            raise ValueError("pass attention_mask / document_ids or seqused, not both")
+        if not sync and document_ids is not None:
+            raise ValueError("document_ids need the plan's counts on the host (sync=True)")
+        if not sync and attention_mask is not None:
+            if tuple(attention_mask.shape) != (B, S):
+                raise ValueError("attention_mask must be [batch, seqlen]")
+            seqused = seqused_from_mask(attention_mask, check=False)
+        elif attention_mask is not None or document_ids is not None:
             info, cu, seqused, pack, unpack = bshd_plan(attention_mask, document_ids, B, S, dev)
             n, mx, T = info[0], info[1], info[2]
             if positions is not None and pack is not None:
@@ -480,9 +500,9 @@ def _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, atten
             cu = cu_seqlens
             if cu.dtype != torch.int32 or not cu.is_contiguous() or cu.device != dev:
                 raise TypeError("cu_seqlens must be a contiguous int32 tensor on the device")
-            mx = max_seqlen
-            if mx is None:
-                mx = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+            # without max_seqlen the bound is T itself (capped at the longest
+            # sequence the kernels take); a longer sequence is a device-data error
+            mx = max_seqlen if max_seqlen is not None else min(T, FLINT_MAX_SEQLEN)
         n = cu.numel() - 1
     else:
         raise ValueError("q must be [B, S, H, D] or [T, H, D]")
@@ -500,7 +520,7 @@ def flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens
                attention_mask=None, document_ids=None, seqused=None,
                max_seqlen: Optional[int] = None, window: int = 513, use_rope: bool = True,
                rope_theta: float = 1.0e6, eps: float = 1.0e-6, out=None, workspace=None,
-               return_lse: bool = False):
+               return_lse: bool = False, sync: bool = True, check: bool = False):
     """Sink-aware GQA attention forward on torch tensors.
 
     q: bf16 [B, S, 32, 128] (BSHD) or [T, 32, 128] (THD); k, v: bf16 with 4
@@ -512,11 +532,20 @@ def flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens
     index in the sequence or document). Returns the output in q's layout; with
     ``return_lse`` also the per-row normalizer, float32 [..., 32] in
     natural-log units (what the backward takes; -inf on padding).
+
+    Device-data errors (bad cu_seqlens or seqused, a row of attention_mask with
+    a hole under ``sync=False``) are found on the device: the call then writes
+    nothing to the output, which holds whatever it held (uninitialized memory
+    when the wrapper allocated it). ``check=True`` synchronizes after the call
+    and raises FlintError on such an error; otherwise read it with
+    ``flint_attn_device_status(workspace)``. ``sync=False`` makes the call read
+    nothing back from the device (for HIP graph capture): an attention_mask is
+    then taken as trailing padding and document_ids are refused.
     """
     import torch
 
     a = _layer_args(q, k, v, q_norm_w, k_norm_w, sinks, positions, cu_seqlens, attention_mask,
-                    seqused, max_seqlen, document_ids=document_ids)
+                    seqused, max_seqlen, document_ids=document_ids, sync=sync)
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
@@ -533,13 +562,24 @@ def flint_attn(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens
         st = flint_attn_fwd(*args, _stream_handle(dev))
         if st != FLINT_OK:
             raise FlintError(st, "flint_attn_fwd")
+        _check_device(check, workspace, dev)
         return a.scatter(o, out)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
     ls = lse if a.pack is None else torch.empty((a.T, q.shape[-2]), dtype=torch.float32, device=dev)
     st = flint_attn_fwd_lse(*args, _ptr(ls), _stream_handle(dev))
     if st != FLINT_OK:
         raise FlintError(st, "flint_attn_fwd_lse")
+    _check_device(check, workspace, dev)
     return a.scatter(o, out), a.scatter(ls, lse, fill=_NEG_INF_BITS)
+
+
+def _check_device(check, workspace, dev):
+    """With ``check``: synchronizes and raises on a device-data error of the call."""
+    if not check:
+        return
+    st, flags = flint_attn_device_status(_ptr(workspace), _stream_handle(dev))
+    if st != FLINT_OK:
+        raise FlintError(st, f"flint_attn device data (flags {flags})")
 
 
 def flint_attn_f16(q, k, v, q_norm_w, k_norm_w, sinks, *, positions=None, cu_seqlens=None,

@@ -1177,8 +1177,11 @@ __global__ __launch_bounds__(1024) void mask_kernel(const uint8_t* __restrict__ 
     atomicMin(&s_first, first);
     __syncthreads();
     if (tid == 0) {
-      seqused[b] = s_cnt;
-      if (s_cnt != s_first) ++s_bad;
+      // a row that is not ones followed by zeros gets the invalid length -1,
+      // which the forward reports as a device-data error
+      const bool bad = s_cnt != s_first;
+      seqused[b] = bad ? -1 : s_cnt;
+      if (bad) ++s_bad;
     }
     __syncthreads();
   }
@@ -1230,6 +1233,12 @@ static int64_t attn_groups(int64_t nqmax) {
     if (dev >= 0 && dev < 64) cus[dev] = n;
   }
   int64_t per_head = n / kG > 0 ? n / kG : 1;
+  // FLINT_ATTN_WORKGROUPS=<n> sets the workgroups per kv head (clamped as
+  // below): the results do not depend on it, which the tests check
+  if (const char* e = getenv("FLINT_ATTN_WORKGROUPS")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v > 0) per_head = v;
+  }
   // each workgroup's item list fits its LDS table
   const int64_t need = (nqmax + kMaxItemsPerGroup - 1) / kMaxItemsPerGroup;
   if (per_head < need) per_head = need;

@@ -199,7 +199,10 @@ int flint_attn_fwd_phases(const void* q, const void* k, const void* v, const flo
  * packing (flint.layers page, FlintAttention.forward, attention_mask), so
  * each row must be ones followed by zeros. Writes seqused[b] (device int32
  * [batch]) and *n_bad (device int32) = the number of rows that are not of that
- * form (their seqused is the count of ones). Asynchronous on `stream`.
+ * form. Such a row gets seqused = -1, which flint_attn_fwd reports as the
+ * device-data error FLINT_DEV_SEQUSED (out untouched), so the lengths can go
+ * to the forward without the host reading n_bad first. Asynchronous on
+ * `stream`.
  */
 int flint_attn_seqused_from_mask(const uint8_t* mask, int32_t batch, int32_t seqlen,
                                  int32_t* seqused, int32_t* n_bad, void* stream);

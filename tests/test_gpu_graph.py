@@ -106,3 +106,59 @@ def test_backward_replayed_from_a_hip_graph():
         assert call(out, torch.cuda.current_stream(d)) == fa.FLINT_OK
     _replays(g, out, ref)
     assert np.isfinite(ref[5].cpu().numpy()).all()
+
+
+def _bshd_inputs(d):
+    wl = make_custom(4343, [300, 300, 300], layout="bshd", seqused=[300, 120, 0])
+    B, S = 3, 300
+    t = dict(q=wl.q.to(d).view(B, S, 32, 128), k=wl.k.to(d).view(B, S, 4, 128),
+             v=wl.v.to(d).view(B, S, 4, 128), qw=wl.q_norm_w.to(d), kw=wl.k_norm_w.to(d),
+             sk=wl.sinks.to(d), mask=wl.attention_mask().to(d))
+    return wl, t
+
+
+def test_torch_wrapper_with_attention_mask_replayed_from_a_hip_graph():
+    """flint_attn(..., attention_mask=..., sync=False) reads nothing back from
+    the device, so the whole wrapper call (mask lengths, row starts, workspace
+    and output allocation, the forward) can be captured; every replay equals
+    the eager call, which equals the default (plan) path bit for bit."""
+    d = torch.device("cuda", 0)
+    wl, t = _bshd_inputs(d)
+    kw = dict(attention_mask=t["mask"], window=SLIDING.window, use_rope=True)
+    args = (t["q"], t["k"], t["v"], t["qw"], t["kw"], t["sk"])
+    ref = fa.flint_attn(*args, sync=False, **kw)
+    planned = fa.flint_attn(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, planned)
+    s = torch.cuda.Stream(d)
+    s.wait_stream(torch.cuda.current_stream(d))
+    with torch.cuda.stream(s):  # warm the allocator's graph-capture path
+        fa.flint_attn(*args, sync=False, **kw)
+    torch.cuda.current_stream(d).wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = fa.flint_attn(*args, sync=False, **kw)
+    _replays(g, [out], [ref])
+
+
+def test_unsynced_mask_with_a_hole_is_a_device_error():
+    """Under sync=False a mask row with a hole becomes length -1: the forward
+    reports FLINT_DEV_SEQUSED and leaves the output untouched; check=True
+    raises it."""
+    d = torch.device("cuda", 0)
+    wl, t = _bshd_inputs(d)
+    mask = t["mask"].clone()
+    mask[1, 200] = 1  # row 1: 120 valid tokens, then a valid token after padding
+    args = (t["q"], t["k"], t["v"], t["qw"], t["kw"], t["sk"])
+    out = torch.full_like(t["q"], 3.0)
+    nbytes = fa.flint_attn_workspace_bytes(900, 3, 300)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=d)
+    fa.flint_attn(*args, attention_mask=mask, sync=False, out=out, workspace=ws)
+    st, flags = fa.flint_attn_device_status(ws.data_ptr(), torch.cuda.current_stream(d).cuda_stream)
+    assert st == fa.FLINT_ERR_DEVICE_DATA and flags & 16
+    assert torch.all(out == 3.0)
+    with pytest.raises(fa.FlintError):
+        fa.flint_attn(*args, attention_mask=mask, sync=False, check=True)
+    su = fa.seqused_from_mask(mask, check=False)
+    assert su.tolist() == [300, -1, 0]

@@ -245,6 +245,8 @@ def test_mask_helper():
     m[2, 10] = 1  # a hole: not trailing padding
     with pytest.raises(ValueError, match="THD"):
         fa.seqused_from_mask(m)
+    # without the host check the row gets the invalid length -1
+    assert fa.seqused_from_mask(m, check=False).tolist() == [50, 7, -1, 1]
 
 
 def test_empty_input():
@@ -314,3 +316,24 @@ def test_c5_rows_across_sequence():
     ref = oracle_rows("c5", 0, rows, workers=min(16, os.cpu_count() or 1))
     stats = grade(got, ref, wl, rows=rows, what="c5")
     _log(f"      {stats}")
+
+
+@pytest.mark.parametrize("groups", ["1", "3", "17", "64", "300"])
+def test_persistent_grid_size_does_not_change_bits(groups, monkeypatch):
+    """The persistent attention kernels deal the same items to however many
+    workgroups run them (FLINT_ATTN_WORKGROUPS per kv head): the outputs are
+    bit for bit those of the default grid, on the 8-wave kernel (a 3000-token
+    THD packing) and on the split kernel (a small one)."""
+    for lengths in ([1200, 1, 700, 1099], [200, 77, 64]):
+        wl = make_custom(260, lengths, layout="thd", seqused=None)
+        for layer in (SLIDING, FULL):
+            monkeypatch.delenv("FLINT_ATTN_WORKGROUPS", raising=False)
+            ref = run_gpu(wl, layer)
+            torch.cuda.synchronize()
+            monkeypatch.setenv("FLINT_ATTN_WORKGROUPS", groups)
+            got = run_gpu(wl, layer)
+            torch.cuda.synchronize()
+            monkeypatch.delenv("FLINT_ATTN_WORKGROUPS", raising=False)
+            _log(f"[gpu] workgroups per kv head {groups}: T={wl.total_tokens} {layer.name} "
+                 f"kernel {fa.flint_attn_fwd_kernel(wl.total_tokens, wl.n_seqs)}")
+            assert torch.equal(got, ref)
