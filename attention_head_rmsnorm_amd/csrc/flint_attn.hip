@@ -130,13 +130,6 @@ __device__ __forceinline__ float sumsq8t(const uint4& c) {
 
 // ----------------------------------------------------------------- schedule
 
-// RoPE frequency of channel pair c: theta^(-c/64) / (2 pi) < 1/(2 pi), scaled
-// by 2^64 so that it fits an unsigned 64-bit integer (a 0.64 fraction).
-__device__ __forceinline__ unsigned long long rope_ratio(double theta, int c) {
-  const double r = pow(theta, -(double)c / 64.0) * 0.15915494309189533577;
-  return (unsigned long long)(r * 18446744073709551616.0);
-}
-
 // Shared memory of schedule_body with NT threads.
 template <int NT>
 struct SchedLds {
@@ -158,7 +151,7 @@ __device__ void schedule_body(const int* __restrict__ cu, const int* __restrict_
                               SchedLds<NT>& sh) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.flags = 0;
-  if (tid < 64) ws.rope_r[tid] = rope_ratio(theta, tid);
+  if (tid < 64) ws.rope[tid] = rope_freq(theta, tid);
   __syncthreads();
 
   int flags = 0;
@@ -300,9 +293,24 @@ __device__ __forceinline__ bool tile_of(const int* __restrict__ cu, const int* _
 }
 
 // Shared memory of kv_tile.
+// Channel pairs (x[i], x[16 + i]), i < 16, turned by the RoPE angles of
+// frequencies f[i] at position pos.
+template <bool kMixed>
+__device__ __forceinline__ void rope16(float* x, int pos, const RopeFreq* f) {
+  const float pf = (float)pos;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float c, s;
+    rope_cos_sin<kMixed>(pos, pf, f[i], &c, &s);
+    const float a = x[i], b = x[16 + i];
+    x[i] = a * c - b * s;
+    x[16 + i] = b * c + a * s;
+  }
+}
+
 struct KvLds {
   __attribute__((aligned(16))) uint16_t vt[kD * kBN];
-  unsigned long long rope[kD / 2];
+  RopeFreq rope[kD / 2];
 };
 
 // One key tile e of kv head g, by 256 threads: RMSNorm + RoPE of K in FP32,
@@ -322,7 +330,7 @@ __device__ void kv_tile(int e, int g, const void* __restrict__ kp, const void* _
   if (!tile_of(cu, seqused, n, T, e, to)) return;
   const int start = to.start, u = to.u;
   const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
-  if (use_rope && tid < kD / 2) sh.rope[tid] = rope_ratio(theta, tid);
+  if (use_rope && tid < kD / 2) sh.rope[tid] = rope_freq(theta, tid);
   const int ell = to.j * kBN + r;
   const bool valid = ell < u;
   const size_t t = (size_t)start + ell;
@@ -362,14 +370,8 @@ __device__ void kv_tile(int e, int g, const void* __restrict__ kp, const void* _
   }
   if (use_rope && valid) {
     const int pos = positions ? positions[t] : ell;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float c, s;
-      rope_cos_sin(pos, sh.rope[16 * p + i], &c, &s);
-      const float a = x[i], b = x[16 + i];
-      x[i] = a * c - b * s;
-      x[16 + i] = b * c + a * s;
-    }
+    if (rope_wave_mixed(pos)) rope16<true>(x, pos, sh.rope + 16 * p);
+    else rope16<false>(x, pos, sh.rope + 16 * p);
   }
   {
     uint4* kfrag = reinterpret_cast<uint4*>(tile);
@@ -482,8 +484,14 @@ __global__ __launch_bounds__(256) void q16_prep_kernel(const float* __restrict__
   float cs[16], sn[16];
   if (use_rope) {
     const int pos = positions ? positions[t] : ell;
+    const float pf = (float)pos;
+    if (rope_wave_mixed(pos)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) rope_cos_sin(pos, ws.rope_r[16 * p + i], &cs[i], &sn[i]);
+      for (int i = 0; i < 16; ++i) rope_cos_sin<true>(pos, pf, ws.rope[16 * p + i], &cs[i], &sn[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rope_cos_sin<false>(pos, pf, ws.rope[16 * p + i], &cs[i], &sn[i]);
+    }
   }
   const float scale = kLog2e * 0.08838834764831845f;
   for (int hl = 0; hl < kHpg; ++hl) {
@@ -822,72 +830,79 @@ __device__ __forceinline__ void load_q(const uint16_t* q, const int* positions, 
   }
 }
 
+// Norm weight, RoPE and one bf16 rounding of a wave's query rows, into the
+// MFMA B-operand layout of Q^T; n2 accumulates the lane's sum of squares of
+// the rounded values. s_qw holds the query norm weights times the softmax
+// scale; channel c pairs with c + 64 under RoPE.
+template <bool kRope, bool kMixed>
+__device__ __forceinline__ void q_scale_rope(const QRaw& qraw, const float* s_qw, const RopeFreq* s_rope,
+                                             float rstd, int half, bf16x8* qf, float& n2) {
+  const float pf = (float)qraw.pos;
+  if constexpr (kRope) {
+    // channels 16kk + 8half + j pair with 16(kk+4) + 8half + j
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      float a[8], b[8];
+      unpack8(qraw.x[kk], a);
+      unpack8(qraw.x[kk + 4], b);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int c = 16 * kk + 8 * half + jj;
+        float cs, sn;
+        rope_cos_sin<kMixed>(qraw.pos, pf, s_rope[c], &cs, &sn);
+        const float x = a[jj] * (rstd * s_qw[c]), y = b[jj] * (rstd * s_qw[c + 64]);
+        a[jj] = x * cs - y * sn;
+        b[jj] = y * cs + x * sn;
+      }
+      const uint4 wa = pack8(a), wb = pack8(b);
+      n2 = sumsq8_dot(wb, sumsq8_dot(wa, n2));
+      qf[kk] = __builtin_bit_cast(bf16x8, wa);
+      qf[kk + 4] = __builtin_bit_cast(bf16x8, wb);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      float a[8];
+      unpack8(qraw.x[kk], a);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) a[jj] *= rstd * s_qw[16 * kk + 8 * half + jj];
+      const uint4 wa = pack8(a);
+      n2 = sumsq8_dot(wa, n2);
+      qf[kk] = __builtin_bit_cast(bf16x8, wa);
+    }
+  }
+}
+
 // Query prologue: RMSNorm, RoPE, softmax scale in log2 units and one bf16
 // rounding, in the MFMA B-operand layout of Q^T; qmax = max |q'| over the
 // wave's 32 queries. With F16 the rows arrive prepared (q16_prep_kernel) and
 // only qmax is formed.
 template <bool F16>
-__device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw,
-                                           const unsigned long long* s_rope, bool rope, float eps,
-                                           int half, bf16x8* qf, float& qmax) {
+__device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw, const RopeFreq* s_rope,
+                                           bool rope, float eps, int half, bf16x8* qf, float& qmax) {
+  float n2 = 0.f;
   if constexpr (F16) {
-    float n2 = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       qf[kk] = __builtin_bit_cast(bf16x8, qraw.x[kk]);
       n2 += sumsq8t<true>(qraw.x[kk]);
     }
-    n2 += __shfl_xor(n2, 32);
-    qmax = sqrtf(n2);
+  } else {
+    // The weight and frequency tables are re-read from LDS for every item; the
+    // empty asm hides that the offset is zero, so the reads are not hoisted and
+    // held in registers across the tile loop.
+    int z = 0;
+    asm volatile("" : "+s"(z));
+    s_qw += z;
+    s_rope += z;
+    float ss = 0.f;
 #pragma unroll
-    for (int off = 1; off < 32; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
-    qmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qmax)));
-    return;
-  }
-  // The weight and frequency tables are re-read from LDS for every item; the
-  // empty asm hides that the offset is zero, so the reads are not hoisted and
-  // held in registers across the tile loop.
-  int z = 0;
-  asm volatile("" : "+s"(z));
-  s_qw += z;
-  s_rope += z;
-  float ss = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) ss += sumsq8(qraw.x[kk]);
-  ss += __shfl_xor(ss, 32);
-  const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
-  const float scale = kLog2e * 0.08838834764831845f;
-  float n2 = 0.f;
-  // channels 16kk + 8half + j pair with 16(kk+4) + 8half + j under RoPE
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    float a[8], b[8];
-    unpack8(qraw.x[kk], a);
-    unpack8(qraw.x[kk + 4], b);
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      a[jj] *= rstd * s_qw[16 * kk + 8 * half + jj];
-      b[jj] *= rstd * s_qw[16 * (kk + 4) + 8 * half + jj];
-    }
-    if (rope) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        float c, sn;
-        rope_cos_sin(qraw.pos, s_rope[16 * kk + 8 * half + jj], &c, &sn);
-        const float x = a[jj], y = b[jj];
-        a[jj] = x * c - y * sn;
-        b[jj] = y * c + x * sn;
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      a[jj] *= scale;
-      b[jj] *= scale;
-    }
-    const uint4 wa = pack8(a), wb = pack8(b);
-    n2 += sumsq8(wa) + sumsq8(wb);
-    qf[kk] = __builtin_bit_cast(bf16x8, wa);
-    qf[kk + 4] = __builtin_bit_cast(bf16x8, wb);
+    for (int kk = 0; kk < 8; ++kk) ss = sumsq8_dot(qraw.x[kk], ss);
+    ss += __shfl_xor(ss, 32);
+    const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+    if (!rope) q_scale_rope<false, false>(qraw, s_qw, s_rope, rstd, half, qf, n2);
+    else if (!rope_wave_mixed(qraw.pos)) q_scale_rope<true, false>(qraw, s_qw, s_rope, rstd, half, qf, n2);
+    else q_scale_rope<true, true>(qraw, s_qw, s_rope, rstd, half, qf, n2);
   }
   n2 += __shfl_xor(n2, 32);
   qmax = sqrtf(n2);
@@ -922,8 +937,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
                                                             float* __restrict__ lse) {
   constexpr float kBound = F16 ? 15.0f : kStaticBound;
   __shared__ uint4 smem[kStages][kTileVec];
-  __shared__ float s_qw[kD];                    // q_norm weights
-  __shared__ unsigned long long s_rope[kD / 2];  // RoPE frequencies, 0.64 fixed point
+  __shared__ float s_qw[kD];                    // q_norm weights times the softmax scale
+  __shared__ RopeFreq s_rope[kD / 2];           // RoPE frequencies
   __shared__ int4 s_items[kMaxItemsPerGroup];
   const int g = blockIdx.x & (kG - 1);
   const int wg = blockIdx.x / kG, nwg = gridDim.x / kG;
@@ -947,8 +962,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   const int slot_ops = group_b ? 0 : 8;  // tile loads per slot
   const float sk = sink[h] * kLog2e;
   const float kmax = key_norm_bound(k_norm_w, lane);  // |k'| of every key is at most this
-  if (tid < kD) s_qw[tid] = q_norm_w[tid];
-  if (tid < kD / 2) s_rope[tid] = ws.rope_r[tid];
+  if (tid < kD) s_qw[tid] = q_norm_w[tid] * kQScale;
+  if (tid < kD / 2) s_rope[tid] = ws.rope[tid];
   for (int jj = tid; jj < nj; jj += kAttnThreads) {
     const int2 it = ws.items[item_rank(jj, sp, nwg)];
     const int4 meta = ws.seq[it.x];
@@ -1298,7 +1313,7 @@ __global__ __launch_bounds__(kHalfThreads, 2) void attn_half_kernel(const uint16
                                                                      float* __restrict__ lse) {
   __shared__ uint4 smem[kHStages][kTileVec];
   __shared__ float s_qw[kD];
-  __shared__ unsigned long long s_rope[kD / 2];
+  __shared__ RopeFreq s_rope[kD / 2];
   __shared__ int4 s_items[kMaxItemsHalf];
   const int g = blockIdx.x & (kG - 1);
   const int hh = (blockIdx.x >> 2) & 1;
@@ -1316,8 +1331,8 @@ __global__ __launch_bounds__(kHalfThreads, 2) void attn_half_kernel(const uint16
   const bool qpos = rope && positions;
   const float sk = sink[h] * kLog2e;
   const float kmax = key_norm_bound(k_norm_w, lane);
-  if (tid < kD) s_qw[tid] = q_norm_w[tid];
-  if (tid < kD / 2) s_rope[tid] = ws.rope_r[tid];
+  if (tid < kD) s_qw[tid] = q_norm_w[tid] * kQScale;
+  if (tid < kD / 2) s_rope[tid] = ws.rope[tid];
   for (int jj = tid; jj < nj; jj += kHalfThreads) {
     const int2 it = ws.items[item_rank(jj, wg, nwg)];
     const int4 meta = ws.seq[it.x];

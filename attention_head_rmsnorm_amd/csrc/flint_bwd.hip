@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void bwd_kv_prep_kernel(const uint16_t* __rest
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float c, s;
-      rope_cos_sin(pos, ws.f.rope_r[16 * p + i], &c, &s);
+      rope_cos_sin(pos, ws.f.rope[16 * p + i], &c, &s);
       const float a = x[i], bb = x[16 + i];
       x[i] = a * c - bb * s;
       x[16 + i] = bb * c + a * s;
@@ -398,26 +398,25 @@ __global__ __launch_bounds__(256) void bwd_q_prep_kernel(const uint16_t* __restr
     dr += __shfl_xor(dr, off);
   }
   const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+  // the norm weight times the softmax scale in log2 units, then RoPE, as the
+  // forward forms its query rows, so the logits recomputed here are the
+  // forward's own
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    x[i] *= rstd * q_norm_w[8 * p + i];
-    x[8 + i] *= rstd * q_norm_w[64 + 8 * p + i];
+    x[i] *= rstd * (q_norm_w[8 * p + i] * kQScale);
+    x[8 + i] *= rstd * (q_norm_w[64 + 8 * p + i] * kQScale);
   }
   if (use_rope && valid) {
     const int pos = positions ? positions[t] : ell;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float c, sn;
-      rope_cos_sin(pos, ws.f.rope_r[8 * p + i], &c, &sn);
+      rope_cos_sin(pos, ws.f.rope[8 * p + i], &c, &sn);
       const float a = x[i], bb = x[8 + i];
       x[i] = a * c - bb * sn;
       x[8 + i] = bb * c + a * sn;
     }
   }
-  // the softmax scale in log2 units, applied and rounded as in the forward, so
-  // the logits recomputed here are the forward's own
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] *= kLog2e * kInvSqrtD;
   const uint4 w0 = pack8(x), w1 = pack8(x + 8);
   uint4* qf = reinterpret_cast<uint4*>(tile);
   // channels 8p.. are k-step p>>1, half p&1; channels 64+8p.. are k-step
@@ -617,7 +616,7 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __re
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float cs, sn;
-        rope_cos_sin(pos, ws.f.rope_r[32 * db + 8 * (i >> 2) + 4 * half + (i & 3)], &cs, &sn);
+        rope_cos_sin(pos, ws.f.rope[32 * db + 8 * (i >> 2) + 4 * half + (i & 3)], &cs, &sn);
         const float a = acc[db][i], b = acc[db + 2][i];
         acc[db][i] = a * cs + b * sn;
         acc[db + 2][i] = b * cs - a * sn;
@@ -995,7 +994,7 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float cs, sn;
-      rope_cos_sin(pos, ws.f.rope_r[16 * p + i], &cs, &sn);
+      rope_cos_sin(pos, ws.f.rope[16 * p + i], &cs, &sn);
       const float a = gk[i], b = gk[16 + i];
       gk[i] = a * cs + b * sn;
       gk[16 + i] = b * cs - a * sn;

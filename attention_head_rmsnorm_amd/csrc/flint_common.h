@@ -27,6 +27,8 @@ constexpr int kTileVec = kTileBytes / 16;   // 16-byte vectors per tile
 constexpr int kBuckets = 4096;              // cost buckets of the schedule sort
 constexpr int kAttnThreads = 64 * kHpg;     // one wave per query head of a group
 constexpr float kLog2e = 1.4426950408889634f;
+// softmax scale of the query rows in log2 units: log2(e) / sqrt(128)
+constexpr float kQScale = kLog2e * 0.08838834764831845f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Keep a stale running max until a tile's max exceeds it by this much (log2
 // units): exp2 values then stay below 2^8, and the final O / l is unchanged.
@@ -48,10 +50,20 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 
+// RoPE frequency of channel pair c, omega_c / (2 pi) = theta^(-c/64) / (2 pi)
+// revolutions per position, held twice: as a 0.64 fixed-point fraction `r`
+// (an exact angle reduction for every int32 position) and as the unevaluated
+// float sum hi + lo of the same value (~48 significant bits; a reduction in
+// full-rate FP32 arithmetic for positions of magnitude below 2^24).
+struct RopeFreq {
+  unsigned long long r;
+  float hi, lo;
+};
+
 struct Ws {
   int* hdr;       // [0] device-data error bits, [1] key tiles (packed layout), [2] query
                   // blocks, [3] 64-row units holding padded rows (forward layout)
-  unsigned long long* rope_r;  // [64] theta^(-c/64) / (2 pi) as a 0.64 fixed-point fraction
+  RopeFreq* rope;  // [64] RoPE frequencies (rope_freq)
   int4* seq;      // [n] {start, length, valid length, first tile}
   int* tbase;     // [n+1] first key tile of each sequence
   int* qbase;     // [n+1] first query block of each sequence
@@ -63,7 +75,7 @@ struct Ws {
 };
 
 struct Layout {
-  size_t hdr, rope_r, seq, tbase, qbase, pbase, tiles, items, kv, q16, total;
+  size_t hdr, rope, seq, tbase, qbase, pbase, tiles, items, kv, q16, total;
   int64_t ntmax, nqmax;
 };
 
@@ -77,7 +89,7 @@ static inline Layout make_layout(int64_t T, int64_t n, bool with_kv = true, bool
   L.nqmax = (T + kBM - 1) / kBM + n;
   size_t o = 0;
   L.hdr = o;   o = align_up(o + 64 * sizeof(int), 256);
-  L.rope_r = o; o = align_up(o + 64 * sizeof(unsigned long long), 256);
+  L.rope = o; o = align_up(o + 64 * sizeof(RopeFreq), 256);
   L.seq = o;   o = align_up(o + (size_t)n * sizeof(int4), 256);
   L.tbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
   L.qbase = o; o = align_up(o + (size_t)(n + 1) * sizeof(int), 256);
@@ -115,16 +127,72 @@ __device__ __forceinline__ uint4 pack8(const float* x) {
   return make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
 }
 
-// cos and sin of the RoPE angle pos * omega_c. The angle in revolutions,
-// pos * omega_c / (2 pi), is reduced exactly: with R = omega_c / (2 pi) as a
-// 0.64 fixed-point fraction, pos * R mod 2^64 is the fractional revolution,
-// whose top 32 bits (as a signed value in [-1/2, 1/2)) feed the hardware
-// sine and cosine, which take revolutions and are accurate to ~1.3e-7.
-__device__ __forceinline__ void rope_cos_sin(int pos, unsigned long long r, float* c, float* s) {
+__device__ __forceinline__ RopeFreq rope_freq(double theta, int c) {
+  RopeFreq f;
+  const double x = pow(theta, -(double)c / 64.0) * 0.15915494309189533577;
+  f.r = (unsigned long long)(x * 18446744073709551616.0);
+  const double R = (double)f.r * 5.421010862427522170e-20;  // r / 2^64
+  f.hi = (float)R;
+  f.lo = (float)(R - (double)f.hi);
+  return f;
+}
+
+// |pos| < 2^24: the position is exact as a float.
+constexpr int kRopeFastPos = 1 << 24;
+__device__ __forceinline__ bool rope_pos_fast(int pos) {
+  return (unsigned)pos + (unsigned)(kRopeFastPos - 1) < (unsigned)(2 * kRopeFastPos - 1);
+}
+
+// Fractional revolutions of pos * r / 2^64, exactly up to the float rounding
+// of the top 32 bits: pos * r mod 2^64 taken as a signed value in [-1/2, 1/2)
+// (four 32-bit integer multiplies).
+__device__ __forceinline__ float rope_rev_exact(int pos, unsigned long long r) {
   const unsigned long long prod = (unsigned long long)(long long)pos * r;
-  const float rev = (float)(int)(unsigned)(prod >> 32) * 2.3283064365386963e-10f;  // 2^-32
+  return (float)(int)(unsigned)(prod >> 32) * 2.3283064365386963e-10f;  // 2^-32
+}
+
+// The same for |pos| < 2^24 (p = (float)pos exact), in FP32: p * hi splits
+// exactly into its rounded value xh and the FMA residual; the integer part of
+// xh is dropped exactly (fract) and the residual plus p * lo is added. The
+// residual and p * lo are each below 1/8 in magnitude, so the result lies in
+// (-1/4, 5/4) within ~2^-24 revolutions of the exact reduction.
+__device__ __forceinline__ float rope_rev_fast(float p, const RopeFreq& f) {
+  const float xh = p * f.hi;
+  const float e = fmaf(p, f.hi, -xh);
+  const float xl = fmaf(p, f.lo, e);
+  return __builtin_amdgcn_fractf(xh) + xl;
+}
+
+// cos and sin of the RoPE angle pos * omega_c from its revolutions; the
+// hardware sine and cosine take revolutions and are accurate to ~1.3e-7.
+// kMixed: the wave holds a position of magnitude >= 2^24 somewhere, so each
+// lane picks the exact reduction for its own such position (a lane's result
+// never depends on the other lanes' positions). Callers pick kMixed once per
+// wave with rope_wave_mixed.
+template <bool kMixed>
+__device__ __forceinline__ void rope_cos_sin(int pos, float pf, const RopeFreq& f, float* c, float* s) {
+  float rev = rope_rev_fast(pf, f);
+  if constexpr (kMixed) rev = rope_pos_fast(pos) ? rev : rope_rev_exact(pos, f.r);
   *s = __builtin_amdgcn_sinf(rev);
   *c = __builtin_amdgcn_cosf(rev);
+}
+
+__device__ __forceinline__ bool rope_wave_mixed(int pos) {
+  return __builtin_amdgcn_ballot_w64(!rope_pos_fast(pos)) != 0;
+}
+
+// One-off form (both reductions evaluated, the lane's own one kept).
+__device__ __forceinline__ void rope_cos_sin(int pos, const RopeFreq& f, float* c, float* s) {
+  rope_cos_sin<true>(pos, (float)pos, f, c, s);
+}
+
+// Sum of squares of eight packed bf16 values plus acc (v_dot2 of c with itself).
+__device__ __forceinline__ float sumsq8_dot(const uint4& c, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, c.x), __builtin_bit_cast(bf16x2_t, c.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, c.y), __builtin_bit_cast(bf16x2_t, c.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, c.z), __builtin_bit_cast(bf16x2_t, c.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, c.w), __builtin_bit_cast(bf16x2_t, c.w), acc, false);
+  return acc;
 }
 
 // acc + sum of the eight packed bf16 values in c (v_dot2 with (1, 1)).
@@ -260,7 +328,7 @@ static inline Ws ws_at(void* workspace, const Layout& L) {
   char* base = static_cast<char*>(workspace);
   Ws ws;
   ws.hdr = reinterpret_cast<int*>(base + L.hdr);
-  ws.rope_r = reinterpret_cast<unsigned long long*>(base + L.rope_r);
+  ws.rope = reinterpret_cast<RopeFreq*>(base + L.rope);
   ws.seq = reinterpret_cast<int4*>(base + L.seq);
   ws.tbase = reinterpret_cast<int*>(base + L.tbase);
   ws.qbase = reinterpret_cast<int*>(base + L.qbase);

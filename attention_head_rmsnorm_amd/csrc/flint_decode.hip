@@ -68,16 +68,10 @@ static DecLayout make_dec_layout(int64_t batch, int64_t cap) {
   return L;
 }
 
-// theta^(-c/64) / (2 pi) as a 0.64 fixed-point fraction (see rope_cos_sin).
-__device__ __forceinline__ unsigned long long rope_r_of(double theta, int c) {
-  const double r = pow(theta, -(double)c / 64.0) * 0.15915494309189533577;
-  return (unsigned long long)(r * 18446744073709551616.0);
-}
-
 // One row of 128 channels per wave, lane c holding channels c and c + 64 (a
 // RoPE pair): RMSNorm with weight w, RoPE at `pos`, then `scale`.
 __device__ __forceinline__ void norm_rope_row(const uint16_t* src, const float* w, float eps,
-                                              bool rope, int pos, unsigned long long r, float scale,
+                                              bool rope, int pos, const RopeFreq& f, float scale,
                                               int lane, float& a, float& b) {
   a = __uint_as_float((uint32_t)src[lane] << 16);
   b = __uint_as_float((uint32_t)src[lane + 64] << 16);
@@ -89,7 +83,7 @@ __device__ __forceinline__ void norm_rope_row(const uint16_t* src, const float* 
   b *= rstd * w[lane + 64];
   if (rope) {
     float c, sn;
-    rope_cos_sin(pos, r, &c, &sn);
+    rope_cos_sin(pos, f, &c, &sn);
     const float x = a, y = b;
     a = x * c - y * sn;
     b = y * c + x * sn;
@@ -135,11 +129,11 @@ __global__ __launch_bounds__(64 * (1 + kHpg)) void decode_append_kernel(
   if (slot < 0) return;
   const bool rope = use_rope != 0;
   const int pos = positions ? positions[(size_t)b * n_new + i] : t;
-  const unsigned long long r = rope ? rope_r_of(theta, lane) : 0ull;
+  const RopeFreq f = rope ? rope_freq(theta, lane) : RopeFreq{0ull, 0.f, 0.f};
   const size_t tok = (size_t)b * n_new + i;
   float a, c;
   if (wave == 0) {
-    norm_rope_row(k + (tok * kG + g) * kD, k_norm_w, eps, rope, pos, r, 1.0f, lane, a, c);
+    norm_rope_row(k + (tok * kG + g) * kD, k_norm_w, eps, rope, pos, f, 1.0f, lane, a, c);
     // block of 32 slots in the decode operand order (see DecFrags)
     const size_t blk = ((size_t)b * kG + g) * (cap / kDecBlock) + slot / kDecBlock;
     const int kb = slot % kDecBlock;
@@ -152,7 +146,7 @@ __global__ __launch_bounds__(64 * (1 + kHpg)) void decode_append_kernel(
     vblk[dec_v_index(kb, lane + 64)] = vr[lane + 64];
   } else if (q) {
     const int h = g * kHpg + wave - 1;
-    norm_rope_row(q + ((size_t)b * kH + h) * kD, q_norm_w, eps, rope, pos, r,
+    norm_rope_row(q + ((size_t)b * kH + h) * kD, q_norm_w, eps, rope, pos, f,
                   kLog2e * 0.08838834764831845f, lane, a, c);
     uint16_t* qr = ws.q + ((size_t)b * kH + h) * kD;
     qr[lane] = bf16_bits(a);

@@ -126,3 +126,22 @@ def with_filler(wl, n_fill=2048, seed=90001):
 def kernel_of(wl):
     """The attention kernel the forward launches for this workload."""
     return fa.flint_attn_fwd_kernel(wl.total_tokens, wl.n_seqs)
+
+
+def huge_positions(wl, seed=5):
+    """The workload with RoPE positions of magnitude 2^24 and more on about
+    half of its tokens (both signs, the int32 limits and the values either
+    side of 2^24 among them) and small ones on the rest, interleaved, so that
+    waves hold both kinds. Positions of magnitude below 2^24 are exact as
+    floats, which the fast angle reduction relies on; the others take the
+    exact integer reduction lane by lane."""
+    rng = np.random.default_rng(seed)
+    T = wl.total_tokens
+    big = rng.integers(2 ** 24, 2 ** 31, size=T, dtype=np.int64)
+    big = np.where(rng.random(T) < 0.5, big, -big)
+    small = rng.integers(-(2 ** 20), 2 ** 20, size=T, dtype=np.int64)
+    pos = np.where(rng.random(T) < 0.5, big, small)
+    edges = [2 ** 24 - 1, 2 ** 24, -(2 ** 24 - 1), -(2 ** 24), 2 ** 31 - 1, -(2 ** 31), 0, -1]
+    pos[: min(T, len(edges))] = edges[: min(T, len(edges))]
+    wl.positions = torch.from_numpy(np.clip(pos, -(2 ** 31), 2 ** 31 - 1).astype(np.int32))
+    return wl

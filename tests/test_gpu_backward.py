@@ -30,7 +30,7 @@ from workload import Layer, make_custom, make_workload
 from workload.gen import FULL, SLIDING, draw_dout
 
 from .common import f64, i64
-from .gpu_common import to_np, valid_rows
+from .gpu_common import huge_positions, to_np, valid_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -150,6 +150,7 @@ CASES = [
     ("window 1", make_custom(309, [150]), Layer(window=1, use_rope=False)),
     ("full rope", make_custom(310, [600]), Layer(window=0, use_rope=True)),
     ("norm x1.6", make_custom(311, [500], norm_scale=1.6), SLIDING),
+    ("positions beyond 2^24", huge_positions(make_custom(312, [260, 90])), SLIDING),
 ]
 
 

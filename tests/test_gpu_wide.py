@@ -23,7 +23,7 @@ from workload.gen import FULL, SLIDING
 
 from .common import f64, oracle_for
 from .rounding_bound import U_BF16, perturbation_sigma
-from .gpu_common import (check_against_oracle, grade, kernel_of, run_gpu, to_np,
+from .gpu_common import (check_against_oracle, grade, huge_positions, kernel_of, run_gpu, to_np,
                          valid_rows, with_filler)
 from .test_gpu_parity import SMALL
 
@@ -155,6 +155,19 @@ def test_thd_document_equals_alone_bitwise_wide():
             alone = run_gpu(one, layer)
             torch.cuda.synchronize()
             assert torch.equal(packed[a:b], alone[:n]), f"document {d} {layer.name}"
+
+
+@pytest.mark.parametrize("layer", [SLIDING, Layer(window=0, use_rope=True)], ids=["sliding", "full-rope"])
+def test_positions_beyond_2_24_both_kernels(layer):
+    """RoPE positions up to the int32 limits, beside small ones in the same
+    waves: keys (the K tiles) and queries (the prologue) graded against the
+    oracle, which turns them in FP64, on both kernels."""
+    wl = huge_positions(make_custom(241, [300, 77, 150], layout="thd"))
+    for w, rows, kern in _both(wl):
+        _log(f"[gpu] positions beyond 2^24: {layer.name} T={w.total_tokens} kernel={kern}")
+        assert kernel_of(w) == kern
+        stats, _ = check_against_oracle(w, layer, rows=rows)
+        _log(f"      {stats}")
 
 
 def test_deterministic_bitwise_wide():
