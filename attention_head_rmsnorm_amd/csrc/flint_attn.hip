@@ -723,15 +723,13 @@ __device__ __forceinline__ float key_norm_bound(const float* __restrict__ k_norm
 
 // Padded rows (index in the sequence at or past the valid length) of `out`
 // are exact zeros and their normalizer -INF (an empty softmax). The schedule
-// lists them in 64-row units (ws.pbase); unit i goes to workgroup i % nw of
-// the ones serving kv head g, which zeroes its `heads` query heads from
-// h0 = g * 8 + hoff on, with its NT threads. Nothing is written when the
-// schedule found invalid device data.
+// lists them in nu 64-row units (ws.pbase; the caller passes nu = 0 when the
+// schedule found invalid device data, so nothing is written then); unit i goes
+// to workgroup i % nw of the ones serving kv head g, which zeroes its `heads`
+// query heads from h0 = g * 8 + hoff on, with its NT threads.
 template <bool F16, int NT>
-__device__ void zero_padded_rows(const Ws& ws, int n, int g, int hoff, int heads, int w, int nw,
+__device__ void zero_padded_rows(const Ws& ws, int n, int nu, int g, int hoff, int heads, int w, int nw,
                                  void* __restrict__ outp, float* __restrict__ lse) {
-  if (ws.hdr[0] != 0) return;
-  const int nu = ws.hdr[3];
   constexpr int kElem = F16 ? 4 : 2;
   const int row_vec = heads * kD * kElem / 16;  // 16-byte vectors of one token's rows
   const int h0 = g * kHpg + hoff;
@@ -893,7 +891,7 @@ __device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw, 
     // held in registers across the tile loop.
     int z = 0;
     asm volatile("" : "+s"(z));
-    s_qw += z;
+    s_qw = static_cast<const float*>(__builtin_assume_aligned(s_qw + z, 16));
     s_rope += z;
     float ss = 0.f;
 #pragma unroll
@@ -937,15 +935,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
                                                             float* __restrict__ lse) {
   constexpr float kBound = F16 ? 15.0f : kStaticBound;
   __shared__ uint4 smem[kStages][kTileVec];
-  __shared__ float s_qw[kD];                    // q_norm weights times the softmax scale
+  __shared__ __attribute__((aligned(16))) float s_qw[kD];  // q_norm weights times the softmax scale
   __shared__ RopeFreq s_rope[kD / 2];           // RoPE frequencies
   __shared__ int4 s_items[kMaxItemsPerGroup];
   const int g = blockIdx.x & (kG - 1);
   const int wg = blockIdx.x / kG, nwg = gridDim.x / kG;
+  // schedule header, read once at entry: query blocks, 64-row units holding
+  // padded rows (none after a device-data error)
+  const int4 hdr = *reinterpret_cast<const int4*>(ws.hdr);
+  const int nitems = hdr.z;
+  const int npad = hdr.x != 0 ? 0 : hdr.w;
   // Items of this workgroup: the snake's ranks grow with j, so they are the
   // first nj; the last, partial round holds ranks below nitems only. The
   // launch keeps nj within kMaxItemsPerGroup.
-  const int nitems = ws.hdr[2];
   const int rounds = nitems / nwg, rem = nitems - rounds * nwg;
   const int sp = snake_pos(wg, nwg);
   const int nj = min(rounds + (((rounds & 1) ? nwg - 1 - sp : sp) < rem ? 1 : 0), kMaxItemsPerGroup);
@@ -1165,7 +1167,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   }
 #undef FLINT_NEXT_SLOT
   }  // nj > 0
-  zero_padded_rows<F16, kAttnThreads>(ws, n, g, 0, kHpg, wg, nwg, outp, lse);
+  zero_padded_rows<F16, kAttnThreads>(ws, n, npad, g, 0, kHpg, wg, nwg, outp, lse);
 }
 
 // ----------------------------------------------------------------- mask helper
@@ -1312,13 +1314,17 @@ __global__ __launch_bounds__(kHalfThreads, 2) void attn_half_kernel(const uint16
                                                                      Ws ws, int n, void* __restrict__ outp,
                                                                      float* __restrict__ lse) {
   __shared__ uint4 smem[kHStages][kTileVec];
-  __shared__ float s_qw[kD];
+  __shared__ __attribute__((aligned(16))) float s_qw[kD];
   __shared__ RopeFreq s_rope[kD / 2];
   __shared__ int4 s_items[kMaxItemsHalf];
   const int g = blockIdx.x & (kG - 1);
   const int hh = (blockIdx.x >> 2) & 1;
   const int wg = blockIdx.x >> 3, nwg = gridDim.x >> 3;
-  const int nitems = ws.hdr[2];
+  // schedule header, read once at entry: query blocks, 64-row units holding
+  // padded rows (none after a device-data error)
+  const int4 hdr = *reinterpret_cast<const int4*>(ws.hdr);
+  const int nitems = hdr.z;
+  const int npad = hdr.x != 0 ? 0 : hdr.w;
   const int rounds = nitems / nwg, rem = nitems - rounds * nwg;
   const int nj = min(rounds + (((rounds & 1) ? nwg - 1 - wg : wg) < rem ? 1 : 0), kMaxItemsHalf);
   if (nj > 0) {
@@ -1447,7 +1453,7 @@ __global__ __launch_bounds__(kHalfThreads, 2) void attn_half_kernel(const uint16
   }
 #undef FLINT_NEXT_SLOT_H
   }  // nj > 0
-  zero_padded_rows<false, kHalfThreads>(ws, n, g, 4 * ((blockIdx.x >> 2) & 1), 4, wg, nwg, outp, lse);
+  zero_padded_rows<false, kHalfThreads>(ws, n, npad, g, 4 * ((blockIdx.x >> 2) & 1), 4, wg, nwg, outp, lse);
 }
 
 // Query blocks per kv head up to which the forward runs on attn_half_kernel:
