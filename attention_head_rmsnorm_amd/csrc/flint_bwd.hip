@@ -714,28 +714,12 @@ __device__ __forceinline__ bf16x8 ld_frag_tr(const uint4* x, unsigned off0, unsi
 }
 
 // Row terms lse (log2 units) and Dr of queries 8rg + 4half + [0, 4) for the
-// lanes of `half`. The step's terms arrive in LDS by a direct global->LDS
-// load, which the compiler's wait insertion cannot tell from the loads still
-// in flight for the next step (it would wait for them too), so the read is
-// written out with its own wait.
+// lanes of `half` (the step's terms, which arrive in LDS with its operands).
 __device__ __forceinline__ void read_stats4(const float* stats, int half, int rg, float* lv, float* rv) {
-  typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  f32x4_t a, b;
-  const unsigned base =
-      (unsigned)(uintptr_t)(const __attribute__((address_space(3))) float*)stats + 16u * half + 32u * rg;
-  // early clobber: a read's destination must not be the address register
-  asm volatile(
-      "ds_read_b128 %0, %2\n\t"
-      "ds_read_b128 %1, %2 offset:128\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a), "=&v"(b)
-      : "v"(base)
-      : "memory");
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    lv[j] = a[j];
-    rv[j] = b[j];
-  }
+  const float4 a = *reinterpret_cast<const float4*>(stats + 4 * half + 8 * rg);
+  const float4 b = *reinterpret_cast<const float4*>(stats + kBM + 4 * half + 8 * rg);
+  lv[0] = a.x; lv[1] = a.y; lv[2] = a.z; lv[3] = a.w;
+  rv[0] = b.x; rv[1] = b.y; rv[2] = b.z; rv[3] = b.w;
 }
 
 // One step of the key-major kernel for the wave's 32 keys, as one straight
@@ -886,6 +870,11 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const uint16_t* 
     dma4(r, lane * 4, kQtPart, dst + 2 * kQtPart);
   };
   load_step(0, 0);
+  // Everything loaded so far (V tiles, K' operands, step 0) is waited for here,
+  // where the compiler sees it: the first ring barrier would wait for it anyway,
+  // and loads still pending at the loop's entry would make the compiler wait for
+  // every load in flight (the next step's) before the LDS reads of every step.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   f32x16 dk[4], dv[4];
 #pragma unroll

@@ -305,6 +305,9 @@ __device__ __forceinline__ int block_cost(int u, int qb, int window) {
 // order in which the softmax output P^T sits in the MFMA B operand.
 __device__ __forceinline__ int vt_slot(int r) { return r ^ ((((r >> 2) ^ (r >> 3)) & 1) * 12); }
 
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt not waited on.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Workgroup barrier for the tile ring. Vector-memory operations complete in
 // issue order, so a wave whose tile loads were followed by exactly `n` more
 // vector-memory operations has that tile in LDS once at most `n` remain in
