@@ -349,6 +349,20 @@ __global__ __launch_bounds__(256) void bwd_kv_prep_kernel(const uint16_t* __rest
 
 // ----------------------------------------------------------------- Q / dO prep
 
+// RoPE on a thread's 8 channel pairs (x[i] with x[8 + i]) at position pos.
+template <bool kMixed>
+__device__ __forceinline__ void rope_rows8(int pos, const RopeFreq* fr, float* x) {
+  const float pf = (float)pos;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float c, sn;
+    rope_cos_sin<kMixed>(pos, pf, fr[i], &c, &sn);
+    const float a = x[i], bb = x[8 + i];
+    x[i] = a * c - bb * sn;
+    x[8 + i] = bb * c + a * sn;
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_q_prep_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ o,
                                                          const uint16_t* __restrict__ dout,
@@ -408,14 +422,8 @@ __global__ __launch_bounds__(256) void bwd_q_prep_kernel(const uint16_t* __restr
   }
   if (use_rope && valid) {
     const int pos = positions ? positions[t] : ell;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float c, sn;
-      rope_cos_sin(pos, ws.f.rope[8 * p + i], &c, &sn);
-      const float a = x[i], bb = x[8 + i];
-      x[i] = a * c - bb * sn;
-      x[8 + i] = bb * c + a * sn;
-    }
+    if (!rope_wave_mixed(pos)) rope_rows8<false>(pos, ws.f.rope + 8 * p, x);
+    else rope_rows8<true>(pos, ws.f.rope + 8 * p, x);
   }
   const uint4 w0 = pack8(x), w1 = pack8(x + 8);
   uint4* qf = reinterpret_cast<uint4*>(tile);
@@ -512,6 +520,23 @@ __device__ __forceinline__ void dq_tile(const uint4* st, int lane, int half, con
       }
     }
   }
+}
+
+// Adjoint of the RoPE rotation on the dQ'^T accumulators of the lane's query:
+// channels c = 32db + 8(i>>2) + 4half + (i&3) (db < 2) pair with c + 64.
+template <bool kMixed>
+__device__ __forceinline__ void rope_adjoint_dq(int pos, const RopeFreq* rope, int half, f32x16* acc) {
+  const float pf = (float)pos;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float cs, sn;
+      rope_cos_sin<kMixed>(pos, pf, rope[32 * db + 8 * (i >> 2) + 4 * half + (i & 3)], &cs, &sn);
+      const float a = acc[db][i], b = acc[db + 2][i];
+      acc[db][i] = a * cs + b * sn;
+      acc[db + 2][i] = b * cs - a * sn;
+    }
 }
 
 __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __restrict__ q,
@@ -611,16 +636,8 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __re
     for (int i = 0; i < 16; ++i) acc[db][i] *= kInvSqrtD;
   if (use_rope) {  // adjoint of the rotation: the opposite turn
     const int pos = positions ? (valid ? positions[(size_t)start + t0 + col] : 0) : t0 + col;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float cs, sn;
-        rope_cos_sin(pos, ws.f.rope[32 * db + 8 * (i >> 2) + 4 * half + (i & 3)], &cs, &sn);
-        const float a = acc[db][i], b = acc[db + 2][i];
-        acc[db][i] = a * cs + b * sn;
-        acc[db + 2][i] = b * cs - a * sn;
-      }
+    if (!rope_wave_mixed(pos)) rope_adjoint_dq<false>(pos, ws.f.rope, half, acc);
+    else rope_adjoint_dq<true>(pos, ws.f.rope, half, acc);
   }
   // RMSNorm adjoint: dq = rstd (dy w - xn mean(xn dy w)), xn = q rstd
   float ss = 0.f;
@@ -928,6 +945,21 @@ __global__ __launch_bounds__(kDkdvThreads) void bwd_dkdv_kernel(const uint16_t* 
 
 // ----------------------------------------------------------------- K/V reduce
 
+// Adjoint of the RoPE rotation on a thread's 16 channel pairs (g[i] with
+// g[16 + i]) at position pos.
+template <bool kMixed>
+__device__ __forceinline__ void rope_adjoint16(int pos, const RopeFreq* fr, float* g) {
+  const float pf = (float)pos;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float cs, sn;
+    rope_cos_sin<kMixed>(pos, pf, fr[i], &cs, &sn);
+    const float a = g[i], b = g[16 + i];
+    g[i] = a * cs + b * sn;
+    g[16 + i] = b * cs - a * sn;
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const uint16_t* __restrict__ k,
                                                             const float* __restrict__ k_norm_w,
                                                             const int* __restrict__ positions,
@@ -980,14 +1012,8 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const uint16_t* __re
   }
   if (use_rope && valid) {  // adjoint of the rotation
     const int pos = positions ? positions[t] : ell;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float cs, sn;
-      rope_cos_sin(pos, ws.f.rope[16 * p + i], &cs, &sn);
-      const float a = gk[i], b = gk[16 + i];
-      gk[i] = a * cs + b * sn;
-      gk[16 + i] = b * cs - a * sn;
-    }
+    if (!rope_wave_mixed(pos)) rope_adjoint16<false>(pos, ws.f.rope + 16 * p, gk);
+    else rope_adjoint16<true>(pos, ws.f.rope + 16 * p, gk);
   }
   float ss = 0.f;
 #pragma unroll
