@@ -522,6 +522,42 @@ __device__ __forceinline__ void dq_tile(const uint4* st, int lane, int half, con
   }
 }
 
+// Reduce-scatter over the 32 lanes of each half-wave: v[0..N) of every lane
+// in, and out in v[0..N/2) of the lane the sums of the values its partner
+// kept. The partner is lane ^ 16 (kLevel 0), or the mirror image within 16
+// lanes, within 8 lanes, lane ^ 2 and lane ^ 1 (kLevel 1 to 4); a lane whose
+// level bit is set keeps the upper half of v. After the five levels lane L of a
+// half holds in v[0], v[1] the sums of entries 2 (L & 31) and 2 (L & 31) + 1.
+template <int kLevel, int N>
+__device__ __forceinline__ void reduce_scatter_step(float* v, int lane) {
+  constexpr int kBit = 4 - kLevel;
+  const bool up = (lane >> kBit) & 1;
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const float keep = up ? v[k + N / 2] : v[k];
+    const float send = up ? v[k] : v[k + N / 2];
+    float recv;
+    if constexpr (kLevel == 0) {
+      // rows 0/1 and 2/3 trade places: even rows find the odd row's value in
+      // the second result, odd rows the even row's in the first
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(send), __float_as_uint(send), false, false);
+      recv = __uint_as_float(up ? r[0] : r[1]);
+    } else {
+      constexpr int kCtrl = kLevel == 1 ? 0x140 : kLevel == 2 ? 0x141 : kLevel == 3 ? 0x4E : 0xB1;
+      recv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), kCtrl, 0xF, 0xF, false));
+    }
+    v[k] = keep + recv;
+  }
+}
+
+__device__ __forceinline__ void reduce_scatter32(float* v, int lane) {
+  reduce_scatter_step<0, 64>(v, lane);
+  reduce_scatter_step<1, 32>(v, lane);
+  reduce_scatter_step<2, 16>(v, lane);
+  reduce_scatter_step<3, 8>(v, lane);
+  reduce_scatter_step<4, 4>(v, lane);
+}
+
 // Adjoint of the RoPE rotation on the dQ'^T accumulators of the lane's query:
 // channels c = 32db + 8(i>>2) + 4half + (i&3) (db < 2) pair with c + 64.
 template <bool kMixed>
@@ -673,27 +709,30 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __re
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, pk),
                                             dqr, col * (kH * kD * 2) + (32 * db + 8 * rg + 4 * half) * 2, 0, 0);
     }
-  // q-norm-weight terms dy * xn, summed over the workgroup's 32 rows x 8 heads
-  __syncthreads();  // every wave is done with the tile ring
-  float* red = reinterpret_cast<float*>(&smem[0][0]);  // [8 waves][32 cols][128]
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
-      *reinterpret_cast<float4*>(red + (wave * kBM + col) * kD + 32 * db + 8 * rg + 4 * half) =
-          make_float4(acc[db][4 * rg] * xq[db][4 * rg], acc[db][4 * rg + 1] * xq[db][4 * rg + 1],
-                      acc[db][4 * rg + 2] * xq[db][4 * rg + 2], acc[db][4 * rg + 3] * xq[db][4 * rg + 3]);
-  __syncthreads();
+  // q-norm-weight terms dy * xn: each wave sums its 32 rows per channel across
+  // its lanes (a reduce-scatter on the VALU), then the 8 waves' sums are added
+  // in wave order through a ring stage that no wave reads any more (the last
+  // tile uses stage (ntiles - 1) % 3, and no loads are pending).
   {
-    const int c = tid & (kD - 1), part = tid >> 7;  // 4 parts of 8 columns
-    float sum = 0.f;
-    for (int w = 0; w < kHpg; ++w)
-      for (int cc = 8 * part; cc < 8 * part + 8; ++cc) sum += red[(w * kBM + cc) * kD + c];
-    float* sum4 = red + kHpg * kBM * kD;
-    sum4[part * kD + c] = sum;
+    float v[64];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[16 * db + i] = acc[db][i] * xq[db][i];
+    reduce_scatter32(v, lane);
+    float* wsum = reinterpret_cast<float*>(smem[ntiles % kBwdStages]);  // [8 waves][128]
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int vi = 2 * col + e2;  // entry 16db + 4rg + j: channel 32db + 8rg + 4half + j
+      wsum[wave * kD + 32 * (vi >> 4) + 8 * ((vi >> 2) & 3) + 4 * half + (vi & 3)] = v[e2];
+    }
     __syncthreads();
-    if (part == 0)
-      ws.wq[(size_t)c * (ws.nqmax * kG) + bid] = (sum4[c] + sum4[kD + c]) + (sum4[2 * kD + c] + sum4[3 * kD + c]);
+    if (tid < kD) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kHpg; ++w) sum += wsum[w * kD + tid];
+      ws.wq[(size_t)tid * (ws.nqmax * kG) + bid] = sum;
+    }
   }
 }
 
