@@ -302,9 +302,7 @@ __device__ __forceinline__ void rope16(float* x, int pos, const RopeFreq* f) {
   for (int i = 0; i < 16; ++i) {
     float c, s;
     rope_cos_sin<kMixed>(pos, pf, f[i], &c, &s);
-    const float a = x[i], b = x[16 + i];
-    x[i] = a * c - b * s;
-    x[16 + i] = b * c + a * s;
+    rope_turn(x[i], x[16 + i], c, s);
   }
 }
 
@@ -848,9 +846,9 @@ __device__ __forceinline__ void q_scale_rope(const QRaw& qraw, const float* s_qw
         const int c = 16 * kk + 8 * half + jj;
         float cs, sn;
         rope_cos_sin<kMixed>(qraw.pos, pf, s_rope[c], &cs, &sn);
-        const float x = a[jj] * (rstd * s_qw[c]), y = b[jj] * (rstd * s_qw[c + 64]);
-        a[jj] = x * cs - y * sn;
-        b[jj] = y * cs + x * sn;
+        a[jj] *= rstd * s_qw[c];
+        b[jj] *= rstd * s_qw[c + 64];
+        rope_turn(a[jj], b[jj], cs, sn);
       }
       const uint4 wa = pack8(a), wb = pack8(b);
       n2 = sumsq8_dot(wb, sumsq8_dot(wa, n2));

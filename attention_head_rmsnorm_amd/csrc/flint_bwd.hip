@@ -294,9 +294,7 @@ __global__ __launch_bounds__(256) void bwd_kv_prep_kernel(const uint16_t* __rest
     for (int i = 0; i < 16; ++i) {
       float c, s;
       rope_cos_sin(pos, ws.f.rope[16 * p + i], &c, &s);
-      const float a = x[i], bb = x[16 + i];
-      x[i] = a * c - bb * s;
-      x[16 + i] = bb * c + a * s;
+      rope_turn(x[i], x[16 + i], c, s);
     }
   }
   {
@@ -349,20 +347,39 @@ __global__ __launch_bounds__(256) void bwd_kv_prep_kernel(const uint16_t* __rest
 
 // ----------------------------------------------------------------- Q / dO prep
 
-// RoPE on a thread's 8 channel pairs (x[i] with x[8 + i]) at position pos.
+// cos and sin of the RoPE angles of a thread's 8 channel pairs (8p + i) at
+// position pos.
 template <bool kMixed>
-__device__ __forceinline__ void rope_rows8(int pos, const RopeFreq* fr, float* x) {
+__device__ __forceinline__ void rope_table8(int pos, const RopeFreq* fr, float* cs, float* sn) {
   const float pf = (float)pos;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float c, sn;
-    rope_cos_sin<kMixed>(pos, pf, fr[i], &c, &sn);
-    const float a = x[i], bb = x[8 + i];
-    x[i] = a * c - bb * sn;
-    x[8 + i] = bb * c + a * sn;
-  }
+  for (int i = 0; i < 8; ++i) rope_cos_sin<kMixed>(pos, pf, fr[i], &cs[i], &sn[i]);
 }
 
+// DPP moves: row_shl:n (0x100 + n) gives lane L the value of lane L + n within
+// its 16-lane row; the quad permutation [1,0,3,2] (0xB1) the value of lane ^ 1.
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ uint4 dpp_u4(const uint4& x) {
+  return make_uint4((unsigned)__builtin_amdgcn_update_dpp(0, (int)x.x, kCtrl, 0xF, 0xF, false),
+                    (unsigned)__builtin_amdgcn_update_dpp(0, (int)x.y, kCtrl, 0xF, 0xF, false),
+                    (unsigned)__builtin_amdgcn_update_dpp(0, (int)x.z, kCtrl, 0xF, 0xF, false),
+                    (unsigned)__builtin_amdgcn_update_dpp(0, (int)x.w, kCtrl, 0xF, 0xF, false));
+}
+
+// Per (32-query block, kv head): the block's rows of the kv head's 8 query
+// heads in turn. Thread (row r, part p) holds channels [8p, 8p+8) (16-byte
+// unit p of the row) and their RoPE partners +64 (unit 8 + p). The RoPE angles
+// and the norm weights depend on the row and the channels only, so they are
+// formed once for the 8 heads. Q' is formed with the attention kernel's own
+// operations in its order, so its bits are the forward's: the sum of squares
+// of each half-row (units 2kk + half, kk = 0..7, by v_dot2 in turn) is formed
+// by thread p = half from units gathered from its 8-thread group, the two
+// halves are added, then the norm weight times the softmax scale and the RoPE
+// turn.
 __global__ __launch_bounds__(256) void bwd_q_prep_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ o,
                                                          const uint16_t* __restrict__ dout,
@@ -371,82 +388,104 @@ __global__ __launch_bounds__(256) void bwd_q_prep_kernel(const uint16_t* __restr
                                                          const float* __restrict__ sink,
                                                          const int* __restrict__ positions,
                                                          float eps, int use_rope, BwdWs ws) {
-  __shared__ float red[4];
-  const int qg = blockIdx.x, h = blockIdx.y;
+  __shared__ float red[4][kHpg];
+  const int qg = blockIdx.x, g = blockIdx.y;
   if (qg >= ws.f.hdr[2]) return;
   const int s = find_seq(ws.f.qbase, ws.n, qg);
   const int qb = qg - ws.f.qbase[s];
   const int4 meta = ws.f.seq[s];
   const int start = meta.x, u = meta.z;
-  const int tid = threadIdx.x, r = tid >> 3, p = tid & 7;
+  const int tid = threadIdx.x, lane = tid & 63, r = tid >> 3, p = tid & 7;
   const int ell = qb * kBM + r;
   const bool valid = ell < u;
   const size_t t = (size_t)start + ell;
-  char* tile = ws.qt + ((size_t)qg * kH + h) * kQtBytes;
 
-  // this thread: channels [8p, 8p+8) and their RoPE partners +64
-  float x[16], dy[16], y[16];
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-  const size_t row = (t * kH + h) * kD;
-  const uint4 qa = valid ? *reinterpret_cast<const uint4*>(q + row + 8 * p) : z4;
-  const uint4 qc = valid ? *reinterpret_cast<const uint4*>(q + row + 64 + 8 * p) : z4;
-  const uint4 da = valid ? *reinterpret_cast<const uint4*>(dout + row + 8 * p) : z4;
-  const uint4 dc = valid ? *reinterpret_cast<const uint4*>(dout + row + 64 + 8 * p) : z4;
-  const uint4 oa = valid ? *reinterpret_cast<const uint4*>(o + row + 8 * p) : z4;
-  const uint4 oc = valid ? *reinterpret_cast<const uint4*>(o + row + 64 + 8 * p) : z4;
-  unpack8(qa, x);
-  unpack8(qc, x + 8);
-  unpack8(da, dy);
-  unpack8(dc, dy + 8);
-  unpack8(oa, y);
-  unpack8(oc, y + 8);
-  float ss = 0.f, dr = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    ss += x[i] * x[i];
-    dr += dy[i] * y[i];
-  }
-#pragma unroll
-  for (int off = 1; off < 8; off <<= 1) {
-    ss += __shfl_xor(ss, off);
-    dr += __shfl_xor(dr, off);
-  }
-  const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
-  // the norm weight times the softmax scale in log2 units, then RoPE, as the
-  // forward forms its query rows, so the logits recomputed here are the
-  // forward's own
+  float wlo[8], whi[8];  // q_norm weights times the softmax scale, as the forward holds them
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    x[i] *= rstd * (q_norm_w[8 * p + i] * kQScale);
-    x[8 + i] *= rstd * (q_norm_w[64 + 8 * p + i] * kQScale);
+    wlo[i] = q_norm_w[8 * p + i] * kQScale;
+    whi[i] = q_norm_w[64 + 8 * p + i] * kQScale;
   }
-  if (use_rope && valid) {
+  float cs[8], sn[8];
+  const bool rot = use_rope && valid;
+  if (rot) {
     const int pos = positions ? positions[t] : ell;
-    if (!rope_wave_mixed(pos)) rope_rows8<false>(pos, ws.f.rope + 8 * p, x);
-    else rope_rows8<true>(pos, ws.f.rope + 8 * p, x);
+    if (!rope_wave_mixed(pos)) rope_table8<false>(pos, ws.f.rope + 8 * p, cs, sn);
+    else rope_table8<true>(pos, ws.f.rope + 8 * p, cs, sn);
   }
-  const uint4 w0 = pack8(x), w1 = pack8(x + 8);
-  uint4* qf = reinterpret_cast<uint4*>(tile);
   // channels 8p.. are k-step p>>1, half p&1; channels 64+8p.. are k-step
   // 4+(p>>1); swizzled operand order (unit 64kk + 32half + (r ^ 8half))
   const int su = 32 * (p & 1) + (r ^ (8 * (p & 1)));
-  qf[64 * (p >> 1) + su] = w0;
-  qf[64 * (4 + (p >> 1)) + su] = w1;
-  // row terms and the block's share of the sink adjoint
-  float* stats = reinterpret_cast<float*>(tile + kQtPart);
-  const float l2 = valid ? lse[t * kH + h] * kLog2e : INFINITY;
-  float share = 0.f;
-  if (p == 0) {
-    stats[r] = l2;
-    stats[kBM + r] = valid ? dr : 0.f;
-    const float sk2 = sink[h] * kLog2e;
-    share = valid ? __builtin_amdgcn_exp2f(sk2 - l2) * dr : 0.f;
-  }
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+
+#pragma unroll 1
+  for (int hl = 0; hl < kHpg; ++hl) {
+    const int h = g * kHpg + hl;
+    char* tile = ws.qt + ((size_t)qg * kH + h) * kQtBytes;
+    const size_t row = (t * kH + h) * kD;
+    const uint4 qa = valid ? *reinterpret_cast<const uint4*>(q + row + 8 * p) : z4;
+    const uint4 qc = valid ? *reinterpret_cast<const uint4*>(q + row + 64 + 8 * p) : z4;
+    const uint4 da = valid ? *reinterpret_cast<const uint4*>(dout + row + 8 * p) : z4;
+    const uint4 dc = valid ? *reinterpret_cast<const uint4*>(dout + row + 64 + 8 * p) : z4;
+    const uint4 oa = valid ? *reinterpret_cast<const uint4*>(o + row + 8 * p) : z4;
+    const uint4 oc = valid ? *reinterpret_cast<const uint4*>(o + row + 64 + 8 * p) : z4;
+    const float lv = valid ? lse[t * kH + h] : 0.f;
+    // sum of squares of the half-row of thread p = half (p < 2): units
+    // p, p + 2, p + 4, p + 6 (its own and its group's qa) then the same of qc
+    float ss;
+    {
+      const uint4 a2 = dpp_u4<0x102>(qa), a4 = dpp_u4<0x104>(qa), a6 = dpp_u4<0x106>(qa);
+      const uint4 c2 = dpp_u4<0x102>(qc), c4 = dpp_u4<0x104>(qc), c6 = dpp_u4<0x106>(qc);
+      float sh = sumsq8_dot(qa, 0.f);
+      sh = sumsq8_dot(a2, sh);
+      sh = sumsq8_dot(a4, sh);
+      sh = sumsq8_dot(a6, sh);
+      sh = sumsq8_dot(qc, sh);
+      sh = sumsq8_dot(c2, sh);
+      sh = sumsq8_dot(c4, sh);
+      sh = sumsq8_dot(c6, sh);
+      ss = sh + dpp_xor1(sh);   // thread 0 of the group: half 0's sum plus half 1's
+      ss = __shfl(ss, lane & ~7);         // to the group's 8 threads
+    }
+    float x[16], dy[16], y[16];
+    unpack8(qa, x);
+    unpack8(qc, x + 8);
+    unpack8(da, dy);
+    unpack8(dc, dy + 8);
+    unpack8(oa, y);
+    unpack8(oc, y + 8);
+    float dr = 0.f;
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) share += __shfl_xor(share, off);
-  if ((tid & 63) == 0) red[tid >> 6] = share;
+    for (int i = 0; i < 16; ++i) dr += dy[i] * y[i];
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) dr += __shfl_xor(dr, off);
+    const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] *= rstd * wlo[i];
+      x[8 + i] *= rstd * whi[i];
+      if (rot) rope_turn(x[i], x[8 + i], cs[i], sn[i]);
+    }
+    uint4* qf = reinterpret_cast<uint4*>(tile);
+    qf[64 * (p >> 1) + su] = pack8(x);
+    qf[64 * (4 + (p >> 1)) + su] = pack8(x + 8);
+    // row terms and the block's share of the sink adjoint
+    float* stats = reinterpret_cast<float*>(tile + kQtPart);
+    const float l2 = valid ? lv * kLog2e : INFINITY;
+    float share = 0.f;
+    if (p == 0) {
+      stats[r] = l2;
+      stats[kBM + r] = valid ? dr : 0.f;
+      const float sk2 = sink[h] * kLog2e;
+      share = valid ? __builtin_amdgcn_exp2f(sk2 - l2) * dr : 0.f;
+    }
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) share += __shfl_xor(share, off);
+    if (lane == 0) red[tid >> 6][hl] = share;
+  }
   __syncthreads();
-  if (tid == 0) ws.sinkpart[(size_t)h * ws.nqmax + qg] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid < kHpg)
+    ws.sinkpart[(size_t)(g * kHpg + tid) * ws.nqmax + qg] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
 }
 
 // ----------------------------------------------------------------- dQ
@@ -1221,7 +1260,7 @@ extern "C" int flint_attn_bwd(const void* q, const void* k, const void* v, const
     bwd_schedule_kernel<<<1, 1024, 0, st>>>(window, ws);
     bwd_kv_prep_kernel<<<dim3((unsigned)L.f.ntmax, kG), 256, 0, st>>>(
         kh, vh, k_norm_w, pos, eps, rope, ws, static_cast<uint16_t*>(dq));
-    bwd_q_prep_kernel<<<dim3((unsigned)L.f.nqmax, kH), 256, 0, st>>>(
+    bwd_q_prep_kernel<<<dim3((unsigned)L.f.nqmax, kG), 256, 0, st>>>(
         qh, static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, q_norm_w,
         sink, pos, eps, rope, ws);
     bwd_dq_kernel<<<(unsigned)(L.f.nqmax * kG), kDqThreads, 0, st>>>(

@@ -177,6 +177,16 @@ __device__ __forceinline__ void rope_cos_sin(int pos, float pf, const RopeFreq& 
   *c = __builtin_amdgcn_cosf(rev);
 }
 
+// The RoPE turn of a channel pair (x: channel c, y: channel c + 64) by the
+// angle's cos and sin, with its products and roundings spelled out, so that
+// every kernel that forms q' or k' forms the same bits.
+__device__ __forceinline__ void rope_turn(float& x, float& y, float cs, float sn) {
+  const float a = fmaf(x, cs, -(y * sn));
+  const float b = fmaf(x, sn, y * cs);
+  x = a;
+  y = b;
+}
+
 __device__ __forceinline__ bool rope_wave_mixed(int pos) {
   return __builtin_amdgcn_ballot_w64(!rope_pos_fast(pos)) != 0;
 }
