@@ -145,7 +145,7 @@ __device__ __forceinline__ bool rope_pos_fast(int pos) {
 
 // Fractional revolutions of pos * r / 2^64, exactly up to the float rounding
 // of the top 32 bits: pos * r mod 2^64 taken as a signed value in [-1/2, 1/2)
-// (four 32-bit integer multiplies).
+// (three 32-bit integer multiplies, quarter rate).
 __device__ __forceinline__ float rope_rev_exact(int pos, unsigned long long r) {
   const unsigned long long prod = (unsigned long long)(long long)pos * r;
   return (float)(int)(unsigned)(prod >> 32) * 2.3283064365386963e-10f;  // 2^-32
