@@ -15,19 +15,18 @@
 // Kernels, in order on the caller's stream:
 //   schedule_kernel (forward)  sequence table, key tiles, query blocks.
 //   bwd_schedule_kernel   one workgroup: cuts the query range seen by each
-//                         128-key block at fixed chunk boundaries and orders
+//                         256-key block at fixed chunk boundaries and orders
 //                         the chunks by query position, so the workgroups on
 //                         one L2 share the query tiles they stream.
 //   bwd_kv_prep_kernel    per (64-key tile, kv head): K' = RoPE(RMSNorm(k)) in
 //                         bf16 as a K' operand tile, V as a V operand tile, and
 //                         K'^T in the key-slot order of the dQ product; zero dq
 //                         rows of padded tokens.
-//   bwd_q_prep_kernel     per (32-query block, head): Q' (with the softmax
-//                         scale in log2 units, rounded as the forward rounds
-//                         it) and dO as operand tiles and transposed
-//                         (query-slot order), the row
-//                         terms lse (log2 units) and Dr, the block's share of
-//                         the sink adjoint.
+//   bwd_q_prep_kernel     per (32-query block, kv head), its 8 query heads in
+//                         turn: Q' (with the softmax scale in log2 units, the
+//                         bits the forward forms) as a swizzled operand tile,
+//                         the row terms lse (log2 units) and Dr, the block's
+//                         share of the sink adjoint.
 //   bwd_dq_kernel         query-major: per (query block, the 8 heads of a kv head),
 //                         over the key tiles in the window: S^T = K'Q'^T,
 //                         dP^T = V dO^T, dS^T, dQ'^T += K'^T dS^T; then RoPE and
