@@ -356,9 +356,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const int* __restrict
   }
 }
 
-// Clears the device-data error bits at the start of a decode call (a kernel,
-// not a memset, so the call can be captured in a graph).
-
 }  // namespace flint
 
 // ----------------------------------------------------------------- decode host side
