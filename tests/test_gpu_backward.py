@@ -20,6 +20,8 @@ logit); the denominator adds the bf16 rounding of the weights it sums,
 
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -225,3 +227,122 @@ def test_backward_full_size_sampled():
     b = float(torch.dot(wl.k_norm_w, dkw.cpu()))
     assert abs(a - b) <= 2e-2 * max(abs(a), abs(b)), f"<w_q,dw_q> {a} vs <w_k,dw_k> {b}"
     _log(f"[bwd] full size: {st}, <w,dw> {a:.4g} / {b:.4g}")
+
+
+def _sub_oracle(wl, layer, dout, s, a, b, rows, keys):
+    """The oracle on tokens [a, b) of sequence s, taken as a sequence of its
+    own with their positions in s. Returns the oracle's dict for the local
+    row and key indices (rows / keys minus a).
+
+    In a sliding layer a row t depends only on keys t - W + 1 .. t and key j
+    only on the queries j .. j + W - 1 and their key sets, so a row with
+    t - W + 1 >= a (or a = 0) and a key with j - W + 1 >= a (or a = 0) whose
+    later valid queries all lie below b get exactly their values in the whole
+    sequence; a whole document (a = 0, b = its length) does so in any layer.
+    """
+    cu = i64(wl.cu_seqlens)
+    g0 = int(cu[s])
+    L = int(cu[s + 1]) - g0
+    u = L if wl.seqused is None else int(i64(wl.seqused)[s])
+    pos = (np.arange(L, dtype=np.int64) if wl.positions is None
+           else i64(wl.positions)[g0:g0 + L])
+    sl = slice(g0 + a, g0 + b)
+    return flint_attention_backward(
+        f64(wl.q[sl]), f64(wl.k[sl]), f64(wl.v[sl]), f64(wl.q_norm_w), f64(wl.k_norm_w),
+        f64(wl.sinks), np.array([0, b - a], np.int64), f64(dout[sl]),
+        seqused=np.array([max(0, min(u, b) - a)], np.int64), positions=pos[a:b],
+        window=layer.window, use_rope=layer.use_rope, theta=layer.theta, eps=layer.eps,
+        rows=np.asarray(rows, np.int64) - a, keys=np.asarray(keys, np.int64) - a)
+
+
+def _check_pieces(wl, layer, name, pieces):
+    """Runs the layer's forward and backward on the whole workload (the
+    benchmark's launch configuration) and grades dq rows, dk / dv keys and
+    the row normalizer of each piece (s, a, b, rows, keys) against the
+    oracle on that piece alone. Padded tokens must get exact zeros."""
+    dout = draw_dout(wl.seed, wl.total_tokens)
+    _log(f"[bwd] {name} {layer.name}: T={wl.total_tokens}, {len(pieces)} pieces")
+    out, lse, (dq, dk, dv, dqw, dkw, dsk) = run_train(wl, layer, dout)
+    cu = i64(wl.cu_seqlens)
+    for s, a, b, rows, keys in pieces:
+        L = int(cu[s + 1] - cu[s])
+        u = L if wl.seqused is None else int(i64(wl.seqused)[s])
+        rows = np.asarray(sorted(set(rows)), np.int64)
+        keys = np.asarray(sorted(set(keys)), np.int64)
+        assert rows.min() >= a and rows.max() < b and keys.min() >= a and keys.max() < b
+        what = f"{name} {layer.name} seq {s} [{a}, {b})"
+        _log(f"[bwd] {what}: {len(rows)} rows, {len(keys)} keys")
+        ref = _sub_oracle(wl, layer, dout, s, a, b, rows[rows < u], keys[keys < u])
+        gr = torch.as_tensor(int(cu[s]) + rows, device=dq.device)
+        gk = torch.as_tensor(int(cu[s]) + keys, device=dq.device)
+        vr, vk = rows < u, keys < u
+        got_dq, got_dk, got_dv = to_np(dq[gr]), to_np(dk[gk]), to_np(dv[gk])
+        assert np.all(got_dq[~vr] == 0.0), f"{what}: padded dq rows are not zeros"
+        assert np.all(got_dk[~vk] == 0.0) and np.all(got_dv[~vk] == 0.0), \
+            f"{what}: padded dk / dv keys are not zeros"
+        st = {"dq": _grade_tensor(got_dq[vr], ref["dq"], np.ones(vr.sum(), bool), f"{what} dq"),
+              "dk": _grade_tensor(got_dk[vk], ref["dk"], np.ones(vk.sum(), bool), f"{what} dk"),
+              "dv": _grade_tensor(got_dv[vk], ref["dv"], np.ones(vk.sum(), bool), f"{what} dv")}
+        lg = lse[gr].float().cpu().numpy().astype(np.float64)
+        lr = ref["lse"][rows[vr] - a]
+        assert np.all(np.isneginf(lg[~vr])), f"{what}: padded lse is not -inf"
+        lerr = float(np.max(np.abs(lg[vr] - lr) / (LSE_ABS + LSE_REL * np.abs(lr))))
+        assert lerr <= 1.0, f"{what}: lse error {lerr:.3f} of its bound"
+        _log(f"[bwd] {what}: " + ", ".join(f"{k} {v[0]:.2e}/{v[1]:.2e}" for k, v in st.items())
+             + f", lse {lerr:.2f} of bound")
+    a = float(torch.dot(wl.q_norm_w, dqw.cpu()))
+    b = float(torch.dot(wl.k_norm_w, dkw.cpu()))
+    assert abs(a - b) <= 2e-2 * max(abs(a), abs(b)), f"<w_q,dw_q> {a} vs <w_k,dw_k> {b}"
+
+
+def _pick(lo, hi, n, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    pick = set(range(lo, min(hi, lo + 6))) | set(range(max(lo, hi - 6), hi))
+    pick |= {e for e in extra if lo <= e < hi}
+    pick |= set(rng.integers(lo, hi, size=n).tolist())
+    return sorted(pick)
+
+
+def test_backward_sliding_full_size_pieces():
+    """8 x 8192 tokens with trailing padding, sliding window 513 with RoPE (the
+    backward benchmark's sliding workload), graded on three pieces: a
+    sequence's first 1,600 tokens, an interior stretch, and the end of the
+    most padded sequence with its padding."""
+    wl = make_workload("c3")
+    layer = wl.layers[0]
+    W = layer.window
+    u6 = int(i64(wl.seqused)[6])
+    a6 = u6 - 1600
+    pieces = [
+        (0, 0, 1600, _pick(0, 1600, 40, 21, (63, 64, 511, 512, 513)),
+         _pick(0, 1600 - W, 40, 22, (63, 64, 511, 512))),
+        (3, 2900, 4700, _pick(2900 + W - 1, 4700, 40, 23, (4095, 4096)),
+         _pick(2900 + W - 1, 4700 - W, 40, 24, (4095, 4096))),
+        (6, a6, 8192, _pick(a6 + W - 1, 8192, 40, 25, (u6 - 1, u6, 8191)),
+         _pick(a6 + W - 1, 8192, 40, 26, (u6 - 1, u6, 8191))),
+    ]
+    _check_pieces(wl, layer, "c3", pieces)
+
+
+@functools.lru_cache(maxsize=1)
+def _c4():
+    return make_workload("c4")
+
+
+@pytest.mark.parametrize("li", [0, 1], ids=["sliding", "full"])
+def test_backward_thd_documents_full_size(li):
+    """16 THD documents of 135 to 7,525 tokens (both layer kinds): three short
+    documents graded whole, and for the sliding layer an interior stretch of
+    the longest one."""
+    wl = _c4()
+    layer = wl.layers[li]
+    lens = np.diff(i64(wl.cu_seqlens))
+    pieces = []
+    for s in (1, 2, 13):
+        L = int(lens[s])
+        pieces.append((s, 0, L, _pick(0, L, 24, 30 + s), _pick(0, L, 24, 50 + s)))
+    if layer.window:
+        W = layer.window
+        pieces.append((10, 3000, 4800, _pick(3000 + W - 1, 4800, 32, 71),
+                       _pick(3000 + W - 1, 4800 - W, 32, 72)))
+    _check_pieces(wl, layer, "c4", pieces)
