@@ -753,8 +753,48 @@ __device__ void zero_padded_rows(const Ws& ws, int n, int nu, int g, int hoff, i
 
 // One work item = 32 query tokens x the 8 query heads of one kv head. A
 // workgroup keeps the list of its items in LDS as {sequence start, valid
-// length, first query, first tile of the sequence}; the rest follows.
-constexpr int kMaxItemsPerGroup = 1024;
+// length, first query, first tile of the sequence}; the rest follows. The
+// list's size is what the LDS left beside the tile ring and the RoPE table
+// holds.
+constexpr int kMaxItemsPerGroup = 896;
+
+// RoPE cos / sin of an item's 32 query rows, formed once per workgroup for
+// its 8 heads (every head of a row turns by the same angles). Lane (col,
+// half) of the query prologue turns channel pairs c = 16kk + 8half + jj; its
+// logical chunk i = 4kk + (jj >> 1) holds {cos, sin} of pairs c0 and c0 + 1,
+// c0 = 16 (i >> 2) + 8 half + 2 (i & 3), and sits at float4 index
+// (2 col + half) * 16 + (i ^ (col & 15)), so 16 consecutive lanes reading
+// their chunk i meet 16 distinct 16-byte bank groups.
+constexpr int kCsChunks = kBM * 2 * 16;  // 1024 float4 = 16 KiB
+
+// Thread tid (of 512) forms logical chunks 2m and 2m + 1 (m = tid & 7), i.e.
+// pairs 16 (m >> 1) + 8 half + 4 (m & 1) + 0..3, of row tid >> 4, half
+// (tid >> 3) & 1, at position pos, with the function every RoPE step uses
+// (kMixed when a lane of the wave needs the exact angle reduction; a lane's
+// values do not depend on the choice).
+template <bool kMixed>
+__device__ __forceinline__ void cs_table_part(float4* s_cs, int tid, int pos, const RopeFreq* s_rope) {
+  const int col = tid >> 4, half = (tid >> 3) & 1, m = tid & 7;
+  const int c0 = 16 * (m >> 1) + 8 * half + 4 * (m & 1);
+  const float pf = (float)pos;
+  float cs[4], sn[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rope_cos_sin<kMixed>(pos, pf, s_rope[c0 + i], &cs[i], &sn[i]);
+  const int base = (2 * col + half) * 16, sw = col & 15;
+  s_cs[base + ((2 * m) ^ sw)] = make_float4(cs[0], sn[0], cs[1], sn[1]);
+  s_cs[base + ((2 * m + 1) ^ sw)] = make_float4(cs[2], sn[2], cs[3], sn[3]);
+}
+
+// s_waitcnt lgkmcnt(0) and a workgroup barrier: LDS writes made before it are
+// seen by every wave after it; vector-memory loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void cs_table(float4* s_cs, int tid, int pos, const RopeFreq* s_rope) {
+  if (rope_wave_mixed(pos)) cs_table_part<true>(s_cs, tid, pos, s_rope);
+  else cs_table_part<false>(s_cs, tid, pos, s_rope);
+}
 
 struct Item {
   int start;    // first token of the sequence
@@ -826,14 +866,33 @@ __device__ __forceinline__ void load_q(const uint16_t* q, const int* positions, 
   }
 }
 
+// The RoPE position of row `row` of item `it` for the cos / sin table: the
+// same value load_q gives the query lane of that row (rows at or past the
+// valid length read 0 when positions are given). One vector-memory operation
+// when positions are read (none otherwise); an absent item (`valid` false)
+// reads nothing in range.
+__device__ __forceinline__ int table_pos_load(const int* positions, bool qpos, const Item& it, bool valid,
+                                              int row) {
+  if (!qpos) return it.t0 + row;
+  const int rows = valid ? min(it.u - it.t0, kBM) : 0;
+  const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int*>(positions + (valid ? it.start + it.t0 : 0)), 0, rows * 4, kBufferWord3);
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(pr, row * 4, 0, 0);
+}
+
 // Norm weight, RoPE and one bf16 rounding of a wave's query rows, into the
 // MFMA B-operand layout of Q^T; n2 accumulates the lane's sum of squares of
 // the rounded values. s_qw holds the query norm weights times the softmax
 // scale; channel c pairs with c + 64 under RoPE.
-template <bool kRope, bool kMixed>
+// kTab: the cos / sin come from the workgroup's table s_cs (lane col =
+// lane & 31) instead of being formed here.
+template <bool kRope, bool kMixed, bool kTab = false>
 __device__ __forceinline__ void q_scale_rope(const QRaw& qraw, const float* s_qw, const RopeFreq* s_rope,
-                                             float rstd, int half, bf16x8* qf, float& n2) {
+                                             float rstd, int half, bf16x8* qf, float& n2,
+                                             const float4* s_cs = nullptr) {
   const float pf = (float)qraw.pos;
+  const int tcol = __lane_id() & 31;
+  const int tbase = (2 * tcol + half) * 16;
   if constexpr (kRope) {
     // channels 16kk + 8half + j pair with 16(kk+4) + 8half + j
 #pragma unroll
@@ -845,7 +904,13 @@ __device__ __forceinline__ void q_scale_rope(const QRaw& qraw, const float* s_qw
       for (int jj = 0; jj < 8; ++jj) {
         const int c = 16 * kk + 8 * half + jj;
         float cs, sn;
-        rope_cos_sin<kMixed>(qraw.pos, pf, s_rope[c], &cs, &sn);
+        if constexpr (kTab) {
+          const float4 t4 = s_cs[tbase + ((4 * kk + (jj >> 1)) ^ (tcol & 15))];
+          cs = (jj & 1) ? t4.z : t4.x;
+          sn = (jj & 1) ? t4.w : t4.y;
+        } else {
+          rope_cos_sin<kMixed>(qraw.pos, pf, s_rope[c], &cs, &sn);
+        }
         a[jj] *= rstd * s_qw[c];
         b[jj] *= rstd * s_qw[c + 64];
         rope_turn(a[jj], b[jj], cs, sn);
@@ -872,10 +937,11 @@ __device__ __forceinline__ void q_scale_rope(const QRaw& qraw, const float* s_qw
 // Query prologue: RMSNorm, RoPE, softmax scale in log2 units and one bf16
 // rounding, in the MFMA B-operand layout of Q^T; qmax = max |q'| over the
 // wave's 32 queries. With F16 the rows arrive prepared (q16_prep_kernel) and
-// only qmax is formed.
-template <bool F16>
+// only qmax is formed. kTab: the RoPE cos / sin come from the table s_cs.
+template <bool F16, bool kTab = false>
 __device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw, const RopeFreq* s_rope,
-                                           bool rope, float eps, int half, bf16x8* qf, float& qmax) {
+                                           bool rope, float eps, int half, bf16x8* qf, float& qmax,
+                                           const float4* s_cs = nullptr) {
   float n2 = 0.f;
   if constexpr (F16) {
 #pragma unroll
@@ -897,6 +963,7 @@ __device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw, 
     ss += __shfl_xor(ss, 32);
     const float rstd = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
     if (!rope) q_scale_rope<false, false>(qraw, s_qw, s_rope, rstd, half, qf, n2);
+    else if (kTab) q_scale_rope<true, false, true>(qraw, s_qw, s_rope, rstd, half, qf, n2, s_cs);
     else if (!rope_wave_mixed(qraw.pos)) q_scale_rope<true, false>(qraw, s_qw, s_rope, rstd, half, qf, n2);
     else q_scale_rope<true, true>(qraw, s_qw, s_rope, rstd, half, qf, n2);
   }
@@ -922,7 +989,13 @@ __device__ __forceinline__ void q_prologue(const QRaw& qraw, const float* s_qw, 
 // holding the fp16-rounded output (the kernel-output boundary restored to
 // FP32). The unshifted path then needs every weight below fp16's largest
 // finite value, so its bound is 15 (log2 units) instead of kStaticBound.
-template <bool F16>
+//
+// kTab (bf16 RoPE layers): the query prologue takes its RoPE cos / sin from
+// the table s_cs. The table of item j + 1 is formed at item j's first tile
+// (after its ring barrier, so every wave has read item j's table) from
+// positions loaded with item j's query rows, and read at item j's end (after
+// its second barrier, or an extra one when the item has one tile).
+template <bool F16, bool kTab = false>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __restrict__ q,
                                                             const float* __restrict__ q_norm_w,
                                                             const float* __restrict__ k_norm_w,
@@ -936,6 +1009,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   __shared__ __attribute__((aligned(16))) float s_qw[kD];  // q_norm weights times the softmax scale
   __shared__ RopeFreq s_rope[kD / 2];           // RoPE frequencies
   __shared__ int4 s_items[kMaxItemsPerGroup];
+  __shared__ float4 s_cs[kCsChunks];  // RoPE cos / sin of the next item's query rows
   const int g = blockIdx.x & (kG - 1);
   const int wg = blockIdx.x / kG, nwg = gridDim.x / kG;
   // schedule header, read once at entry: query blocks, 64-row units holding
@@ -958,7 +1032,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   const int voff = lane * 16 + (wave & 3) * 1024;  // group A's tile copies
   const bool rope = use_rope != 0;
   const bool qpos = rope && positions;
-  const int q_ops = qpos ? 9 : 8;
+  static_assert(!(F16 && kTab), "the FP16 variant takes prepared query rows");
+  const bool tab = kTab && rope;
+  const int q_ops = (qpos ? 9 : 8) + (kTab && qpos ? 1 : 0);  // query rows, position, table position
   const int slot_ops = group_b ? 0 : 8;  // tile loads per slot
   const float sk = sink[h] * kLog2e;
   const float kmax = key_norm_bound(k_norm_w, lane);  // |k'| of every key is at most this
@@ -970,6 +1046,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     s_items[jj] = make_int4(meta.x, meta.z, it.y * kBM, meta.w);
   }
   __syncthreads();
+  if (tab) {  // the first item's table
+    const Item i0 = item_from(s_items[0], window);
+    cs_table(s_cs, tid, table_pos_load(positions, qpos, i0, true, tid >> 4), s_rope);
+    lds_barrier();
+  }
 
   // Tile cursor: the next slot to load is tile ck of item cj (cn tiles from
   // workspace tile ctf). Slot s of the ring lives in stage s % kStages; the
@@ -1018,6 +1099,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   }
   QRaw qraw;
   load_q(q, positions, qpos, it, h, col, half, qraw);
+  int pnext = 0;  // this thread's table row position of the item after the current one
+  if (kTab && tab) pnext = table_pos_load(positions, qpos, item_from(s_items[min(1, nj - 1)], window), nj > 1, tid >> 4);
   ops += q_ops;
   int endq = ops;  // `ops` after the current item's query loads
   // group A's pending copies of the tile two slots ahead
@@ -1027,7 +1110,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
   uint4* pst = smem[0];
   bf16x8 qf[8];
   float qmax;
-  q_prologue<F16>(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
+  q_prologue<F16, kTab>(qraw, s_qw, s_rope, rope, eps, half, qf, qmax, s_cs);
 
   for (int j = 0; j < nj; ++j) {
     // Softmax shift: none when the logit bound |q'| max|k'| and the sink stay
@@ -1067,6 +1150,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
       int lo = 0;
       FLINT_NEXT_SLOT(ld, r, lo);
       tile_logits<F16>(smem[slot % kStages], lane, qf, s0, s1);
+      if (kTab && tab && k == 0 && j + 1 < nj) cs_table(s_cs, tid, pnext, s_rope);
       // Group A copies the tile of slot + 2 into the stage the barrier freed,
       // in one burst after its logits, at the top of the next body (or before
       // the next item's query loads): measured faster than spreading the
@@ -1092,6 +1176,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
     if (more) {
       nx = item_from(s_items[j + 1], window);
       load_q(q, positions, qpos, nx, h, col, half, qraw);
+      if (kTab && tab)
+        pnext = table_pos_load(positions, qpos, item_from(s_items[min(j + 2, nj - 1)], window), j + 2 < nj,
+                               tid >> 4);
       ops += q_ops;
       endq = ops;
     }
@@ -1120,7 +1207,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const uint16_t* __re
       }
     // The next item's query prologue runs before this item's output stores,
     // so its query loads are the newest vector-memory operations it waits on.
-    if (more) q_prologue<F16>(qraw, s_qw, s_rope, rope, eps, half, qf, qmax);
+    if (more) {
+      if (kTab && tab && it.ntiles == 1) lds_barrier();  // the table written at this item's only tile
+      q_prologue<F16, kTab>(qraw, s_qw, s_rope, rope, eps, half, qf, qmax, s_cs);
+    }
     // Rows past the valid length fall outside the store range and are dropped.
     constexpr int kOutElem = F16 ? 4 : 2;  // FP32 restored from fp16, or bf16
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -1561,6 +1651,9 @@ static int fwd_impl(const void* q, const void* k, const void* v, const float* q_
     else if (use_split_kernel(L.nqmax))
       attn_half_kernel<<<(unsigned)(attn_groups_half(L.nqmax) * kG * 2), kHalfThreads, 0, st>>>(
           qh, q_norm_w, k_norm_w, sink, pos, window, rope, eps, ws, n_seqs, oh, lse);
+    else if (rope)
+      attn_kernel<false, true><<<grid, kAttnThreads, 0, st>>>(qh, q_norm_w, k_norm_w, sink, pos, window,
+                                                              rope, eps, ws, n_seqs, oh, lse);
     else
       attn_kernel<false><<<grid, kAttnThreads, 0, st>>>(qh, q_norm_w, k_norm_w, sink, pos, window, rope,
                                                         eps, ws, n_seqs, oh, lse);
