@@ -71,7 +71,7 @@ struct BwdWs {
   char* kvb;       // [kG][ntmax][kKvbBytes]
   char* qt;        // [nqmax][kH][kQtBytes]
   float* sinkpart; // [kH][nqmax]: sum over the block's rows of p_sink * Dr
-  float* wq;       // [kD][nqmax * kG]: q-norm-weight terms per dQ workgroup
+  float* wq;       // [kD][nqmax * kG]: q-norm-weight terms per (query block, kv head)
   float* wk;       // [kD][ntmax * kG]: k-norm-weight terms per (tile, kv head)
   int* cb;         // [ntmax] first chunk slot of the key block starting at tile e
   int* nc;         // [ntmax] its chunks
@@ -769,7 +769,10 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const uint16_t* __re
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < kHpg; ++w) sum += wsum[w * kD + tid];
-      ws.wq[(size_t)tid * (ws.nqmax * kG) + bid] = sum;
+      // indexed by the query block's place in the sequences, not by the
+      // workgroup: the schedule's order of equal-cost items varies from call
+      // to call, and the finalize sums these terms in index order
+      ws.wq[(size_t)tid * (ws.nqmax * kG) + qg * kG + g] = sum;
     }
   }
 }
