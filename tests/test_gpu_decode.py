@@ -274,3 +274,29 @@ def test_decode_step_replayed_from_a_hip_graph():
         assert torch.equal(out_g, out_e), f"replay {i} differs from the eager step"
         float(torch.randn(1 << 20, device=d).sum())  # eager work between replays
     assert cache.device_status()[0] == fa.FLINT_OK
+
+
+@pytest.mark.parametrize("layer", [FULL, SLIDING], ids=["full", "sliding"])
+def test_decode_does_not_depend_on_workspace_contents(layer):
+    """A decode step from identical caches gives the same bits on a zeroed
+    workspace, on one filled with NaN bit patterns, and again on a zeroed one:
+    the split partials and the merge read only what the step wrote."""
+    wl = make_custom(341, [700, 300, 1500])
+    prefix = [650, 250, 1400]
+    d = _d()
+    cu = i64(wl.cu_seqlens)
+    rows = torch.as_tensor([int(cu[b]) + prefix[b] for b in range(3)])
+    q, k, v = (wl.q[rows].contiguous().to(d), wl.k[rows].contiguous().to(d), wl.v[rows].contiguous().to(d))
+    pos = None if wl.positions is None else wl.positions[rows].contiguous().to(d)
+    qw, kw, sk = wl.q_norm_w.to(d), wl.k_norm_w.to(d), wl.sinks.to(d)
+    outs = []
+    for fill in (0x00, 0xFF, 0x00):
+        cache = _cache_for(wl, layer, prefix, 2048)
+        cache.workspace.fill_(fill)
+        out = cache.decode(q, k, v, qw, kw, sk, pos)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all(), f"fill {fill:#x}: non-finite output"
+        outs.append((out.clone(), cache.k.clone(), cache.vt.clone()))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
