@@ -107,3 +107,54 @@ def test_max_seqlen_full_uniform_weights():
          f"alternating max abs {float(e2.max()):.3g}")
     assert bool((e0 <= tol0).all()) and bool((e2 <= tol2).all())
     del v, out
+
+
+def test_max_seqlen_sliding_rope_backward_pieces():
+    """The backward of the sliding RoPE layer at 2^21 tokens, graded on three
+    stretches the oracle takes alone (with their true positions): a sliding
+    row depends only on its 513 keys and a key only on the 513 queries after
+    it, so rows and keys at least 512 tokens inside a stretch get their
+    whole-sequence gradients. The logit-scale identity <w_q, dw_q> =
+    <w_k, dw_k> holds for the weight gradients at any size."""
+    from oracle import flint_attention_backward
+
+    d = torch.device("cuda", 0)
+    W = 513
+    _log(f"[gpu] max seqlen sliding RoPE backward: one sequence of {T} tokens")
+    q, k, v = draw_large(2023, T, d)
+    dout = draw_large(2024, T, d)[0]
+    qw, kw, sk = draw_large_params(2023)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=d)
+    kwargs = dict(cu_seqlens=cu, max_seqlen=T, window=W, use_rope=True)
+    out, lse = fa.flint_attn(q, k, v, qw.to(d), kw.to(d), sk.to(d), return_lse=True, **kwargs)
+    dq, dk, dv, dqw, dkw, dsk = fa.flint_attn_backward(dout, q, k, v, qw.to(d), kw.to(d), sk.to(d), out, lse,
+                                                       **kwargs)
+    torch.cuda.synchronize()
+    del out, lse
+    rng = np.random.default_rng(8)
+    worst = {}
+    for a, b in ((0, 1600), ((1 << 20) - 800, (1 << 20) + 1000), (T - 1800, T)):
+        r0 = a + W - 1 if a > 0 else 0
+        k1 = b - W + 1 if b < T else T
+        rows = sorted({r0, r0 + 1, b - 1} | {int(x) for x in rng.integers(r0, b, 20)})
+        keys = sorted({r0, k1 - 1} | {int(x) for x in rng.integers(r0, k1, 20)})
+        _log(f"      stretch [{a}, {b}): {len(rows)} rows, {len(keys)} keys")
+        ref = flint_attention_backward(
+            f64(q[a:b].cpu()), f64(k[a:b].cpu()), f64(v[a:b].cpu()), f64(qw), f64(kw), f64(sk),
+            np.array([0, b - a]), f64(dout[a:b].cpu()), positions=np.arange(a, b), window=W, use_rope=True,
+            rows=np.array(rows) - a, keys=np.array(keys) - a)
+        for name, got, want in (("dq", dq[torch.as_tensor(rows, device=d)], ref["dq"]),
+                                ("dk", dk[torch.as_tensor(keys, device=d)], ref["dk"]),
+                                ("dv", dv[torch.as_tensor(keys, device=d)], ref["dv"])):
+            g = got.float().cpu().numpy().astype(np.float64)
+            scale = float(np.max(np.abs(want)))
+            mx = float(np.max(np.abs(g - want))) / scale
+            rms = float(np.linalg.norm(g - want) / np.linalg.norm(want))
+            worst[name] = max(worst.get(name, 0.0), mx)
+            assert mx <= 2e-2 and rms <= 1e-2, f"[{a}, {b}) {name}: max {mx:.3g}, rms {rms:.3g}"
+    wa = float(torch.dot(qw, dqw.cpu()))
+    wb = float(torch.dot(kw, dkw.cpu()))
+    _log(f"      worst max errors {worst}; <w_q,dw_q> {wa:.5g}, <w_k,dw_k> {wb:.5g}")
+    assert abs(wa - wb) <= 2e-2 * max(abs(wa), abs(wb))
+    assert torch.isfinite(dsk).all()
+    del q, k, v, dout, dq, dk, dv
