@@ -194,43 +194,26 @@ __device__ __forceinline__ void dec_load(const uint16_t* kblk, const uint16_t* v
   for (int db = 0; db < 8; ++db) f.v[db] = __builtin_bit_cast(bf16x8_t, vp[db * 64]);
 }
 
-__global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__ cache_len, int cap,
-                                                         int window,
-                                                         const uint16_t* __restrict__ k_cache,
-                                                         const uint16_t* __restrict__ vt_cache,
-                                                         DecWs ws) {
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x, col = lane & 15, qd = lane >> 4;
-  const int len = cache_len[b];
-  if (len < 0 || (window == 0 && len >= cap)) return;
-  int t_lo, t_hi, blk_lo, nblk;
-  dec_range(len, window, &t_lo, &t_hi, &blk_lo, &nblk);
-  const int bs = s * ws.bps;
-  if (bs >= nblk) return;
-  const int be = min(bs + ws.bps, nblk);
-
-  bf16x8_t qf[4];
-#pragma unroll
-  for (int ds = 0; ds < 4; ++ds) {
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (col < kHpg)
-      w = *reinterpret_cast<const uint4*>(ws.q + ((size_t)b * kH + g * kHpg + col) * kD + 32 * ds + 8 * qd);
-    qf[ds] = __builtin_bit_cast(bf16x8_t, w);
-  }
-  const size_t blk0 = ((size_t)b * kG + g) * (cap / kDecBlock);
-  // cache block of token block blk (a ring of cap / 32 blocks on sliding layers)
-  auto cblk = [&](int blk) { return blk0 + (window > 0 ? blk % (cap / kDecBlock) : blk); };
-
-  float m = -INFINITY, l = 0.f;
-  f32x4 acc[8];
+// Blocks [b0, b1) of the keys [t_lo, t_hi] of one (sequence, kv head) for one
+// wave: streaming softmax (running max per head) and the unnormalized output.
+// qf: the query fragments (columns 0-7 the kv head's 8 query heads, 8-15 zero);
+// cblk(blk): the cache block of token block blk. Returns m and l per column
+// (reduced over the lane's rows) and acc.
+template <typename CBlk>
+__device__ __forceinline__ void dec_split(const uint16_t* __restrict__ k_cache,
+                                          const uint16_t* __restrict__ vt_cache, CBlk cblk, int b0,
+                                          int b1, int t_lo, int t_hi, int lane, const bf16x8_t* qf,
+                                          float& m, float& l, f32x4* acc) {
+  const int qd = lane >> 4;
+  m = -INFINITY;
+  l = 0.f;
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  if (b0 >= b1) return;
   DecFrags cur, nxt;
-  dec_load(k_cache + cblk(blk_lo + bs) * kDecBlockElems, vt_cache + cblk(blk_lo + bs) * kDecBlockElems,
-           lane, cur);
-  for (int blk = blk_lo + bs; blk < blk_lo + be; ++blk) {
-    if (blk + 1 < blk_lo + be)
+  dec_load(k_cache + cblk(b0) * kDecBlockElems, vt_cache + cblk(b0) * kDecBlockElems, lane, cur);
+  for (int blk = b0; blk < b1; ++blk) {
+    if (blk + 1 < b1)
       dec_load(k_cache + cblk(blk + 1) * kDecBlockElems, vt_cache + cblk(blk + 1) * kDecBlockElems, lane,
                nxt);
     f32x4 sc[2];
@@ -278,6 +261,38 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__
   }
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+}
+
+__global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__ cache_len, int cap,
+                                                         int window,
+                                                         const uint16_t* __restrict__ k_cache,
+                                                         const uint16_t* __restrict__ vt_cache,
+                                                         DecWs ws) {
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, col = lane & 15, qd = lane >> 4;
+  const int len = cache_len[b];
+  if (len < 0 || (window == 0 && len >= cap)) return;
+  int t_lo, t_hi, blk_lo, nblk;
+  dec_range(len, window, &t_lo, &t_hi, &blk_lo, &nblk);
+  const int bs = s * ws.bps;
+  if (bs >= nblk) return;
+  const int be = min(bs + ws.bps, nblk);
+
+  bf16x8_t qf[4];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (col < kHpg)
+      w = *reinterpret_cast<const uint4*>(ws.q + ((size_t)b * kH + g * kHpg + col) * kD + 32 * ds + 8 * qd);
+    qf[ds] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  const size_t blk0 = ((size_t)b * kG + g) * (cap / kDecBlock);
+  // cache block of token block blk (a ring of cap / 32 blocks on sliding layers)
+  auto cblk = [&](int blk) { return blk0 + (window > 0 ? blk % (cap / kDecBlock) : blk); };
+
+  float m, l;
+  f32x4 acc[8];
+  dec_split(k_cache, vt_cache, cblk, blk_lo + bs, blk_lo + be, t_lo, t_hi, lane, qf, m, l, acc);
   if (col < kHpg) {
     const size_t base = (((size_t)b * kG + g) * ws.nsplit + s) * kHpg + col;
     float* pr = ws.part + base * kD;
@@ -285,6 +300,123 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(const int* __restrict__
     for (int db = 0; db < 8; ++db)
       *reinterpret_cast<f32x4*>(pr + 16 * db + 4 * qd) = acc[db];
     if (qd == 0) *reinterpret_cast<float2*>(ws.ml + base * 2) = make_float2(m, l);
+  }
+}
+
+// The whole decode step of a small cache in one launch, one workgroup of 8
+// waves per (sequence, kv head): wave 0 appends the new key (as
+// decode_append_kernel does), every wave forms one query head's row into LDS;
+// after a barrier (which also makes wave 0's cache writes visible to the
+// workgroup) the 8 waves split the key blocks among themselves as the
+// split-K kernel splits them among workgroups, and the partial results merge
+// through LDS with the sink joining once, as in decode_merge_kernel. The
+// launch count is what bounds the step at these sizes.
+constexpr int kDecFusedWaves = 8;
+// Which step a call takes, from measurements (us per step, fused against
+// split-K): short caches, such as the sliding layers' 544-slot rings, take
+// the fused step at any batch (batch 1: 9.1 against 12.8; batch 64: 17.1
+// against 28.8); longer caches take it when the batch gives at least 128
+// workgroups (64 x 8,192 slots: 178 against 212; 64 x 32,768: 709 against
+// 827), and otherwise keep the split-K kernel, which spreads a few long
+// sequences over many waves (1 x 4,000: 22.7 against 12.2; 16 x 32,768: 329
+// against 212).
+constexpr int kDecFusedMaxBlocks = 32;         // 1,024 slots
+constexpr int kDecFusedMaxBlocksWide = 1056;   // 33,792 slots: 32,768 tokens and the next ones
+constexpr int kDecFusedWideGroups = 128;
+
+__global__ __launch_bounds__(64 * kDecFusedWaves) void decode_fused_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ q_norm_w, const float* __restrict__ k_norm_w, const float* __restrict__ sink,
+    const int* __restrict__ positions, const int* __restrict__ cache_len, int cap, int window, int use_rope,
+    double theta, float eps, uint16_t* __restrict__ k_cache, uint16_t* __restrict__ vt_cache, DecWs ws,
+    uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[kHpg][kD];
+  __shared__ __attribute__((aligned(16))) float s_part[kDecFusedWaves][kHpg][kD];
+  __shared__ float s_ml[kDecFusedWaves][kHpg][2];
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if ((g | b) == 0) {
+    // the call's device-data flags, written whole by this one workgroup
+    int bad = 0;
+    for (int s2 = tid; s2 < gridDim.y; s2 += blockDim.x) {
+      const int l2 = cache_len[s2];
+      bad |= (l2 < 0 || (window == 0 && l2 > cap - 1)) ? 1 : 0;
+    }
+    bad = __syncthreads_or(bad);
+    if (tid == 0) ws.hdr[0] = bad ? FLINT_DEV_CACHE : 0;
+  }
+  const int len = cache_len[b];
+  uint16_t* o = out + ((size_t)b * kH + g * kHpg) * kD;
+  const int slot = len >= 0 ? dec_slot(len, cap, window) : -1;
+  if (slot < 0) {  // skipped sequence: zero output, as the merge writes it
+    for (int i = tid; i < kHpg * kD; i += blockDim.x) o[i] = 0;
+    return;
+  }
+  const bool rope = use_rope != 0;
+  const int pos = positions ? positions[b] : len;
+  const RopeFreq f = rope ? rope_freq(theta, lane) : RopeFreq{0ull, 0.f, 0.f};
+  float a, c;
+  if (wave == 0) {
+    norm_rope_row(k + ((size_t)b * kG + g) * kD, k_norm_w, eps, rope, pos, f, 1.0f, lane, a, c);
+    const size_t blk = ((size_t)b * kG + g) * (cap / kDecBlock) + slot / kDecBlock;
+    const int kb = slot % kDecBlock;
+    uint16_t* kblk = k_cache + blk * kDecBlockElems;
+    kblk[dec_k_index(kb, lane)] = bf16_bits(a);
+    kblk[dec_k_index(kb, lane + 64)] = bf16_bits(c);
+    const uint16_t* vr = v + ((size_t)b * kG + g) * kD;
+    uint16_t* vblk = vt_cache + blk * kDecBlockElems;
+    vblk[dec_v_index(kb, lane)] = vr[lane];
+    vblk[dec_v_index(kb, lane + 64)] = vr[lane + 64];
+  }
+  norm_rope_row(q + ((size_t)b * kH + g * kHpg + wave) * kD, q_norm_w, eps, rope, pos, f,
+                kLog2e * 0.08838834764831845f, lane, a, c);
+  s_q[wave][lane] = bf16_bits(a);
+  s_q[wave][lane + 64] = bf16_bits(c);
+  __syncthreads();
+
+  int t_lo, t_hi, blk_lo, nblk;
+  dec_range(len, window, &t_lo, &t_hi, &blk_lo, &nblk);
+  const int col = lane & 15, qd = lane >> 4;
+  bf16x8_t qf[4];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (col < kHpg) w = *reinterpret_cast<const uint4*>(&s_q[col][32 * ds + 8 * qd]);
+    qf[ds] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  const size_t blk0 = ((size_t)b * kG + g) * (cap / kDecBlock);
+  auto cblk = [&](int blk) { return blk0 + (window > 0 ? blk % (cap / kDecBlock) : blk); };
+  const int per = (nblk + kDecFusedWaves - 1) / kDecFusedWaves;
+  const int b0 = blk_lo + min(nblk, wave * per), b1 = blk_lo + min(nblk, (wave + 1) * per);
+  float m, l;
+  f32x4 acc[8];
+  dec_split(k_cache, vt_cache, cblk, b0, b1, t_lo, t_hi, lane, qf, m, l, acc);
+  if (col < kHpg) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(&s_part[wave][col][16 * db + 4 * qd]) = acc[db];
+    if (qd == 0) {
+      s_ml[wave][col][0] = m;
+      s_ml[wave][col][1] = l;
+    }
+  }
+  __syncthreads();
+  // merge: output (head hh, channel ch) over the waves' partial results
+  for (int e = tid; e < kHpg * kD; e += blockDim.x) {
+    const int hh = e / kD, ch = e % kD;
+    const float sk = sink[g * kHpg + hh] * kLog2e;
+    float mt = sk;
+#pragma unroll
+    for (int w = 0; w < kDecFusedWaves; ++w) mt = fmaxf(mt, s_ml[w][hh][0]);
+    float lsum = (mt == -INFINITY || sk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sk - mt);
+    float acc2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecFusedWaves; ++w) {
+      const float mw = s_ml[w][hh][0];
+      const float sc = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mt);
+      lsum += s_ml[w][hh][1] * sc;
+      acc2 += s_part[w][hh][ch] * sc;
+    }
+    o[hh * kD + ch] = bf16_bits(lsum > 0.f ? acc2 / lsum : 0.f);
   }
 }
 
@@ -463,6 +595,22 @@ extern "C" int flint_attn_decode(const void* q, const void* k, const void* v, co
   const uint16_t* kc = static_cast<const uint16_t*>(k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(vt_cache);
   (void)hipGetLastError();
+  const int cblocks = cache_cap / kDecBlock;
+  if (cblocks <= kDecFusedMaxBlocks ||
+      (cblocks <= kDecFusedMaxBlocksWide && (int64_t)batch * kG >= kDecFusedWideGroups)) {
+    // the whole step in one launch
+    decode_fused_kernel<<<dim3(kG, (unsigned)batch), 64 * kDecFusedWaves, 0, st>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        q_norm_w, k_norm_w, sink, rope ? positions : nullptr, cache_len, cache_cap, window, rope,
+        (double)rope_theta, eps, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(vt_cache), ws,
+        static_cast<uint16_t*>(out));
+    if (hipGetLastError() != hipSuccess) return FLINT_ERR_HIP;
+    if (debug_sync()) {
+      int32_t flags = 0;
+      return flint_attn_device_status(workspace, stream, &flags);
+    }
+    return FLINT_OK;
+  }
   decode_append_kernel<<<dim3(1, kG, (unsigned)batch), 64 * (1 + kHpg), 0, st>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       q_norm_w, k_norm_w, rope ? positions : nullptr, cache_len, 1, cache_cap, window, rope,

@@ -300,3 +300,30 @@ def test_decode_does_not_depend_on_workspace_contents(layer):
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert torch.equal(a, b)
+
+
+def test_full_layer_wide_batch():
+    """32 sequences (128 workgroups: the one-launch step also for caches longer
+    than 1,024 slots) of mixed lengths at block edges, every step graded."""
+    edges = [0, 1, 31, 32, 33, 255, 256, 257, 1000, 2049]
+    prefix = [edges[i % len(edges)] + 7 * (i // len(edges)) for i in range(32)]
+    steps = 2
+    wl = make_custom(4010, [p + steps for p in prefix], layers=(FULL,))
+    _decode_and_check(wl, FULL, prefix, steps, 2080, "full wide batch")
+
+
+def test_full_cache_overflow_beside_a_valid_sequence():
+    """Batch 2 over 2,048 slots (the split-K step): the full sequence reports
+    the overflow and gets zeros, the other decodes normally."""
+    d = _d()
+    wl = make_custom(4011, [2049, 102], layers=(FULL,))
+    cache = _cache_for(wl, FULL, [2048, 100], 2048)
+    rows = np.array([2048, 2049 + 100])
+    idx = torch.as_tensor(rows)
+    out = cache.decode(wl.q[idx].contiguous().to(d), wl.k[idx].contiguous().to(d),
+                       wl.v[idx].contiguous().to(d), wl.q_norm_w.to(d), wl.k_norm_w.to(d), wl.sinks.to(d))
+    st, flags = cache.device_status()
+    assert st == fa.FLINT_ERR_DEVICE_DATA and flags & fa.FLINT_DEV_CACHE
+    assert torch.count_nonzero(out[0]).item() == 0
+    ref = oracle_for(wl, FULL, rows=rows[1:])
+    grade(to_np(out[1:]), ref, wl, rows=rows[1:], what="valid sequence beside an overflow")
