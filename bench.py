@@ -939,11 +939,16 @@ def main():
         raise RuntimeError(f"device data error flags {flags}")
 
     K = args.steps
-    if args.torch_events:
+    evs = None
+    if not args.torch_events:
+        try:
+            evs = [(TimingEvent(), TimingEvent()) for _ in range(K)]
+        except (OSError, RuntimeError) as e:  # no fence-free events here: torch's instead
+            print(f"fence-free HIP events unavailable ({e}); timing with torch.cuda.Event", file=sys.stderr)
+            args.torch_events = True
+    if evs is None:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(K)]
-    else:
-        evs = [(TimingEvent(), TimingEvent()) for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
