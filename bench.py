@@ -52,6 +52,7 @@ KERNEL_SRCS = [os.path.join(ROOT, "attention_head_rmsnorm_amd", "csrc", f)
 TRAFFIC_PROFILES = {
     "tstar": os.path.join(ROOT, "profiles", "attn_kernel_s8192_full_nope_traffic.md"),
     "c3": os.path.join(ROOT, "profiles", "attn_kernel_b8_s8192_sw513_rope_traffic.md"),
+    "c1": os.path.join(ROOT, "profiles", "attn_s768_sw513_rope_traffic.md"),
 }
 COPY_PROBE_BYTES = 1 << 30
 
@@ -1012,7 +1013,8 @@ def main():
             "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
             "frac": round(attn_tflops / BF16_PEAK_TFLOPS if bound == "mfma" else alg_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "attn_kernel",
+            "kernel": ("attn_half_kernel" if fa.flint_attn_fwd_kernel(T, n) == fa.FLINT_KERNEL_SPLIT
+                       else "attn_kernel"),
             "algorithmic_bytes": alg_bytes,
             "algorithmic_flops": flops,
             "intensity_flop_per_byte": round(intensity, 1),
